@@ -1,0 +1,217 @@
+/*
+ * dspark.h -- C ABI of the DSpark draft pass on AMD Instinct MI355X (gfx950).
+ *
+ * The draft pass (huggingface.co "Kimi-K3-DSpark-NVFP4", original card,
+ * "Model Overview"; alphaneural.io "kimi-k3-dspark-gguf", "How it works";
+ * graysoft.dev "Lucebox Kimi-K3-DSpark Q8_0 GGUF", "Architecture metadata"):
+ * five captured target hidden states of a 7-token block are fused by fc, run
+ * through dense non-causal decoder layers whose MLA attention reads the
+ * 576-element latent cache with kv_b absorbed, projected through the lm_head,
+ * rolled out by the rank-256 Markov head and scored by the confidence head.
+ * The acceptance length is the prefix run length of matches against a
+ * verifier stream ("Why acceptance is so sensitive"; "Sampling options").
+ *
+ * Conventions for every call:
+ *  - All functions return int32_t: DSPARK_OK (0) or a negative error code.
+ *    Arguments are validated before anything is enqueued; on error nothing
+ *    is enqueued and dspark_last_error() returns a thread-local message.
+ *  - Device pointers are HIP device addresses owned by the caller.  The
+ *    library allocates no device memory, never frees caller memory and never
+ *    synchronises the stream on the hot path (draft / layer / accept calls
+ *    enqueue asynchronously on `stream`, a hipStream_t passed as void*;
+ *    NULL means the legacy default stream).
+ *  - Element layouts are row-major; "[a][b]" means b is contiguous.
+ *  - A model is read-only after creation; calls on distinct streams with
+ *    distinct workspaces may run concurrently.  Calls that share a workspace
+ *    must be ordered by the caller.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ---- */
+#define DSPARK_OK 0
+#define DSPARK_EINVAL (-1)       /* null / misaligned pointer, out-of-range value */
+#define DSPARK_EUNSUPPORTED (-2) /* shape or format the kernels do not cover     */
+#define DSPARK_EWORKSPACE (-3)   /* buffer smaller than the size query returned  */
+#define DSPARK_EHIP (-4)         /* HIP runtime error; message has the HIP text  */
+#define DSPARK_ENODEVICE (-5)    /* no usable gfx950 device                      */
+
+/* ---- storage formats of weights and activations ---- */
+#define DSPARK_DT_F32 0
+#define DSPARK_DT_BF16 1
+/* Q8_0: blocks of 32 consecutive weights along a row, 34 bytes each: an fp16
+ * scale d (little-endian) then 32 int8 codes q; weight = d * q (graysoft.dev
+ * card, "Conversion result": GGUF MOSTLY_Q8_0).  cols % 32 == 0. */
+#define DSPARK_DT_Q8_0 2
+/* FP8 E4M3FN codes (OCP: bias 7, no inf, 0x7F/0xFF NaN, max 448) with one fp32
+ * scale per output row; weight = scale[row] * e4m3(code) (huggingface.co card,
+ * "Limitations": per-channel weight-only FP8). */
+#define DSPARK_DT_FP8_E4M3 3
+
+/* ---- weight table ids ---- */
+#define DSPARK_W_FC 0          /* [hidden][n_captured*hidden] fc ("context_proj")  */
+#define DSPARK_W_FC_NORM 1     /* [hidden] f32, RMSNorm gain after fc              */
+#define DSPARK_W_FINAL_NORM 2  /* [hidden] f32                                     */
+#define DSPARK_W_LM_HEAD 3     /* [vocab][hidden]                                  */
+#define DSPARK_W_MARKOV_W1 4   /* [vocab][markov_rank] (BF16 or F32)               */
+#define DSPARK_W_MARKOV_W2 5   /* [vocab][markov_rank] (BF16 or F32)               */
+#define DSPARK_W_CONF_W 6      /* [hidden + markov_rank] f32                       */
+#define DSPARK_W_CONF_B 7      /* [1] f32                                          */
+#define DSPARK_W_LAYER_BASE 16
+#define DSPARK_W_LAYER_STRIDE 16
+/* per-layer tensors: id = DSPARK_LAYER_W(layer, k) */
+#define DSPARK_L_IN_NORM 0     /* [hidden] f32                                     */
+#define DSPARK_L_Q_A 1         /* [q_lora][hidden]                                  */
+#define DSPARK_L_Q_A_NORM 2    /* [q_lora] f32                                      */
+#define DSPARK_L_KV_A 3        /* [kv_lora + qk_rope][hidden] (kv_a_proj_with_mqa)  */
+#define DSPARK_L_KV_A_NORM 4   /* [kv_lora] f32                                     */
+#define DSPARK_L_Q_B 5         /* [n_heads*(qk_nope+qk_rope)][q_lora]               */
+#define DSPARK_L_KV_B 6        /* [n_heads*(qk_nope+v_head)][kv_lora]; per head the
+                                  first qk_nope rows are W_UK, the next v_head W_UV */
+#define DSPARK_L_O 7           /* [hidden][n_heads*v_head]                          */
+#define DSPARK_L_POST_NORM 8   /* [hidden] f32                                      */
+#define DSPARK_L_GATE 9        /* [inter][hidden]                                   */
+#define DSPARK_L_UP 10         /* [inter][hidden]                                   */
+#define DSPARK_L_DOWN 11       /* [hidden][inter]                                   */
+#define DSPARK_LAYER_W(l, k) (DSPARK_W_LAYER_BASE + (l) * DSPARK_W_LAYER_STRIDE + (k))
+
+/* config flags */
+#define DSPARK_CFG_LAYERS_ONLY 1 /* the table holds decoder layers only (no fc,
+                                    lm_head, Markov or confidence tensors): only
+                                    dspark_layer_forward may be called */
+
+typedef struct dspark_config {
+  int32_t hidden, n_layers, n_heads, q_lora, kv_lora, qk_nope, qk_rope, v_head;
+  int32_t inter, vocab, markov_rank, block, n_captured;
+  int32_t flags;
+  float rms_eps;       /* RMSNorm: g * x / sqrt(mean(x^2) + eps)               */
+  float rope_theta;    /* RoPE base; consecutive pairs (2k, 2k+1) rotate        */
+  float yarn_factor;   /* 1 = plain RoPE; s > 1: YaRN NTK-by-parts, logit x m^2 */
+  int32_t yarn_orig_ctx;
+  float yarn_beta_fast, yarn_beta_slow;
+} dspark_config;
+
+typedef struct dspark_weight {
+  int32_t id;          /* DSPARK_W_* or DSPARK_LAYER_W(l, k)                    */
+  int32_t dtype;       /* DSPARK_DT_*; norms and the confidence head are F32    */
+  const void* data;    /* device; F32 float[rows][cols]; BF16 uint16[rows][cols];
+                          Q8_0 uint8[rows][cols/32*34]; FP8 uint8[rows][cols]   */
+  const void* scales;  /* device float[rows] for FP8, else NULL                 */
+  int64_t rows, cols;  /* vectors: rows = length, cols = 1                      */
+} dspark_weight;
+
+typedef struct dspark_model dspark_model; /* opaque, host memory */
+
+/* Bytes of device memory the caller must provide to dspark_model_create for
+ * the repacked weights (device layouts: 16-row tiles in MFMA fragment order,
+ * Q8_0 codes and fp16 scales in separate planes).  0 on invalid input (see
+ * dspark_last_error). */
+size_t dspark_packed_bytes(const dspark_config* cfg, const dspark_weight* w, int32_t n);
+
+/* Validate the config and the weight table, repack every tensor into
+ * `packed_buf` (caller-owned device memory of at least packed_bytes, 256-byte
+ * aligned) with kernels on `stream`, then synchronise the stream once.  The
+ * caller may free the source tensors after this returns.  *out is a host
+ * handle owned by the library; free it with dspark_model_destroy. */
+int32_t dspark_model_create(const dspark_config* cfg, const dspark_weight* w, int32_t n,
+                            void* packed_buf, size_t packed_bytes, void* stream,
+                            dspark_model** out);
+
+/* Free the host handle (the packed buffer stays the caller's). */
+int32_t dspark_model_destroy(dspark_model* m);
+
+/* Workspace bytes for one draft / layer call over n_seq sequences whose cache
+ * lengths sum to total_ctx.  0 on invalid input. */
+size_t dspark_workspace_bytes(const dspark_model* m, int32_t n_seq, int64_t total_ctx);
+
+typedef struct dspark_block_in {
+  int32_t n_seq;              /* >= 1                                            */
+  int32_t act_dtype;          /* captured states: DSPARK_DT_F32 or DSPARK_DT_BF16 */
+  int32_t kv_dtype;           /* latent caches: DSPARK_DT_F32 or DSPARK_DT_BF16   */
+  int32_t pad_;
+  int64_t total_ctx;          /* == kv_offsets[n_seq] (host copy, for planning)   */
+  const void* captured;       /* device [n_seq][n_captured][block][hidden]; fc
+                                 concatenates the n_captured states per token in
+                                 this (capture) order                            */
+  const void* const* kv;      /* host array of n_layers device pointers, each
+                                 [total_ctx][kv_lora + qk_rope]: per token the
+                                 normed c_kv then the roped k_pe, used as stored;
+                                 sequence s owns rows kv_offsets[s] .. [s+1]-1   */
+  const int32_t* kv_offsets;  /* device int32 [n_seq + 1], non-decreasing, [0]=0 */
+  const int32_t* prev_token;  /* device int32 [n_seq]: last verified token, the
+                                 Markov predecessor of position 0; -1 (or any
+                                 value outside [0, vocab)) = none               */
+  const int32_t* forced_prev; /* optional device int32 [n_seq][block]: when set,
+                                 position i >= 1 uses forced_prev[s][i-1] as its
+                                 Markov predecessor instead of the drafted token
+                                 (teacher-forced rollout); NULL = free running   */
+} dspark_block_in;
+
+typedef struct dspark_block_out {
+  int32_t* tokens;  /* device int32 [n_seq][block], greedy draft (required)      */
+  float* conf;      /* device float [n_seq][block] confidence (required)         */
+  float* logits;    /* optional device float [n_seq][block][vocab]: backbone
+                       logits plus the Markov term, the argmax input; NULL = skip */
+  float* hidden;    /* optional device float [n_seq][block][hidden]: final-normed
+                       hidden state fed to the lm_head; NULL = skip             */
+} dspark_block_out;
+
+/* One draft pass for every sequence's block (one pass of the hot path):
+ * fc + RMSNorm -> n_layers x (RMSNorm, fused q_a/kv_a, q/kv norms + rope, q_b,
+ * absorbed split-K MLA attention over cache rows and the block's own 7 latent
+ * rows (no mask), un-absorb, o_proj + residual, RMSNorm, SwiGLU + residual) ->
+ * final RMSNorm -> lm_head -> for i = 0..block-1: l_i = z_i + W2 W1[t_{i-1}],
+ * t_i = argmax l_i (lowest index on ties), conf_i = sigmoid(w_h . hf_i +
+ * w_m . W1[t_{i-1}] + b).  Position of block token i = that sequence's cache
+ * length + i.  Asynchronous on `stream`.  `workspace` must hold
+ * dspark_workspace_bytes(m, in->n_seq, in->total_ctx) bytes, 256-byte aligned.
+ * Errors: EINVAL (nulls, n_seq < 1, dtype mismatch), EWORKSPACE, EHIP. */
+int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in,
+                           dspark_block_out* out, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/* One decoder layer on a given residual stream (the single-layer unit):
+ * x_out = x_in + o_proj(MLA(RMSNorm(x_in))) and, when with_mlp != 0, then
+ * x_out += SwiGLU(RMSNorm(x_out)).  x_in, x_out: device float
+ * [n_seq*block][hidden] (may alias).  kv: device [total_ctx][kv_lora+qk_rope] of
+ * kv_dtype; kv_offsets: device [n_seq+1].  Asynchronous on `stream`. */
+int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_mlp,
+                             int32_t n_seq, const float* x_in, float* x_out,
+                             const void* kv, int32_t kv_dtype, const int32_t* kv_offsets,
+                             int64_t total_ctx, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* Acceptance length (huggingface.co card, "Why acceptance is so sensitive":
+ * a block is accepted up to its first mismatch): out_len[s] = the largest
+ * k <= block with draft[s][j] == verifier[s][j] for all j < k.  Device
+ * pointers, asynchronous on `stream`.  Token values are not range-checked. */
+int32_t dspark_accept_len(const int32_t* draft, const int32_t* verifier, int32_t n_seq,
+                          int32_t block, int32_t* out_len, void* stream);
+
+/* Same on host pointers, synchronous, no device needed. */
+int32_t dspark_accept_len_host(const int32_t* draft, const int32_t* verifier, int32_t n_seq,
+                               int32_t block, int32_t* out_len);
+
+/* Decode one repacked matrix of the model back to float [rows][cols] (device
+ * pointer `out`) with the same per-lane decoders the GEMM kernels use.
+ * Accepted ids: DSPARK_W_FC, DSPARK_W_LM_HEAD, DSPARK_W_MARKOV_W2 and per layer
+ * Q_B, O, DOWN, Q_A (rows of q_a then kv_a, fused on the device) and GATE
+ * (rows of gate then up).  Q8_0 gives d*q and BF16 / F32 the stored value,
+ * all exact in fp32; FP8 gives s*e4m3(q) rounded to nearest fp32.
+ * Asynchronous on `stream`.  Intended for tests. */
+int32_t dspark_dequant(const dspark_model* m, int32_t weight_id, float* out, void* stream);
+
+/* Thread-local text of the last error ("" if none). */
+const char* dspark_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */

@@ -1,0 +1,183 @@
+// Shared device-side definitions of the DSpark draft-pass library (gfx950).
+//
+// Data layouts in HBM (all owned by the caller; see include/dspark.h):
+//
+//  Packed weight matrix [N][K] (logical rows n, reduction index k), padded to
+//  16-row tiles and Kp = round_up(K, 64):
+//   * BF16:   one 1 KiB chunk per (tile t, 32-wide k block kb), chunk index
+//             t*KB + kb; lane l of a wave owns 16 bytes = 8 bf16 of row
+//             16t + (l & 15), columns 32kb + 8(l >> 4) .. +7.  This is the B
+//             operand of v_mfma_f32_16x16x32_bf16, so one dwordx4 load per lane
+//             per MFMA, and a wave streams contiguous 1 KiB chunks.
+//   * Q8_0 / FP8: one 1 KiB chunk per (tile, pair of k blocks), index
+//             t*(KB/2) + p; lane l owns 16 bytes: 8 codes of block 2p then 8
+//             codes of block 2p+1, same row / column rule as BF16.
+//             Q8_0 scales: one dword per (tile, pair, row): [tiles][KB/2][16]
+//             holding the fp16 scales of blocks 2p (low half) and 2p+1, so a
+//             wave reads 64 contiguous bytes of scales per 1 KiB of codes.
+//             FP8 scales: fp32 [tiles*16].
+//   * F32:    one 1 KiB chunk per (tile, 16-wide k group g); lane l owns 4
+//             floats of row 16t + (l & 15), columns 16g + 4(l >> 4) .. +3,
+//             fed to four v_mfma_f32_16x16x4_f32 in turn.
+//  Grouped matrices (per-head W_UK^T and W_UV) pad every group of G rows to
+//  TG = ceil(G/16) tiles, so no tile spans two heads.
+//
+//  Activation fragments ("A" operand, written by the elementwise kernels):
+//   * bf16 family, hi/lo (M <= 8): per group [KB][64 lanes][8] bf16; lane l
+//     holds row m = l & 15 for m < 8 as the bf16 rounding hi = bf16(v) and
+//     for m >= 8 the residual lo = bf16(v - hi) of row m - 8, columns
+//     32kb + 8(l >> 4) .. +7.  Summing MFMA output rows m and m + 8 gives the
+//     product with ~16 significant bits of the fp32 activation at no extra
+//     MFMA cost (rows 8..15 would otherwise be padding).
+//   * bf16 family, plain (M > 8): per group [MT][KB][64][8], row 16mt + (l & 15).
+//   * f32 family: per group [MT][Kp/16][64][4] fp32, row 16mt + (l & 15),
+//     columns 16g + 4(l >> 4) .. +3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_Q8_0 = 2, DT_FP8 = 3 };
+
+// ------------------------------------------------------------------ scalars --
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// ------------------------------------------------------------ weight decode --
+// Two int8 codes (bytes sh/8 and sh/8 + 1 of w) -> two bf16 in one dword.  Codes
+// are integers of magnitude <= 127, exact in bf16; the fp32 conversion is exact
+// and its upper half is the bf16 pattern.
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int sh) {
+  float f0 = (float)(int8_t)(w >> sh);
+  float f1 = (float)(int8_t)(w >> (sh + 8));
+  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = i8x2_to_bf16x2(lo, 0);
+  r[1] = i8x2_to_bf16x2(lo, 16);
+  r[2] = i8x2_to_bf16x2(hi, 0);
+  r[3] = i8x2_to_bf16x2(hi, 16);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Eight FP8 E4M3FN codes -> eight bf16 (every E4M3 value is exact in bf16),
+// using the gfx950 scaled conversion with scale 1.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// ---------------------------------------------------------------- matrices --
+// Device view of one packed weight matrix (see the layout notes above).
+struct PackedMat {
+  const unsigned char* codes;  // code plane
+  const void* scales;          // Q8_0: u32 [tiles][KB/2][16]; FP8: f32 [tiles*16]; else null
+  int fmt;                     // DT_*
+  int ngroups;                 // >= 1
+  int G;                       // logical rows per group
+  int TG;                      // 16-row tiles per group
+  int K;                       // logical reduction length
+  int Kp;                      // padded to a multiple of 64
+  int KB;                      // Kp / 32
+};
+
+// Activation fragment buffer descriptor.
+struct FragDesc {
+  void* ptr;
+  int f32;          // 1: f32 family, 0: bf16 family
+  int hilo;         // bf16 family with M <= 8
+  int KB;           // Kp / 32 (bf16 family) ; Kp / 16 groups for f32 family in KG
+  int KG;           // Kp / 16
+  int MT;           // m-tiles of 16 rows
+  long long gstride;  // elements per group
+};
+
+// Write activation element (row m, column k) of group g into a fragment buffer.
+__device__ __forceinline__ void frag_put(const FragDesc& fd, int g, int m, int k, float v) {
+  if (fd.f32) {
+    const int grp = k >> 4, q = (k >> 2) & 3, i = k & 3;
+    const int mt = m >> 4, lane = q * 16 + (m & 15);
+    float* p = (float*)fd.ptr + (long long)g * fd.gstride;
+    p[((long long)(mt * fd.KG + grp) * 64 + lane) * 4 + i] = v;
+    return;
+  }
+  const int kb = k >> 5, q = (k >> 3) & 3, i = k & 7;
+  uint16_t* p = (uint16_t*)fd.ptr + (long long)g * fd.gstride;
+  const uint32_t hb = f32_to_bf16_bits(v);
+  if (fd.hilo) {
+    const float lo = v - bf16_bits_to_f32(hb);
+    p[((long long)kb * 64 + q * 16 + m) * 8 + i] = (uint16_t)hb;
+    p[((long long)kb * 64 + q * 16 + 8 + m) * 8 + i] = (uint16_t)f32_to_bf16_bits(lo);
+  } else {
+    const int mt = m >> 4, lane = q * 16 + (m & 15);
+    p[((long long)(mt * fd.KB + kb) * 64 + lane) * 8 + i] = (uint16_t)hb;
+  }
+}
+
+// ------------------------------------------------------------- reductions --
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over a 256-thread block; `red` is __shared__ float[4].
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+__device__ __forceinline__ float block_max256(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Order-preserving 64-bit key of (value, index): larger value wins, and on
+// equal values the lower index wins.  -0 is folded into +0 first.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ int key_index(unsigned long long k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+}
+
+constexpr int KEY_SLOTS = 16;  // argmax partial slots per (sequence, position)
+
+}  // namespace dspark

@@ -1,0 +1,931 @@
+// Host side of the C ABI declared in include/dspark.h: validation, the packed
+// weight plan and repack, the per-call workspace plan, and the launch sequence
+// of one draft pass (all launches asynchronous on the caller's stream).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dspark.h"
+#include "kernels.h"
+
+using namespace dspark;
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(DSPARK_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+inline long long rup(long long a, long long b) { return (a + b - 1) / b * b; }
+inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+// ----------------------------------------------------------- packed plan --
+struct Mat {
+  PackedMat pm{};
+  long long codes_off = -1, scales_off = -1, codes_bytes = 0, scales_bytes = 0;
+  bool present = false;
+};
+
+void mat_geom(Mat& m, int fmt, int ngroups, int G, int K) {
+  PackedMat& p = m.pm;
+  p.fmt = fmt;
+  p.ngroups = ngroups;
+  p.G = G;
+  p.TG = (int)cdiv(G, 16);
+  p.K = K;
+  p.Kp = (int)rup(K, 64);
+  p.KB = p.Kp / 32;
+  const long long T = (long long)ngroups * p.TG;
+  const int esz = fmt == DT_F32 ? 4 : fmt == DT_BF16 ? 2 : 1;
+  m.codes_bytes = T * 16 * p.Kp * esz;
+  m.scales_bytes = fmt == DT_Q8_0 ? T * (p.KB / 2) * 16 * 4 : fmt == DT_FP8 ? T * 16 * 4 : 0;
+  m.present = true;
+}
+
+struct Layer {
+  Mat qkva, qb, uk, uv, o, gu, down;
+  long long in_norm = -1, q_a_norm = -1, kv_a_norm = -1, post_norm = -1;
+};
+
+}  // namespace
+
+struct dspark_model {
+  dspark_config c{};
+  unsigned char* base = nullptr;
+  long long bytes = 0;
+  bool layers_only = false;
+  Mat fc, lm, w2;
+  long long fc_norm = -1, final_norm = -1, conf_w = -1, conf_b = -1, w1 = -1, freqs = -1;
+  int w1_fmt = DT_BF16, w1_ld = 0;
+  std::vector<Layer> L;
+  float tau = 1.f;
+  bool has_mlp = true;
+};
+
+namespace {
+
+const dspark_weight* find_w(const dspark_weight* w, int n, int id) {
+  for (int i = 0; i < n; ++i)
+    if (w[i].id == id) return &w[i];
+  return nullptr;
+}
+
+int32_t check_cfg(const dspark_config* c) {
+  if (!c) return fail(DSPARK_EINVAL, "config is NULL");
+  if (c->hidden <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->q_lora <= 0 || c->kv_lora <= 0 ||
+      c->qk_nope <= 0 || c->qk_rope <= 0 || c->v_head <= 0 || c->block <= 0)
+    return fail(DSPARK_EINVAL, "config has a non-positive dimension");
+  if (!(c->flags & DSPARK_CFG_LAYERS_ONLY) &&
+      (c->vocab <= 0 || c->markov_rank <= 0 || c->n_captured <= 0 || c->inter <= 0))
+    return fail(DSPARK_EINVAL, "config has a non-positive head / fc dimension");
+  if (c->qk_rope % 2) return fail(DSPARK_EUNSUPPORTED, "qk_rope must be even");
+  if ((c->kv_lora + c->qk_rope) % 8) return fail(DSPARK_EUNSUPPORTED, "kv_lora + qk_rope must be a multiple of 8");
+  if (c->kv_lora % 16) return fail(DSPARK_EUNSUPPORTED, "kv_lora must be a multiple of 16");
+  if (c->block > 64) return fail(DSPARK_EUNSUPPORTED, "block > 64");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f) || !(c->yarn_factor >= 1.f))
+    return fail(DSPARK_EINVAL, "rms_eps / rope_theta / yarn_factor out of range");
+  return DSPARK_OK;
+}
+
+// Look up one matrix source: id, allowed dtypes, exact shape.
+int32_t get_mat(const dspark_weight* w, int n, int id, long long rows, long long cols, const dspark_weight** out,
+                bool required = true) {
+  const dspark_weight* x = find_w(w, n, id);
+  *out = x;
+  if (!x) return required ? fail(DSPARK_EINVAL, "weight id %d missing", id) : DSPARK_OK;
+  if (x->rows != rows || x->cols != cols)
+    return fail(DSPARK_EINVAL, "weight id %d: shape [%lld][%lld], expected [%lld][%lld]", id, (long long)x->rows,
+                (long long)x->cols, rows, cols);
+  if (x->dtype < DSPARK_DT_F32 || x->dtype > DSPARK_DT_FP8_E4M3)
+    return fail(DSPARK_EUNSUPPORTED, "weight id %d: unknown dtype %d", id, x->dtype);
+  if (!x->data) return fail(DSPARK_EINVAL, "weight id %d: data is NULL", id);
+  if (x->dtype == DSPARK_DT_Q8_0 && cols % 32) return fail(DSPARK_EUNSUPPORTED, "weight id %d: Q8_0 needs cols %% 32 == 0", id);
+  if (x->dtype == DSPARK_DT_FP8_E4M3 && !x->scales) return fail(DSPARK_EINVAL, "weight id %d: FP8 scales NULL", id);
+  return DSPARK_OK;
+}
+
+int32_t get_vec(const dspark_weight* w, int n, int id, long long len, const dspark_weight** out) {
+  const dspark_weight* x = find_w(w, n, id);
+  *out = x;
+  if (!x) return fail(DSPARK_EINVAL, "weight id %d missing", id);
+  if (x->dtype != DSPARK_DT_F32) return fail(DSPARK_EUNSUPPORTED, "weight id %d must be F32", id);
+  if (x->rows * x->cols != len) return fail(DSPARK_EINVAL, "weight id %d: length %lld, expected %lld", id,
+                                            (long long)(x->rows * x->cols), len);
+  if (!x->data) return fail(DSPARK_EINVAL, "weight id %d: data is NULL", id);
+  return DSPARK_OK;
+}
+
+// Build the plan (geometry + offsets) of every packed item; returns total bytes.
+int32_t build_plan(const dspark_config* c, const dspark_weight* w, int n, dspark_model& m) {
+  int32_t rc = check_cfg(c);
+  if (rc) return rc;
+  if (!w || n <= 0) return fail(DSPARK_EINVAL, "weight table empty");
+  m.c = *c;
+  m.layers_only = (c->flags & DSPARK_CFG_LAYERS_ONLY) != 0;
+  const long long H = c->hidden, nh = c->n_heads, r = c->kv_lora, dr = c->qk_rope, dn = c->qk_nope, dv = c->v_head;
+  const long long latent = r + dr;
+  long long off = 0;
+  auto take = [&](long long bytes) {
+    const long long o = off;
+    off = rup(off + bytes, 256);
+    return o;
+  };
+  auto place = [&](Mat& mt) {
+    mt.codes_off = take(mt.codes_bytes);
+    if (mt.scales_bytes) mt.scales_off = take(mt.scales_bytes);
+  };
+  const dspark_weight *a, *b;
+  m.L.assign(c->n_layers, Layer());
+  m.has_mlp = true;
+  for (int l = 0; l < c->n_layers; ++l) {
+    Layer& L = m.L[l];
+    const dspark_weight* v;
+    if ((rc = get_vec(w, n, DSPARK_LAYER_W(l, DSPARK_L_IN_NORM), H, &v))) return rc;
+    L.in_norm = take(H * 4);
+    if ((rc = get_vec(w, n, DSPARK_LAYER_W(l, DSPARK_L_Q_A_NORM), c->q_lora, &v))) return rc;
+    L.q_a_norm = take(c->q_lora * 4);
+    if ((rc = get_vec(w, n, DSPARK_LAYER_W(l, DSPARK_L_KV_A_NORM), r, &v))) return rc;
+    L.kv_a_norm = take(r * 4);
+    if ((rc = get_mat(w, n, DSPARK_LAYER_W(l, DSPARK_L_Q_A), c->q_lora, H, &a))) return rc;
+    if ((rc = get_mat(w, n, DSPARK_LAYER_W(l, DSPARK_L_KV_A), latent, H, &b))) return rc;
+    if (a->dtype != b->dtype) return fail(DSPARK_EUNSUPPORTED, "layer %d: q_a and kv_a dtypes differ", l);
+    mat_geom(L.qkva, a->dtype, 1, (int)(c->q_lora + latent), (int)H);
+    place(L.qkva);
+    if ((rc = get_mat(w, n, DSPARK_LAYER_W(l, DSPARK_L_Q_B), nh * (dn + dr), c->q_lora, &a))) return rc;
+    mat_geom(L.qb, a->dtype, 1, (int)(nh * (dn + dr)), c->q_lora);
+    place(L.qb);
+    if ((rc = get_mat(w, n, DSPARK_LAYER_W(l, DSPARK_L_KV_B), nh * (dn + dv), r, &a))) return rc;
+    if (a->dtype != DSPARK_DT_BF16 && a->dtype != DSPARK_DT_F32)
+      return fail(DSPARK_EUNSUPPORTED, "layer %d: kv_b must be BF16 or F32", l);
+    mat_geom(L.uk, a->dtype, (int)nh, (int)r, (int)dn);
+    place(L.uk);
+    mat_geom(L.uv, a->dtype, (int)nh, (int)dv, (int)r);
+    place(L.uv);
+    if ((rc = get_mat(w, n, DSPARK_LAYER_W(l, DSPARK_L_O), H, nh * dv, &a))) return rc;
+    mat_geom(L.o, a->dtype, 1, (int)H, (int)(nh * dv));
+    place(L.o);
+    const dspark_weight* g = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_GATE));
+    if (!g) {
+      if (!m.layers_only) return fail(DSPARK_EINVAL, "layer %d: gate missing", l);
+      m.has_mlp = false;
+      continue;
+    }
+    if ((rc = get_vec(w, n, DSPARK_LAYER_W(l, DSPARK_L_POST_NORM), H, &v))) return rc;
+    L.post_norm = take(H * 4);
+    if ((rc = get_mat(w, n, DSPARK_LAYER_W(l, DSPARK_L_GATE), c->inter, H, &a))) return rc;
+    if ((rc = get_mat(w, n, DSPARK_LAYER_W(l, DSPARK_L_UP), c->inter, H, &b))) return rc;
+    if (a->dtype != b->dtype) return fail(DSPARK_EUNSUPPORTED, "layer %d: gate and up dtypes differ", l);
+    mat_geom(L.gu, a->dtype, 1, 2 * c->inter, (int)H);
+    place(L.gu);
+    if ((rc = get_mat(w, n, DSPARK_LAYER_W(l, DSPARK_L_DOWN), H, c->inter, &a))) return rc;
+    mat_geom(L.down, a->dtype, 1, (int)H, c->inter);
+    place(L.down);
+  }
+  // one workspace plan serves every layer: all layers must share layer 0's formats
+  for (int l = 1; l < c->n_layers; ++l) {
+    const Layer &A = m.L[0], &B = m.L[l];
+    if (A.qkva.pm.fmt != B.qkva.pm.fmt || A.qb.pm.fmt != B.qb.pm.fmt || A.uk.pm.fmt != B.uk.pm.fmt ||
+        A.o.pm.fmt != B.o.pm.fmt || A.gu.pm.fmt != B.gu.pm.fmt || A.down.pm.fmt != B.down.pm.fmt ||
+        A.gu.present != B.gu.present)
+      return fail(DSPARK_EUNSUPPORTED, "layer %d formats differ from layer 0", l);
+  }
+  if (!m.layers_only) {
+    const dspark_weight* v;
+    if ((rc = get_mat(w, n, DSPARK_W_FC, H, (long long)c->n_captured * H, &a))) return rc;
+    mat_geom(m.fc, a->dtype, 1, (int)H, (int)(c->n_captured * H));
+    place(m.fc);
+    if ((rc = get_vec(w, n, DSPARK_W_FC_NORM, H, &v))) return rc;
+    m.fc_norm = take(H * 4);
+    if ((rc = get_vec(w, n, DSPARK_W_FINAL_NORM, H, &v))) return rc;
+    m.final_norm = take(H * 4);
+    if ((rc = get_mat(w, n, DSPARK_W_LM_HEAD, c->vocab, H, &a))) return rc;
+    mat_geom(m.lm, a->dtype, 1, c->vocab, (int)H);
+    place(m.lm);
+    if ((rc = get_mat(w, n, DSPARK_W_MARKOV_W1, c->vocab, c->markov_rank, &a))) return rc;
+    if ((rc = get_mat(w, n, DSPARK_W_MARKOV_W2, c->vocab, c->markov_rank, &b))) return rc;
+    if ((a->dtype != DSPARK_DT_BF16 && a->dtype != DSPARK_DT_F32) || a->dtype != b->dtype)
+      return fail(DSPARK_EUNSUPPORTED, "Markov W1/W2 must both be BF16 or both F32");
+    mat_geom(m.w2, b->dtype, 1, c->vocab, c->markov_rank);
+    place(m.w2);
+    m.w1_fmt = a->dtype;
+    m.w1_ld = m.w2.pm.Kp;
+    m.w1 = take((long long)c->vocab * m.w1_ld * (a->dtype == DSPARK_DT_F32 ? 4 : 2));
+    if ((rc = get_vec(w, n, DSPARK_W_CONF_W, H + c->markov_rank, &v))) return rc;
+    m.conf_w = take((H + c->markov_rank) * 4);
+    if ((rc = get_vec(w, n, DSPARK_W_CONF_B, 1, &v))) return rc;
+    m.conf_b = take(4);
+  }
+  m.freqs = take((dr / 2) * 8);
+  m.bytes = off;
+  // softmax scale: (0.1 ln s + 1)^2 / sqrt(qk_nope + qk_rope)
+  const double s = c->yarn_factor;
+  const double msc = s > 1.0 ? (0.1 * std::log(s) + 1.0) : 1.0;
+  m.tau = (float)(msc * msc / std::sqrt((double)(dn + dr)));
+  return DSPARK_OK;
+}
+
+// Rope angular frequencies (YaRN NTK-by-parts when yarn_factor > 1), fp64.
+std::vector<double> rope_freqs(const dspark_config& c) {
+  const int d = c.qk_rope;
+  std::vector<double> f(d / 2);
+  const double s = c.yarn_factor, L = c.yarn_orig_ctx;
+  const double lo = c.yarn_beta_slow, hi = c.yarn_beta_fast;
+  for (int k = 0; k < d / 2; ++k) {
+    const double theta = std::pow((double)c.rope_theta, -2.0 * k / d);
+    if (s == 1.0) {
+      f[k] = theta;
+      continue;
+    }
+    const double rot = L * theta / (2.0 * M_PI);  // rotations over the original window
+    double gamma = (rot - lo) / (hi - lo);
+    gamma = gamma < 0 ? 0 : gamma > 1 ? 1 : gamma;
+    f[k] = (1.0 - gamma) * theta / s + gamma * theta;
+  }
+  return f;
+}
+
+void bind(dspark_model& m, Mat& mt) {
+  if (!mt.present) return;
+  mt.pm.codes = m.base + mt.codes_off;
+  mt.pm.scales = mt.scales_off >= 0 ? (const void*)(m.base + mt.scales_off) : nullptr;
+}
+
+int32_t repack(dspark_model& m, Mat& mt, const dspark_weight* src, int xf, int row0, int nrows, hipStream_t st) {
+  RepackArgs a{};
+  a.src = src->data;
+  a.src_fmt = src->dtype;
+  a.src_scales = (const float*)src->scales;
+  a.src_rows = src->rows;
+  a.src_cols = src->cols;
+  a.xf = xf;
+  a.dn = m.c.qk_nope;
+  a.dv = m.c.v_head;
+  a.r = m.c.kv_lora;
+  a.codes = m.base + mt.codes_off;
+  a.scales = mt.scales_off >= 0 ? (void*)(m.base + mt.scales_off) : nullptr;
+  a.dst = mt.pm;
+  a.row0 = row0;
+  a.nrows = nrows;
+  HIPCHK(launch_repack(a, st));
+  return DSPARK_OK;
+}
+
+int32_t copy_vec(dspark_model& m, long long off, const dspark_weight* w, hipStream_t st) {
+  HIPCHK(hipMemcpyAsync(m.base + off, w->data, (size_t)(w->rows * w->cols * 4), hipMemcpyDeviceToDevice, st));
+  return DSPARK_OK;
+}
+
+// ---------------------------------------------------------- workspace plan --
+struct Frag {
+  FragDesc fd{};
+  long long off = 0, bytes = 0;
+};
+
+void frag_geom(Frag& f, const PackedMat& w, int M, bool hilo) {
+  f.fd.f32 = w.fmt == DT_F32;
+  f.fd.hilo = (!f.fd.f32 && hilo) ? 1 : 0;
+  f.fd.KB = w.KB;
+  f.fd.KG = w.Kp / 16;
+  f.fd.MT = f.fd.hilo ? 1 : (M + 15) / 16;
+  const long long per = f.fd.f32 ? (long long)f.fd.MT * f.fd.KG * 64 * 4 : (long long)f.fd.MT * f.fd.KB * 64 * 8;
+  f.fd.gstride = per;
+  f.bytes = per * (f.fd.f32 ? 4 : 2) * w.ngroups;
+}
+
+struct Plan {
+  int n_seq = 0, M = 0;
+  long long total_ctx = 0;
+  bool kv_f32 = false;
+  long long x = 0, part = 0, q = 0, bkeys = 0, opart = 0, mlpart = 0, z = 0, keys = 0, hconf = 0, total = 0;
+  long long zero_begin = 0, zero_end = 0;
+  Frag f_fc, f_qkva, f_qb, f_uk, f_uv, f_o, f_gu, f_down, f_lm;
+  GemvPlan p_fc{}, p_qkva{}, p_qb{}, p_uk{}, p_uv{}, p_o{}, p_gu{}, p_down{}, p_lm{}, p_w2{};
+  int rows = 0, rows_pad = 0, DQ = 0, C = 0, slots = 0;
+};
+
+GemvPlan plan_for(const PackedMat& w, int M, bool allow_split = true) {
+  GemvPlan p = plan_gemv(w, M, false);
+  if (!allow_split && p.S > 1) {
+    const int ksteps = w.fmt == DT_F32 ? (w.Kp >> 4) : w.KB;
+    p.ksteps_per_split = ksteps;
+    p.S = 1;
+  }
+  return p;
+}
+
+void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f32, Plan& P) {
+  const dspark_config& c = m.c;
+  P.n_seq = n_seq;
+  P.total_ctx = total_ctx;
+  P.kv_f32 = kv_f32;
+  const int M = n_seq * c.block;
+  P.M = M;
+  const bool hilo = M <= 8;
+  long long off = 0;
+  auto take = [&](long long bytes) {
+    const long long o = off;
+    off = rup(off + bytes, 256);
+    return o;
+  };
+  const Layer& L0 = m.L[0];
+  P.x = take((long long)M * c.hidden * 4);
+  long long part = 0;
+  auto gp = [&](GemvPlan& gpn, const Mat& mt, bool split = true) {
+    gpn = plan_for(mt.pm, M, split);
+    part = std::max(part, (long long)gpn.S * M * mt.pm.ngroups * mt.pm.G * 4);
+  };
+  gp(P.p_qkva, L0.qkva);
+  gp(P.p_qb, L0.qb);
+  gp(P.p_uk, L0.uk);
+  gp(P.p_uv, L0.uv);
+  gp(P.p_o, L0.o);
+  if (m.has_mlp) {
+    gp(P.p_gu, L0.gu);
+    gp(P.p_down, L0.down);
+  }
+  if (!m.layers_only) {
+    gp(P.p_fc, m.fc);
+    P.p_lm = plan_for(m.lm.pm, M, false);
+    P.p_w2 = plan_gemv(m.w2.pm, n_seq, true);
+  }
+  frag_geom(P.f_qkva, L0.qkva.pm, M, hilo);
+  frag_geom(P.f_qb, L0.qb.pm, M, hilo);
+  frag_geom(P.f_uk, L0.uk.pm, M, hilo);
+  frag_geom(P.f_uv, L0.uv.pm, M, hilo);
+  frag_geom(P.f_o, L0.o.pm, M, hilo);
+  if (m.has_mlp) {
+    frag_geom(P.f_gu, L0.gu.pm, M, hilo);
+    frag_geom(P.f_down, L0.down.pm, M, hilo);
+  }
+  if (!m.layers_only) {
+    frag_geom(P.f_fc, m.fc.pm, M, hilo);
+    frag_geom(P.f_lm, m.lm.pm, M, hilo);
+    P.f_fc.off = take(P.f_fc.bytes);
+  }
+  // zeroed region: fragment buffers, argmax keys and the query buffer
+  P.zero_begin = off;
+  for (Frag* f : {&P.f_qkva, &P.f_qb, &P.f_uk, &P.f_uv, &P.f_o, &P.f_gu, &P.f_down, &P.f_lm})
+    if (f->bytes) f->off = take(f->bytes);
+  P.keys = take((long long)n_seq * c.block * KEY_SLOTS * 8);
+  P.rows = c.block * c.n_heads;
+  P.rows_pad = (int)rup(P.rows, 64);
+  P.DQ = (int)rup(c.kv_lora + c.qk_rope, 32);
+  P.q = take((long long)n_seq * P.rows_pad * P.DQ * (kv_f32 ? 4 : 2));
+  P.zero_end = off;
+  P.part = take(part);
+  P.bkeys = take((long long)M * (c.kv_lora + c.qk_rope) * (kv_f32 ? 4 : 2));
+  P.C = 256;
+  P.slots = (int)(cdiv(total_ctx + (long long)n_seq * c.block, P.C) + n_seq);
+  if (!kv_f32) {
+    P.opart = take((long long)P.slots * P.rows_pad * c.kv_lora * 4);
+    P.mlpart = take((long long)P.slots * P.rows_pad * 2 * 4);
+  }
+  if (!m.layers_only) {
+    P.z = take((long long)M * c.vocab * 4);
+    P.hconf = take((long long)M * 4);
+  }
+  P.total = off;
+}
+
+void bind_frag(Frag& f, unsigned char* ws) {
+  f.fd.ptr = f.bytes ? (void*)(ws + f.off) : nullptr;
+}
+
+// One GEMV launch with the STORE epilogue into the partial buffer.
+hipError_t run_gemv(const Mat& mt, const GemvPlan& p, const Frag& f, int M, float* out, hipStream_t st) {
+  GemvArgs a{};
+  a.w = mt.pm;
+  a.act = f.fd.ptr;
+  a.act_gstride = f.fd.gstride;
+  a.M = M;
+  a.hilo = p.hilo;
+  a.ksteps_per_split = p.ksteps_per_split;
+  a.out = out;
+  a.out_ld = (long long)mt.pm.ngroups * mt.pm.G;
+  a.out_split_stride = (long long)M * a.out_ld;
+  return launch_gemv(a, p, GEMV_STORE, st);
+}
+
+struct Ctx {
+  const dspark_model* m;
+  Plan P;
+  unsigned char* ws;
+  hipStream_t st;
+  float* part() const { return (float*)(ws + P.part); }
+  float* x() const { return (float*)(ws + P.x); }
+};
+
+// Attention half of layer l (input fragments already in f_qkva); leaves the
+// o_proj partials in the partial buffer.
+int32_t attn_half(Ctx& C, int l, const void* kv, const int32_t* offs) {
+  const dspark_model& m = *C.m;
+  const dspark_config& c = m.c;
+  const Layer& L = m.L[l];
+  Plan& P = C.P;
+  const int M = P.M;
+  const double* freqs = (const double*)(m.base + m.freqs);
+  HIPCHK(run_gemv(L.qkva, P.p_qkva, P.f_qkva, M, C.part(), C.st));
+  {
+    QkvaArgs a{};
+    a.part = C.part();
+    a.S = P.p_qkva.S;
+    a.part_ld = L.qkva.pm.G;
+    a.part_ss = (long long)M * a.part_ld;
+    a.M = M;
+    a.q_lora = c.q_lora;
+    a.r = c.kv_lora;
+    a.dr = c.qk_rope;
+    a.latent = c.kv_lora + c.qk_rope;
+    a.block = c.block;
+    a.g_qa = (const float*)(m.base + L.q_a_norm);
+    a.g_kva = (const float*)(m.base + L.kv_a_norm);
+    a.eps = c.rms_eps;
+    a.fd_qb = P.f_qb.fd;
+    a.bkeys = C.ws + P.bkeys;
+    a.kv_f32 = P.kv_f32;
+    a.offs = offs;
+    a.freqs = freqs;
+    HIPCHK(launch_qkva_post(a, C.st));
+  }
+  HIPCHK(run_gemv(L.qb, P.p_qb, P.f_qb, M, C.part(), C.st));
+  {
+    QbArgs a{};
+    a.part = C.part();
+    a.S = P.p_qb.S;
+    a.part_ld = L.qb.pm.G;
+    a.part_ss = (long long)M * a.part_ld;
+    a.M = M;
+    a.nh = c.n_heads;
+    a.dn = c.qk_nope;
+    a.dr = c.qk_rope;
+    a.r = c.kv_lora;
+    a.block = c.block;
+    a.DQ = P.DQ;
+    a.rows_pad = P.rows_pad;
+    a.fd_uk = P.f_uk.fd;
+    a.q = C.ws + P.q;
+    a.q_f32 = P.kv_f32;
+    a.offs = offs;
+    a.freqs = freqs;
+    HIPCHK(launch_qb_post(a, C.st));
+  }
+  HIPCHK(run_gemv(L.uk, P.p_uk, P.f_uk, M, C.part(), C.st));
+  {
+    AbsorbArgs a{};
+    a.part = C.part();
+    a.part_ld = (long long)L.uk.pm.ngroups * L.uk.pm.G;
+    a.M = M;
+    a.nh = c.n_heads;
+    a.r = c.kv_lora;
+    a.block = c.block;
+    a.DQ = P.DQ;
+    a.rows_pad = P.rows_pad;
+    a.q = C.ws + P.q;
+    a.q_f32 = P.kv_f32;
+    if (P.p_uk.S != 1) return fail(DSPARK_EUNSUPPORTED, "absorb GEMM planned with split-K");
+    HIPCHK(launch_absorb_post(a, C.st));
+  }
+  {
+    AttnArgs a{};
+    a.q = C.ws + P.q;
+    a.cache = kv;
+    a.bkeys = C.ws + P.bkeys;
+    a.offs = offs;
+    a.n_seq = P.n_seq;
+    a.block = c.block;
+    a.nh = c.n_heads;
+    a.rows = P.rows;
+    a.rows_pad = P.rows_pad;
+    a.latent = c.kv_lora + c.qk_rope;
+    a.r = c.kv_lora;
+    a.DQ = P.DQ;
+    a.C = P.C;
+    a.slots = P.slots;
+    a.tau = m.tau;
+    a.fd_uv = P.f_uv.fd;
+    if (P.kv_f32) {
+      HIPCHK(launch_attn_f32(a, C.st));
+    } else {
+      a.o_part = (float*)(C.ws + P.opart);
+      a.ml_part = (float*)(C.ws + P.mlpart);
+      HIPCHK(launch_attn_bf16(a, C.st));
+      HIPCHK(launch_attn_combine(a, C.st));
+    }
+  }
+  HIPCHK(run_gemv(L.uv, P.p_uv, P.f_uv, M, C.part(), C.st));
+  {
+    FragArgs a{};
+    a.part = C.part();
+    a.S = P.p_uv.S;
+    a.part_ld = (long long)L.uv.pm.ngroups * L.uv.pm.G;
+    a.part_ss = (long long)M * a.part_ld;
+    a.M = M;
+    a.K = c.n_heads * c.v_head;
+    a.fd = P.f_o.fd;
+    HIPCHK(launch_to_frag(a, C.st));
+  }
+  HIPCHK(run_gemv(L.o, P.p_o, P.f_o, M, C.part(), C.st));
+  return DSPARK_OK;
+}
+
+// SwiGLU half of layer l (input fragments in f_gu); leaves down partials.
+int32_t mlp_half(Ctx& C, int l) {
+  const dspark_model& m = *C.m;
+  const Layer& L = m.L[l];
+  Plan& P = C.P;
+  const int M = P.M;
+  HIPCHK(run_gemv(L.gu, P.p_gu, P.f_gu, M, C.part(), C.st));
+  FragArgs a{};
+  a.part = C.part();
+  a.S = P.p_gu.S;
+  a.part_ld = L.gu.pm.G;
+  a.part_ss = (long long)M * a.part_ld;
+  a.M = M;
+  a.K = m.c.inter;
+  a.fd = P.f_down.fd;
+  a.swiglu = 1;
+  HIPCHK(launch_to_frag(a, C.st));
+  HIPCHK(run_gemv(L.down, P.p_down, P.f_down, M, C.part(), C.st));
+  return DSPARK_OK;
+}
+
+ResidArgs resid_base(Ctx& C, const GemvPlan& p, const Mat& mt) {
+  ResidArgs a{};
+  a.part = C.part();
+  a.S = p.S;
+  a.part_ld = (long long)mt.pm.ngroups * mt.pm.G;
+  a.part_ss = (long long)C.P.M * a.part_ld;
+  a.x_in = C.x();
+  a.x_out = C.x();
+  a.mode = RESID_ADD;
+  a.eps = C.m->c.rms_eps;
+  a.M = C.P.M;
+  a.H = C.m->c.hidden;
+  return a;
+}
+
+int32_t check_ws(const Plan& P, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(DSPARK_EINVAL, "workspace is NULL");
+  if ((uintptr_t)ws % 256) return fail(DSPARK_EINVAL, "workspace must be 256-byte aligned");
+  if ((long long)ws_bytes < P.total)
+    return fail(DSPARK_EWORKSPACE, "workspace %zu bytes, need %lld", ws_bytes, P.total);
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+// ============================================================== the C ABI ==
+extern "C" {
+
+const char* dspark_last_error(void) { return g_err.c_str(); }
+
+size_t dspark_packed_bytes(const dspark_config* cfg, const dspark_weight* w, int32_t n) {
+  dspark_model m;
+  if (build_plan(cfg, w, n, m)) return 0;
+  return (size_t)m.bytes;
+}
+
+int32_t dspark_model_create(const dspark_config* cfg, const dspark_weight* w, int32_t n, void* packed_buf,
+                            size_t packed_bytes, void* stream, dspark_model** out) {
+  g_err.clear();
+  if (!out) return fail(DSPARK_EINVAL, "out is NULL");
+  *out = nullptr;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(DSPARK_ENODEVICE, "no HIP device");
+  dspark_model* m = new dspark_model();
+  int32_t rc = build_plan(cfg, w, n, *m);
+  if (rc) {
+    delete m;
+    return rc;
+  }
+  if (!packed_buf || (uintptr_t)packed_buf % 256) {
+    delete m;
+    return fail(DSPARK_EINVAL, "packed_buf NULL or not 256-byte aligned");
+  }
+  if ((long long)packed_bytes < m->bytes) {
+    const long long need = m->bytes;
+    delete m;
+    return fail(DSPARK_EWORKSPACE, "packed buffer %zu bytes, need %lld", packed_bytes, need);
+  }
+  m->base = (unsigned char*)packed_buf;
+  hipStream_t st = (hipStream_t)stream;
+  auto body = [&]() -> int32_t {
+    const dspark_config& c = m->c;
+    HIPCHK(hipMemsetAsync(m->base, 0, (size_t)m->bytes, st));
+    for (Mat* mt : {&m->fc, &m->lm, &m->w2}) bind(*m, *mt);
+    for (int l = 0; l < c.n_layers; ++l) {
+      Layer& L = m->L[l];
+      for (Mat* mt : {&L.qkva, &L.qb, &L.uk, &L.uv, &L.o, &L.gu, &L.down}) bind(*m, *mt);
+      const dspark_weight* x;
+      int32_t r2;
+      x = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_Q_A));
+      if ((r2 = repack(*m, L.qkva, x, XF_NORMAL, 0, c.q_lora, st))) return r2;
+      x = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_KV_A));
+      if ((r2 = repack(*m, L.qkva, x, XF_NORMAL, c.q_lora, c.kv_lora + c.qk_rope, st))) return r2;
+      x = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_Q_B));
+      if ((r2 = repack(*m, L.qb, x, XF_NORMAL, 0, L.qb.pm.G, st))) return r2;
+      x = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_KV_B));
+      if ((r2 = repack(*m, L.uk, x, XF_UK, 0, c.n_heads * c.kv_lora, st))) return r2;
+      if ((r2 = repack(*m, L.uv, x, XF_UV, 0, c.n_heads * c.v_head, st))) return r2;
+      x = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_O));
+      if ((r2 = repack(*m, L.o, x, XF_NORMAL, 0, c.hidden, st))) return r2;
+      if ((r2 = copy_vec(*m, L.in_norm, find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_IN_NORM)), st))) return r2;
+      if ((r2 = copy_vec(*m, L.q_a_norm, find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_Q_A_NORM)), st))) return r2;
+      if ((r2 = copy_vec(*m, L.kv_a_norm, find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_KV_A_NORM)), st))) return r2;
+      if (L.gu.present) {
+        x = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_GATE));
+        if ((r2 = repack(*m, L.gu, x, XF_NORMAL, 0, c.inter, st))) return r2;
+        x = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_UP));
+        if ((r2 = repack(*m, L.gu, x, XF_NORMAL, c.inter, c.inter, st))) return r2;
+        x = find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_DOWN));
+        if ((r2 = repack(*m, L.down, x, XF_NORMAL, 0, c.hidden, st))) return r2;
+        if ((r2 = copy_vec(*m, L.post_norm, find_w(w, n, DSPARK_LAYER_W(l, DSPARK_L_POST_NORM)), st))) return r2;
+      }
+    }
+    if (!m->layers_only) {
+      int32_t r2;
+      if ((r2 = repack(*m, m->fc, find_w(w, n, DSPARK_W_FC), XF_NORMAL, 0, c.hidden, st))) return r2;
+      if ((r2 = repack(*m, m->lm, find_w(w, n, DSPARK_W_LM_HEAD), XF_NORMAL, 0, c.vocab, st))) return r2;
+      if ((r2 = repack(*m, m->w2, find_w(w, n, DSPARK_W_MARKOV_W2), XF_NORMAL, 0, c.vocab, st))) return r2;
+      const dspark_weight* w1 = find_w(w, n, DSPARK_W_MARKOV_W1);
+      const size_t esz = m->w1_fmt == DT_F32 ? 4 : 2;
+      HIPCHK(hipMemcpy2DAsync(m->base + m->w1, (size_t)m->w1_ld * esz, w1->data, (size_t)c.markov_rank * esz,
+                              (size_t)c.markov_rank * esz, (size_t)c.vocab, hipMemcpyDeviceToDevice, st));
+      if ((r2 = copy_vec(*m, m->fc_norm, find_w(w, n, DSPARK_W_FC_NORM), st))) return r2;
+      if ((r2 = copy_vec(*m, m->final_norm, find_w(w, n, DSPARK_W_FINAL_NORM), st))) return r2;
+      if ((r2 = copy_vec(*m, m->conf_w, find_w(w, n, DSPARK_W_CONF_W), st))) return r2;
+      if ((r2 = copy_vec(*m, m->conf_b, find_w(w, n, DSPARK_W_CONF_B), st))) return r2;
+    }
+    const std::vector<double> f = rope_freqs(c);
+    HIPCHK(hipMemcpyAsync(m->base + m->freqs, f.data(), f.size() * 8, hipMemcpyHostToDevice, st));
+    HIPCHK(hipStreamSynchronize(st));
+    return DSPARK_OK;
+  };
+  rc = body();
+  if (rc) {
+    delete m;
+    return rc;
+  }
+  *out = m;
+  return DSPARK_OK;
+}
+
+int32_t dspark_model_destroy(dspark_model* m) {
+  delete m;
+  return DSPARK_OK;
+}
+
+size_t dspark_workspace_bytes(const dspark_model* m, int32_t n_seq, int64_t total_ctx) {
+  if (!m || n_seq < 1 || total_ctx < 0) {
+    fail(DSPARK_EINVAL, "workspace query: bad model / n_seq / total_ctx");
+    return 0;
+  }
+  // size for the larger of the two KV precisions
+  Plan a, b;
+  make_plan(*m, n_seq, total_ctx, false, a);
+  make_plan(*m, n_seq, total_ctx, true, b);
+  return (size_t)std::max(a.total, b.total);
+}
+
+int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dspark_block_out* out, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!m || !in || !out) return fail(DSPARK_EINVAL, "model / in / out is NULL");
+  if (m->layers_only) return fail(DSPARK_EINVAL, "model holds decoder layers only");
+  const dspark_config& c = m->c;
+  if (in->n_seq < 1) return fail(DSPARK_EINVAL, "n_seq < 1");
+  if (in->n_seq > 16) return fail(DSPARK_EUNSUPPORTED, "n_seq > 16");
+  if (in->total_ctx < 0) return fail(DSPARK_EINVAL, "total_ctx < 0");
+  if (!in->captured || !in->kv || !in->kv_offsets || !in->prev_token || !out->tokens || !out->conf)
+    return fail(DSPARK_EINVAL, "a required pointer is NULL");
+  if (in->act_dtype != DSPARK_DT_F32 && in->act_dtype != DSPARK_DT_BF16)
+    return fail(DSPARK_EINVAL, "act_dtype must be F32 or BF16");
+  if (in->kv_dtype != DSPARK_DT_F32 && in->kv_dtype != DSPARK_DT_BF16)
+    return fail(DSPARK_EINVAL, "kv_dtype must be F32 or BF16");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!in->kv[l] && in->total_ctx > 0) return fail(DSPARK_EINVAL, "kv[%d] is NULL", l);
+  const bool kv_f32 = in->kv_dtype == DSPARK_DT_F32;
+  Ctx C;
+  C.m = m;
+  make_plan(*m, in->n_seq, in->total_ctx, kv_f32, C.P);
+  if (!kv_f32 && !attn_bf16_supported(C.P.DQ, c.kv_lora))
+    return fail(DSPARK_EUNSUPPORTED, "no bf16 attention kernel for latent %d / kv_lora %d", c.kv_lora + c.qk_rope,
+                c.kv_lora);
+  if (kv_f32 && (c.kv_lora + c.qk_rope > 1024)) return fail(DSPARK_EUNSUPPORTED, "f32 latent > 1024");
+  int32_t rc = check_ws(C.P, workspace, ws_bytes);
+  if (rc) return rc;
+  C.ws = (unsigned char*)workspace;
+  C.st = (hipStream_t)stream;
+  Plan& P = C.P;
+  for (Frag* f : {&P.f_fc, &P.f_qkva, &P.f_qb, &P.f_uk, &P.f_uv, &P.f_o, &P.f_gu, &P.f_down, &P.f_lm}) bind_frag(*f, C.ws);
+  const int M = P.M;
+  {
+    InitArgs a{};
+    a.zero_ptr = C.ws + P.zero_begin;
+    a.zero_bytes = P.zero_end - P.zero_begin;
+    a.captured = in->captured;
+    a.cap_f32 = in->act_dtype == DSPARK_DT_F32;
+    a.n_seq = in->n_seq;
+    a.ncap = c.n_captured;
+    a.block = c.block;
+    a.H = c.hidden;
+    a.fd_fc = P.f_fc.fd;
+    HIPCHK(launch_init(a, C.st));
+  }
+  HIPCHK(run_gemv(m->fc, P.p_fc, P.f_fc, M, C.part(), C.st));
+  {
+    ResidArgs a = resid_base(C, P.p_fc, m->fc);
+    a.mode = RESID_NORM_FIRST;
+    a.x_in = nullptr;
+    a.g0 = (const float*)(m->base + m->fc_norm);
+    a.g1 = (const float*)(m->base + m->L[0].in_norm);
+    a.fd = P.f_qkva.fd;
+    HIPCHK(launch_resid_norm(a, C.st));
+  }
+  for (int l = 0; l < c.n_layers; ++l) {
+    if ((rc = attn_half(C, l, in->kv[l], in->kv_offsets))) return rc;
+    {
+      ResidArgs a = resid_base(C, P.p_o, m->L[l].o);
+      a.g1 = (const float*)(m->base + m->L[l].post_norm);
+      a.fd = P.f_gu.fd;
+      HIPCHK(launch_resid_norm(a, C.st));
+    }
+    if ((rc = mlp_half(C, l))) return rc;
+    {
+      ResidArgs a = resid_base(C, P.p_down, m->L[l].down);
+      if (l + 1 < c.n_layers) {
+        a.g1 = (const float*)(m->base + m->L[l + 1].in_norm);
+        a.fd = P.f_qkva.fd;
+      } else {
+        a.g1 = (const float*)(m->base + m->final_norm);
+        a.fd = P.f_lm.fd;
+        a.hidden_out = out->hidden;
+        a.conf_wh = (const float*)(m->base + m->conf_w);
+        a.hconf = (float*)(C.ws + P.hconf);
+      }
+      HIPCHK(launch_resid_norm(a, C.st));
+    }
+  }
+  float* z = (float*)(C.ws + P.z);
+  HIPCHK(run_gemv(m->lm, P.p_lm, P.f_lm, M, z, C.st));
+  for (int i = 0; i < c.block; ++i) {
+    GemvArgs a{};
+    a.w = m->w2.pm;
+    a.act = m->base + m->w1;
+    a.M = in->n_seq;
+    a.ksteps_per_split = P.p_w2.ksteps_per_split;
+    a.gather_ld = m->w1_ld;
+    a.prev_token = in->prev_token;
+    a.forced = in->forced_prev;
+    a.keys = (unsigned long long*)(C.ws + P.keys);
+    a.step = i;
+    a.block = c.block;
+    a.z = z;
+    a.logits = out->logits;
+    HIPCHK(launch_gemv(a, P.p_w2, GEMV_MARKOV, C.st));
+  }
+  {
+    MarkovFinalArgs a{};
+    a.keys = (const unsigned long long*)(C.ws + P.keys);
+    a.prev_token = in->prev_token;
+    a.forced = in->forced_prev;
+    a.w1 = m->base + m->w1;
+    a.w1_f32 = m->w1_fmt == DT_F32;
+    a.w1_ld = m->w1_ld;
+    a.R = c.markov_rank;
+    a.conf_wm = (const float*)(m->base + m->conf_w) + c.hidden;
+    a.conf_b = (const float*)(m->base + m->conf_b);
+    a.hconf = (const float*)(C.ws + P.hconf);
+    a.tokens = out->tokens;
+    a.conf = out->conf;
+    a.n_seq = in->n_seq;
+    a.block = c.block;
+    a.vocab = c.vocab;
+    HIPCHK(launch_markov_final(a, C.st));
+  }
+  return DSPARK_OK;
+}
+
+int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_mlp, int32_t n_seq, const float* x_in,
+                             float* x_out, const void* kv, int32_t kv_dtype, const int32_t* kv_offsets,
+                             int64_t total_ctx, void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!m) return fail(DSPARK_EINVAL, "model is NULL");
+  const dspark_config& c = m->c;
+  if (layer < 0 || layer >= c.n_layers) return fail(DSPARK_EINVAL, "layer %d out of range", layer);
+  if (with_mlp && !m->L[layer].gu.present) return fail(DSPARK_EINVAL, "layer %d has no MLP weights", layer);
+  if (n_seq < 1) return fail(DSPARK_EINVAL, "n_seq < 1");
+  if (!x_in || !x_out || !kv_offsets || (!kv && total_ctx > 0)) return fail(DSPARK_EINVAL, "a required pointer is NULL");
+  if (kv_dtype != DSPARK_DT_F32 && kv_dtype != DSPARK_DT_BF16) return fail(DSPARK_EINVAL, "bad kv_dtype");
+  if (total_ctx < 0) return fail(DSPARK_EINVAL, "total_ctx < 0");
+  const bool kv_f32 = kv_dtype == DSPARK_DT_F32;
+  Ctx C;
+  C.m = m;
+  make_plan(*m, n_seq, total_ctx, kv_f32, C.P);
+  if (!kv_f32 && !attn_bf16_supported(C.P.DQ, c.kv_lora))
+    return fail(DSPARK_EUNSUPPORTED, "no bf16 attention kernel for this latent size");
+  int32_t rc = check_ws(C.P, workspace, ws_bytes);
+  if (rc) return rc;
+  C.ws = (unsigned char*)workspace;
+  C.st = (hipStream_t)stream;
+  Plan& P = C.P;
+  for (Frag* f : {&P.f_qkva, &P.f_qb, &P.f_uk, &P.f_uv, &P.f_o, &P.f_gu, &P.f_down}) bind_frag(*f, C.ws);
+  {
+    InitArgs a{};
+    a.zero_ptr = C.ws + P.zero_begin;
+    a.zero_bytes = P.zero_end - P.zero_begin;
+    HIPCHK(launch_init(a, C.st));
+  }
+  const Layer& L = m->L[layer];
+  {
+    ResidArgs a = resid_base(C, P.p_o, L.o);
+    a.mode = RESID_COPY;
+    a.x_in = x_in;
+    a.g1 = (const float*)(m->base + L.in_norm);
+    a.fd = P.f_qkva.fd;
+    HIPCHK(launch_resid_norm(a, C.st));
+  }
+  if ((rc = attn_half(C, layer, kv, kv_offsets))) return rc;
+  ResidArgs a = resid_base(C, P.p_o, L.o);
+  if (!with_mlp) {
+    a.x_out = x_out;
+    HIPCHK(launch_resid_norm(a, C.st));
+    return DSPARK_OK;
+  }
+  a.g1 = (const float*)(m->base + L.post_norm);
+  a.fd = P.f_gu.fd;
+  HIPCHK(launch_resid_norm(a, C.st));
+  if ((rc = mlp_half(C, layer))) return rc;
+  ResidArgs b = resid_base(C, P.p_down, L.down);
+  b.x_out = x_out;
+  HIPCHK(launch_resid_norm(b, C.st));
+  return DSPARK_OK;
+}
+
+int32_t dspark_accept_len_host(const int32_t* draft, const int32_t* verifier, int32_t n_seq, int32_t block,
+                               int32_t* out_len) {
+  g_err.clear();
+  if (!draft || !verifier || !out_len) return fail(DSPARK_EINVAL, "NULL pointer");
+  if (n_seq < 0 || block < 0) return fail(DSPARK_EINVAL, "negative n_seq / block");
+  for (int s = 0; s < n_seq; ++s) {
+    int k = 0;
+    while (k < block && draft[(long long)s * block + k] == verifier[(long long)s * block + k]) ++k;
+    out_len[s] = k;
+  }
+  return DSPARK_OK;
+}
+
+int32_t dspark_accept_len(const int32_t* draft, const int32_t* verifier, int32_t n_seq, int32_t block,
+                          int32_t* out_len, void* stream) {
+  g_err.clear();
+  if (!draft || !verifier || !out_len) return fail(DSPARK_EINVAL, "NULL pointer");
+  if (n_seq < 0 || block < 0) return fail(DSPARK_EINVAL, "negative n_seq / block");
+  if (n_seq == 0) return DSPARK_OK;
+  HIPCHK(launch_accept_len(draft, verifier, n_seq, block, out_len, (hipStream_t)stream));
+  return DSPARK_OK;
+}
+
+int32_t dspark_dequant(const dspark_model* m, int32_t id, float* out, void* stream) {
+  g_err.clear();
+  if (!m || !out) return fail(DSPARK_EINVAL, "NULL pointer");
+  const Mat* mt = nullptr;
+  if (id == DSPARK_W_FC) mt = &m->fc;
+  else if (id == DSPARK_W_LM_HEAD) mt = &m->lm;
+  else if (id == DSPARK_W_MARKOV_W2) mt = &m->w2;
+  else if (id >= DSPARK_W_LAYER_BASE) {
+    const int l = (id - DSPARK_W_LAYER_BASE) / DSPARK_W_LAYER_STRIDE, k = (id - DSPARK_W_LAYER_BASE) % DSPARK_W_LAYER_STRIDE;
+    if (l < m->c.n_layers) {
+      const Layer& L = m->L[l];
+      switch (k) {
+        case DSPARK_L_Q_B: mt = &L.qb; break;
+        case DSPARK_L_O: mt = &L.o; break;
+        case DSPARK_L_DOWN: mt = &L.down; break;
+        case DSPARK_L_GATE: mt = &L.gu; break;   // gate rows then up rows
+        case DSPARK_L_Q_A: mt = &L.qkva; break;  // q_a rows then kv_a rows
+        default: break;
+      }
+    }
+  }
+  if (!mt || !mt->present) return fail(DSPARK_EINVAL, "weight id %d has no packed matrix to decode", id);
+  HIPCHK(launch_dequant(mt->pm, out, (hipStream_t)stream));
+  return DSPARK_OK;
+}
+
+}  // extern "C"

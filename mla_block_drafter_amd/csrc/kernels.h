@@ -1,0 +1,157 @@
+// Launch interfaces of the DSpark HIP kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace dspark {
+
+// ------------------------------------------------------------- skinny GEMM --
+// out[split][m][col] = sum over the split's k range of act[m][k] * W[col][k]
+// for the M activation rows (M = 7 per sequence), W streamed once from HBM.
+enum { GEMV_STORE = 0, GEMV_MARKOV = 1 };
+
+struct GemvArgs {
+  PackedMat w;
+  const void* act;        // fragment buffer (STORE) or plain gather table (MARKOV)
+  long long act_gstride;  // elements per group in the fragment buffer
+  int M;                  // valid activation rows
+  int hilo;               // bf16 family with M <= 8
+  int ksteps_per_split;   // in 32-wide blocks (bf16 family) or 16-wide groups (f32)
+  // STORE
+  float* out;             // [S][M][out_ld]
+  long long out_ld;
+  long long out_split_stride;
+  // MARKOV: M = n_seq; activation row m = W1[t_prev(m)], t_prev resolved in-kernel
+  int gather_ld;          // elements per table row (>= Kp)
+  const int32_t* prev_token;
+  const int32_t* forced;
+  unsigned long long* keys;  // [n_seq][block][KEY_SLOTS]
+  int step, block;
+  const float* z;         // [n_seq*block][V]
+  float* logits;          // optional [n_seq][block][V]
+};
+
+struct GemvPlan {
+  int MT, TPW, S, ksteps_per_split, hilo;
+  int grid_x;
+};
+
+GemvPlan plan_gemv(const PackedMat& w, int M, bool markov);
+hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
+
+// --------------------------------------------------------------- attention --
+struct AttnArgs {
+  const void* q;          // [n_seq][rows_pad][DQ] (bf16 or f32)
+  const void* cache;      // [total][latent]
+  const void* bkeys;      // [n_seq*block][latent]
+  const int32_t* offs;    // [n_seq + 1]
+  int n_seq, block, nh, rows, rows_pad, latent, r, DQ;
+  int C;                  // keys per split (multiple of 32)
+  int slots;              // slot bound (grid.y)
+  float tau;
+  float* o_part;          // [slots][rows_pad][r]
+  float* ml_part;         // [slots][rows_pad][2]
+  FragDesc fd_uv;         // output fragments (un-absorb input, grouped by head)
+};
+
+bool attn_bf16_supported(int DQ, int r);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
+
+// ------------------------------------------------------------ elementwise --
+struct InitArgs {
+  void* zero_ptr;         // 16-byte aligned
+  long long zero_bytes;   // multiple of 16
+  // fc input fragments (optional: captured == nullptr to skip)
+  const void* captured;   // [n_seq][ncap][block][H]
+  int cap_f32;
+  int n_seq, ncap, block, H;
+  FragDesc fd_fc;
+};
+hipError_t launch_init(const InitArgs& a, hipStream_t st);
+
+enum { RESID_COPY = 0, RESID_ADD = 1, RESID_NORM_FIRST = 2 };
+struct ResidArgs {
+  const float* part; int S; long long part_ld, part_ss;
+  const float* x_in; float* x_out;
+  int mode;
+  const float* g0;        // NORM_FIRST gain
+  const float* g1;        // gain of the normed output fed to the next GEMM (null: none)
+  float eps;
+  int M, H;
+  FragDesc fd;            // next GEMM input
+  float* hidden_out;      // optional [M][H] normed output
+  const float* conf_wh;   // optional [H]: hconf[m] = normed . conf_wh
+  float* hconf;
+};
+hipError_t launch_resid_norm(const ResidArgs& a, hipStream_t st);
+
+struct QkvaArgs {
+  const float* part; int S; long long part_ld, part_ss;
+  int M, q_lora, r, dr, latent, block;
+  const float* g_qa; const float* g_kva; float eps;
+  FragDesc fd_qb;
+  void* bkeys; int kv_f32;   // [M][latent]
+  const int32_t* offs;
+  const double* freqs;        // [dr/2]
+};
+hipError_t launch_qkva_post(const QkvaArgs& a, hipStream_t st);
+
+struct QbArgs {
+  const float* part; int S; long long part_ld, part_ss;
+  int M, nh, dn, dr, r, block, DQ, rows_pad;
+  FragDesc fd_uk;             // absorb input, groups = heads
+  void* q; int q_f32;         // [n_seq][rows_pad][DQ]
+  const int32_t* offs;
+  const double* freqs;
+};
+hipError_t launch_qb_post(const QbArgs& a, hipStream_t st);
+
+struct AbsorbArgs {
+  const float* part; long long part_ld;   // [M][nh*r]
+  int M, nh, r, block, DQ, rows_pad;
+  void* q; int q_f32;
+};
+hipError_t launch_absorb_post(const AbsorbArgs& a, hipStream_t st);
+
+struct FragArgs {           // plain copy of GEMM output into the next fragments
+  const float* part; int S; long long part_ld, part_ss;
+  int M, K;
+  FragDesc fd;
+  int swiglu;               // 1: value = silu(part[k]) * part[K + k]
+};
+hipError_t launch_to_frag(const FragArgs& a, hipStream_t st);
+
+struct MarkovFinalArgs {
+  const unsigned long long* keys;
+  const int32_t* prev_token; const int32_t* forced;
+  const void* w1; int w1_f32; int w1_ld; int R;
+  const float* conf_wm; const float* conf_b; const float* hconf;
+  int32_t* tokens; float* conf;
+  int n_seq, block, vocab;
+};
+hipError_t launch_markov_final(const MarkovFinalArgs& a, hipStream_t st);
+
+hipError_t launch_accept_len(const int32_t* d, const int32_t* v, int n_seq, int block, int32_t* out,
+                             hipStream_t st);
+
+// ---------------------------------------------------------------- repack --
+enum { XF_NORMAL = 0, XF_UK = 1, XF_UV = 2 };
+struct RepackArgs {
+  const void* src; int src_fmt; const float* src_scales;
+  long long src_rows, src_cols;   // source tensor geometry
+  int xf;                         // transform
+  int dn, dv, r;                  // kv_b geometry (XF_UK / XF_UV)
+  unsigned char* codes; void* scales;  // destination planes
+  PackedMat dst;
+  int row0;                       // destination logical row of source row 0 (XF_NORMAL)
+  int nrows;                      // destination logical rows written
+};
+hipError_t launch_repack(const RepackArgs& a, hipStream_t st);
+hipError_t launch_dequant(const PackedMat& w, float* out, hipStream_t st);
+
+}  // namespace dspark

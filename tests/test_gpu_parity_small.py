@@ -1,0 +1,133 @@
+"""GPU parity at sizes the oracle finishes in seconds: the tiny all-fp32
+drafter and a ragged mid-size geometry (hidden 352, vocab 1000, inter 480,
+v_head 24, three sequences with cache lengths 0 / 37 / 300) in every weight
+format, plus decoding and acceptance checks."""
+import itertools
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import codecs, dspark as O
+from synth import configs as C, gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mla_block_drafter_amd import dspark as D
+    D.lib()
+
+
+def _gw(wl):
+    from tests.gpu_common import GpuWorkload
+    return GpuWorkload(wl)
+
+
+SMALL = C.small_model()
+FORMATS = {
+    "bf16": C.ALL_BF16,
+    "q8_0": C.Q8,
+    "fp8": C.FP8_PC,
+    "f32w_bf16kv": C.Formats(fc="f32", q_a="f32", q_b="f32", kv_b="f32", o="f32", mlp="f32",
+                              lm_head="f32", markov="f32"),
+}
+
+
+def test_tiny_f32_exact_tokens():
+    """The tiny all-fp32 drafter: tokens exact (no near-ties), fp32 tolerance."""
+    from tests.gpu_common import full_parity
+    wl = C.CFG1.replace(fixture_gains=True)
+    g = _gw(wl)
+    ref = O.draft_block(wl, g.stored, g.inputs)
+    print("tiny ref tokens", ref["tokens"].tolist(), flush=True)
+    out, free, ties = full_parity(g, ref, tol=1e-4, max_ties=0)
+    np.testing.assert_array_equal(free["tokens"], ref["tokens"])
+    np.testing.assert_array_equal(out["tokens"], ref["tokens"])
+
+
+def test_tiny_metric_config_and_markov_dominant():
+    from tests.gpu_common import full_parity
+    for wl in (C.CFG1, C.CFG1.replace(markov_dominant=True, fixture_gains=True)):
+        g = _gw(wl)
+        ref = O.draft_block(wl, g.stored, g.inputs)
+        out, free, ties = full_parity(g, ref, tol=1e-4, max_ties=0)
+        np.testing.assert_array_equal(free["tokens"], ref["tokens"])
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_small_ragged_all_formats(fmt):
+    from tests.gpu_common import full_parity
+    wl = C.Workload(f"small_{fmt}", SMALL, FORMATS[fmt], seed=777, kv_lens=(0, 37, 300),
+                    fixture_gains=True)
+    g = _gw(wl)
+    ref = O.draft_block(wl, g.stored, g.inputs)
+    out, free, ties = full_parity(g, ref, tol=2e-2, max_ties=2)
+    print(fmt, "near-ties", ties, flush=True)
+
+
+def test_small_sharp_attention_bf16():
+    from tests.gpu_common import full_parity
+    wl = C.Workload("small_sharp", SMALL, C.ALL_BF16, seed=778, kv_lens=(129,), fixture_gains=True,
+                    sharp_attention=True)
+    g = _gw(wl)
+    ref = O.draft_block(wl, g.stored, g.inputs)
+    full_parity(g, ref, tol=2e-2, max_ties=2)
+
+
+def test_dequant_bit_exact():
+    """Decoding the repacked planes gives exactly the oracle's decoded values
+    (Q8_0 d*q and bf16 exact in fp32; FP8 s*e4m3(q) correctly rounded)."""
+    from mla_block_drafter_amd import dspark as D
+    for fmt, names in [("q8_0", ["L0.q_b", "L1.o", "L0.down", "fc"]), ("fp8", ["L0.q_b", "L1.down", "fc"]),
+                       ("bf16", ["lm_head", "L0.o", "markov_w2"]), ("f32w_bf16kv", ["L0.o", "lm_head"])]:
+        wl = C.Workload("deq", SMALL, FORMATS[fmt], seed=31, kv_lens=(5,))
+        g = _gw(wl)
+        for name in names:
+            st = g.stored[name]
+            rows, cols = st.shape
+            out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+            g.model.dequant(name, out)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            want = codecs.decode(st).astype(np.float32)   # exact for q8_0 / bf16 / f32; RNE for fp8
+            np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32), err_msg=f"{fmt} {name}")
+        # fused gate/up and q_a/kv_a decode as stacked rows
+        out = torch.empty((2 * SMALL.inter, SMALL.hidden), dtype=torch.float32, device="cuda")
+        g.model.dequant("L0.gate", out)
+        torch.cuda.synchronize()
+        want = np.concatenate([codecs.decode(g.stored["L0.gate"]), codecs.decode(g.stored["L0.up"])])
+        np.testing.assert_array_equal(out.cpu().numpy(), want.astype(np.float32))
+
+
+def test_accept_len_device_brute_force():
+    from mla_block_drafter_amd import dspark as D
+    for alpha, blk in [(3, 4), (2, 7)]:
+        seqs = np.array(list(itertools.product(range(alpha), repeat=blk)), dtype=np.int32)
+        rng = np.random.default_rng(blk)
+        d = seqs[rng.integers(0, len(seqs), size=len(seqs))]
+        dt, vt = torch.from_numpy(d).cuda(), torch.from_numpy(seqs).cuda()
+        out = torch.empty(len(seqs), dtype=torch.int32, device="cuda")
+        D.accept_len(dt, vt, out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy(), O.accept_len(d, seqs))
+    # planted first mismatch
+    d = np.random.default_rng(0).integers(0, 163840, size=(8, 7)).astype(np.int32)
+    v = gen.planted_verifier(d, np.arange(8, dtype=np.int32), np.full(8, 5, np.int32), 163840)
+    out = torch.empty(8, dtype=torch.int32, device="cuda")
+    D.accept_len(torch.from_numpy(d).cuda(), torch.from_numpy(v).cuda(), out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), np.arange(8))
+
+
+def test_determinism_bitwise():
+    wl = C.Workload("small_det", SMALL, C.Q8, seed=9, kv_lens=(300, 11), fixture_gains=True)
+    g = _gw(wl)
+    a = g.draft()
+    b = g.draft()
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
