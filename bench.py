@@ -1,0 +1,206 @@
+#!/usr/bin/env python
+"""Benchmark of one DSpark draft pass on one MI355X.
+
+A step is one pass of the whole hot path (fc, 5 MLA decoder layers, lm_head,
+Markov rollout, confidence) over one 7-token block of the full-size Q8_0
+workload at context 8192 (seeded synthetic weights ~N(0, 0.02) and inputs),
+with every input already resident in HBM.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 3]
+
+value = draft-pass latency in microseconds per 7-token block (lower is
+better); the JSON also carries the achieved algorithmic HBM bandwidth of the
+pass, the roofline of the dominant kernel (the lm_head GEMM, one launch per
+pass, timed live with HIP events recorded on the library's stream around
+that launch), and the CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft-pass latency (us/7-token block, bs=1) + achieved HBM GB/s % of peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, stored, inp):
+    """The oracle (float64 numpy) on a bounded sample of the same workload:
+    fc + fc-norm and decoder layer 0 (attention over the full cache + SwiGLU),
+    scaled to a whole pass by algorithmic bytes."""
+    import numpy as np
+    from oracle import dspark as O
+    from synth import accounting as A
+    m = wl.model
+    W = O.Weights(stored)
+    t0 = time.perf_counter()
+    cap = O._decode_input(inp.captured, wl.formats.captured).reshape(wl.n_seq, m.n_captured, m.block, m.hidden)
+    X = cap.transpose(0, 2, 1, 3).reshape(wl.n_seq * m.block, m.n_captured * m.hidden)
+    x = O.rmsnorm(X @ W("fc").T, W("fc_norm"), m.rms_eps)
+    caches = [O._decode_input(inp.caches[0], wl.formats.kv_cache)]
+    x = O.layer(m, W, 0, x, caches, inp.kv_offsets)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(x).all()
+    pb = A.pass_bytes(wl)
+    sample = pb["fc"] + pb["fc_norm"] + pb["captured"] + pb["kv_cache"] // m.n_layers
+    sample += sum(v for k, v in pb.items() if k.startswith("L0."))
+    total = sum(pb.values())
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 0) for i in threadpool_info()) or cores
+    except Exception:
+        pass
+    return {"value": round(dt * 1e6 * total / sample, 1), "unit": "us/block", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fc + layer 0 of {wl.name} ({sample / 1e6:.1f} MB of {total / 1e6:.1f} MB "
+                      f"algorithmic bytes) in {dt:.2f} s, float64 numpy, scaled by bytes"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the draft pass is not "
+              "sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mla_block_drafter_amd import dspark as D
+    from synth import accounting as A, configs as C, gen
+
+    wl = C.PRESETS[args.config]
+    m = wl.model
+    assert not wl.attn_only, "bench runs whole draft passes"
+    t = time.time()
+    stored = gen.make_weights(wl)
+    inp = gen.make_inputs(wl)
+    log(f"[bench] generated {wl.name} in {time.time() - t:.1f}s")
+    t = time.time()
+    model = D.Model(m, D.upload_stored(stored))
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"[bench] model packed ({model.packed_bytes / 1e9:.2f} GB) in {time.time() - t:.1f}s")
+
+    dev = "cuda"
+    cap = (torch.from_numpy(inp.captured).to(dev) if wl.formats.captured == "f32"
+           else torch.from_numpy(inp.captured.view(np.int16)).to(dev).view(torch.bfloat16))
+    kv = [(torch.from_numpy(c).to(dev) if wl.formats.kv_cache == "f32"
+           else torch.from_numpy(c.view(np.int16)).to(dev).view(torch.bfloat16)) for c in inp.caches]
+    offs = torch.from_numpy(inp.kv_offsets).to(dev)
+    prev = torch.from_numpy(inp.prev_token).to(dev)
+    n, B = wl.n_seq, m.block
+    ws = model.workspace(n, wl.total_ctx)
+    tokens = torch.empty((n, B), dtype=torch.int32, device=dev)
+    conf = torch.empty((n, B), dtype=torch.float32, device=dev)
+
+    def run(evs=None):
+        model.draft_block(cap, kv, offs, prev, wl.total_ctx, tokens, conf, ws, stage_events=evs)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * D.N_STAGES)] for _ in range(K)]
+    for row in evs:
+        for e in row:
+            e.record()
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record()
+    for k in range(K):
+        run(evs[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_begin.elapsed_time(t_end) / K
+    stage_ms = np.array([[evs[k][2 * s].elapsed_time(evs[k][2 * s + 1]) for s in range(D.N_STAGES)]
+                         for k in range(K)]).mean(axis=0)
+    log("[bench] eager: %.1f us/pass; stages (us): %s" % (
+        ms_step * 1e3, ", ".join(f"{nm} {v * 1e3:.1f}" for nm, v in zip(D.STAGES, stage_ms))))
+
+    graph_ms = None
+    if not args.no_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                run()
+            torch.cuda.current_stream().wait_stream(s)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(K):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            graph_ms = a.elapsed_time(b) / K
+            log("[bench] graph: %.1f us/pass" % (graph_ms * 1e3))
+        except Exception as e:  # graph capture is an extra, never the headline
+            log(f"[bench] graph capture skipped: {e!r}")
+
+    total_bytes = A.total_bytes(wl)
+    blocks = n
+    lm_bytes = A.lm_head_launch_bytes(wl)
+    lm_ms = float(stage_ms[2])
+    lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
+    pass_gbs = total_bytes / (ms_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.time()
+        cpu = cpu_baseline(wl, stored, inp)
+        log(f"[bench] cpu baseline in {time.time() - t:.1f}s: {cpu}")
+    fmt = {C.Q8_0: "q8_0", C.FP8: "fp8_e4m3", C.BF16: "bf16", C.F32: "f32"}[wl.formats.mlp]
+    out = {
+        "metric": METRIC,
+        "value": round(ms_step * 1e3 / blocks, 2),
+        "unit": "us/block",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_seq": n, "block": B, "ctx": int(wl.total_ctx // n),
+                   "hidden": m.hidden, "layers": m.n_layers, "vocab": m.vocab, "weights": fmt,
+                   "algorithmic_bytes": total_bytes},
+        "hbm_gbs": round(pass_gbs, 1),
+        "hbm_frac_of_peak": round(pass_gbs / HBM_PEAK_GBS, 4),
+        "graph_us_per_block": None if graph_ms is None else round(graph_ms * 1e3 / blocks, 2),
+        "stage_us": {nm: round(v * 1e3, 2) for nm, v in zip(D.STAGES, stage_ms)},
+        "roofline": {"bound": "hbm", "kernel": "lm_head GEMM (k_gemv_bf, BF16 weights)",
+                     "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -161,7 +161,18 @@ typedef struct dspark_block_out {
                        logits plus the Markov term, the argmax input; NULL = skip */
   float* hidden;    /* optional device float [n_seq][block][hidden]: final-normed
                        hidden state fed to the lm_head; NULL = skip             */
+  void* const* stage_events; /* optional host array of 2*DSPARK_N_STAGES
+                       hipEvent_t: events[2s] / events[2s+1] are recorded on the
+                       stream right before / after stage s (profiling aid);
+                       NULL = none                                               */
 } dspark_block_out;
+
+/* stages of one draft pass, for dspark_block_out.stage_events */
+#define DSPARK_STAGE_FC 0      /* input fragments + fc GEMM + fc norm            */
+#define DSPARK_STAGE_LAYERS 1  /* all decoder layers and the final norm          */
+#define DSPARK_STAGE_LM_HEAD 2 /* the lm_head GEMM (exactly one kernel launch)   */
+#define DSPARK_STAGE_MARKOV 3  /* Markov rollout, argmax, confidence              */
+#define DSPARK_N_STAGES 4
 
 /* One draft pass for every sequence's block (one pass of the hot path):
  * fc + RMSNorm -> n_layers x (RMSNorm, fused q_a/kv_a, q/kv norms + rope, q_b,

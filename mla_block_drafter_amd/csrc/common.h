@@ -104,19 +104,26 @@ struct PackedMat {
   int KB;                      // Kp / 32
 };
 
-// Activation fragment buffer descriptor.
+// Input buffer descriptor of one GEMM: either plain fp32 rows [group][M][ld]
+// (rows = 1: the GEMM builds its MFMA fragments in LDS) or prepared fragments.
 struct FragDesc {
   void* ptr;
-  int f32;          // 1: f32 family, 0: bf16 family
+  int rows;         // 1: fp32 rows, row stride ld, group stride gstride
+  int ld;
+  int f32;          // fragments: 1 f32 family, 0 bf16 family
   int hilo;         // bf16 family with M <= 8
-  int KB;           // Kp / 32 (bf16 family) ; Kp / 16 groups for f32 family in KG
-  int KG;           // Kp / 16
+  int KB;           // Kp / 32 (bf16 family)
+  int KG;           // Kp / 16 (f32 family)
   int MT;           // m-tiles of 16 rows
   long long gstride;  // elements per group
 };
 
-// Write activation element (row m, column k) of group g into a fragment buffer.
+// Write activation element (row m, column k) of group g into a GEMM input.
 __device__ __forceinline__ void frag_put(const FragDesc& fd, int g, int m, int k, float v) {
+  if (fd.rows) {
+    ((float*)fd.ptr)[(long long)g * fd.gstride + (long long)m * fd.ld + k] = v;
+    return;
+  }
   if (fd.f32) {
     const int grp = k >> 4, q = (k >> 2) & 3, i = k & 3;
     const int mt = m >> 4, lane = q * 16 + (m & 15);

@@ -298,9 +298,19 @@ struct Frag {
   long long off = 0, bytes = 0;
 };
 
-void frag_geom(Frag& f, const PackedMat& w, int M, bool hilo) {
+// Input buffer of one GEMM: fp32 rows when the GEMM stages its activations
+// in LDS (plan.amode != 0), else prepared fragments.
+void frag_geom(Frag& f, const PackedMat& w, int M, const GemvPlan& p) {
+  f.fd = FragDesc{};
+  if (p.amode != 0) {
+    f.fd.rows = 1;
+    f.fd.ld = w.K;
+    f.fd.gstride = (long long)M * w.K;
+    f.bytes = f.fd.gstride * 4 * w.ngroups;
+    return;
+  }
   f.fd.f32 = w.fmt == DT_F32;
-  f.fd.hilo = (!f.fd.f32 && hilo) ? 1 : 0;
+  f.fd.hilo = p.hilo;
   f.fd.KB = w.KB;
   f.fd.KG = w.Kp / 16;
   f.fd.MT = f.fd.hilo ? 1 : (M + 15) / 16;
@@ -313,22 +323,13 @@ struct Plan {
   int n_seq = 0, M = 0;
   long long total_ctx = 0;
   bool kv_f32 = false;
-  long long x = 0, part = 0, q = 0, bkeys = 0, opart = 0, mlpart = 0, z = 0, keys = 0, hconf = 0, total = 0;
+  long long x = 0, part = 0, q = 0, bkeys = 0, opart = 0, mlpart = 0, z = 0, keys = 0, total = 0;
+  long long ssq_a = 0, ssq_b = 0, ssq_cq = 0, dot = 0;
   long long zero_begin = 0, zero_end = 0;
   Frag f_fc, f_qkva, f_qb, f_uk, f_uv, f_o, f_gu, f_down, f_lm;
   GemvPlan p_fc{}, p_qkva{}, p_qb{}, p_uk{}, p_uv{}, p_o{}, p_gu{}, p_down{}, p_lm{}, p_w2{};
   int rows = 0, rows_pad = 0, DQ = 0, C = 0, slots = 0;
 };
-
-GemvPlan plan_for(const PackedMat& w, int M, bool allow_split = true) {
-  GemvPlan p = plan_gemv(w, M, false);
-  if (!allow_split && p.S > 1) {
-    const int ksteps = w.fmt == DT_F32 ? (w.Kp >> 4) : w.KB;
-    p.ksteps_per_split = ksteps;
-    p.S = 1;
-  }
-  return p;
-}
 
 void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f32, Plan& P) {
   const dspark_config& c = m.c;
@@ -337,7 +338,6 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   P.kv_f32 = kv_f32;
   const int M = n_seq * c.block;
   P.M = M;
-  const bool hilo = M <= 8;
   long long off = 0;
   auto take = [&](long long bytes) {
     const long long o = off;
@@ -347,36 +347,36 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   const Layer& L0 = m.L[0];
   P.x = take((long long)M * c.hidden * 4);
   long long part = 0;
-  auto gp = [&](GemvPlan& gpn, const Mat& mt, bool split = true) {
-    gpn = plan_for(mt.pm, M, split);
-    part = std::max(part, (long long)gpn.S * M * mt.pm.ngroups * mt.pm.G * 4);
+  auto gp = [&](GemvPlan& gpn, const Mat& mt, bool split) {
+    gpn = plan_gemv(mt.pm, M, split);
+    if (split) part = std::max(part, (long long)gpn.S * M * mt.pm.ngroups * mt.pm.G * 4);
   };
-  gp(P.p_qkva, L0.qkva);
-  gp(P.p_qb, L0.qb);
-  gp(P.p_uk, L0.uk);
-  gp(P.p_uv, L0.uv);
-  gp(P.p_o, L0.o);
+  gp(P.p_qkva, L0.qkva, true);
+  gp(P.p_qb, L0.qb, true);
+  gp(P.p_uk, L0.uk, false);   // epilogue writes the query buffer
+  gp(P.p_uv, L0.uv, false);   // epilogue writes the o_proj fragments
+  gp(P.p_o, L0.o, true);
   if (m.has_mlp) {
-    gp(P.p_gu, L0.gu);
-    gp(P.p_down, L0.down);
+    gp(P.p_gu, L0.gu, true);
+    gp(P.p_down, L0.down, true);
   }
   if (!m.layers_only) {
-    gp(P.p_fc, m.fc);
-    P.p_lm = plan_for(m.lm.pm, M, false);
-    P.p_w2 = plan_gemv(m.w2.pm, n_seq, true);
+    gp(P.p_fc, m.fc, true);
+    P.p_lm = plan_gemv(m.lm.pm, M, false);
+    P.p_w2 = plan_gemv(m.w2.pm, n_seq, false, true);
   }
-  frag_geom(P.f_qkva, L0.qkva.pm, M, hilo);
-  frag_geom(P.f_qb, L0.qb.pm, M, hilo);
-  frag_geom(P.f_uk, L0.uk.pm, M, hilo);
-  frag_geom(P.f_uv, L0.uv.pm, M, hilo);
-  frag_geom(P.f_o, L0.o.pm, M, hilo);
+  frag_geom(P.f_qkva, L0.qkva.pm, M, P.p_qkva);
+  frag_geom(P.f_qb, L0.qb.pm, M, P.p_qb);
+  frag_geom(P.f_uk, L0.uk.pm, M, P.p_uk);
+  frag_geom(P.f_uv, L0.uv.pm, M, P.p_uv);
+  frag_geom(P.f_o, L0.o.pm, M, P.p_o);
   if (m.has_mlp) {
-    frag_geom(P.f_gu, L0.gu.pm, M, hilo);
-    frag_geom(P.f_down, L0.down.pm, M, hilo);
+    frag_geom(P.f_gu, L0.gu.pm, M, P.p_gu);
+    frag_geom(P.f_down, L0.down.pm, M, P.p_down);
   }
   if (!m.layers_only) {
-    frag_geom(P.f_fc, m.fc.pm, M, hilo);
-    frag_geom(P.f_lm, m.lm.pm, M, hilo);
+    frag_geom(P.f_fc, m.fc.pm, M, P.p_fc);
+    frag_geom(P.f_lm, m.lm.pm, M, P.p_lm);
     P.f_fc.off = take(P.f_fc.bytes);
   }
   // zeroed region: fragment buffers, argmax keys and the query buffer
@@ -397,10 +397,12 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
     P.opart = take((long long)P.slots * P.rows_pad * c.kv_lora * 4);
     P.mlpart = take((long long)P.slots * P.rows_pad * 2 * 4);
   }
-  if (!m.layers_only) {
-    P.z = take((long long)M * c.vocab * 4);
-    P.hconf = take((long long)M * 4);
-  }
+  const long long ssq = (long long)M * SSQ_LD * 4;
+  P.ssq_a = take(ssq);
+  P.ssq_b = take(ssq);
+  P.ssq_cq = take(ssq);
+  P.dot = take(ssq);
+  if (!m.layers_only) P.z = take((long long)M * c.vocab * 4);
   P.total = off;
 }
 
@@ -408,18 +410,26 @@ void bind_frag(Frag& f, unsigned char* ws) {
   f.fd.ptr = f.bytes ? (void*)(ws + f.off) : nullptr;
 }
 
-// One GEMV launch with the STORE epilogue into the partial buffer.
-hipError_t run_gemv(const Mat& mt, const GemvPlan& p, const Frag& f, int M, float* out, hipStream_t st) {
+GemvArgs gemv_base(const Mat& mt, const GemvPlan& p, const Frag& f, int M) {
   GemvArgs a{};
   a.w = mt.pm;
   a.act = f.fd.ptr;
   a.act_gstride = f.fd.gstride;
+  a.act_ld = f.fd.ld;
   a.M = M;
   a.hilo = p.hilo;
   a.ksteps_per_split = p.ksteps_per_split;
-  a.out = out;
   a.out_ld = (long long)mt.pm.ngroups * mt.pm.G;
   a.out_split_stride = (long long)M * a.out_ld;
+  return a;
+}
+
+// One GEMV launch with the STORE epilogue into `out` (optionally row-scaled).
+hipError_t run_gemv(const Mat& mt, const GemvPlan& p, const Frag& f, int M, float* out, hipStream_t st,
+                    RowScale rs = RowScale{}) {
+  GemvArgs a = gemv_base(mt, p, f, M);
+  a.out = out;
+  a.rs = rs;
   return launch_gemv(a, p, GEMV_STORE, st);
 }
 
@@ -430,11 +440,28 @@ struct Ctx {
   hipStream_t st;
   float* part() const { return (float*)(ws + P.part); }
   float* x() const { return (float*)(ws + P.x); }
+  float* ssq(long long off) const { return (float*)(ws + off); }
+  RowScale rs(long long off, int n) const {
+    RowScale r{};
+    r.ssq = (const float*)(ws + off);
+    r.nch = (n + 255) / 256;
+    r.invn = 1.f / (float)n;
+    r.eps = m->c.rms_eps;
+    return r;
+  }
+  PartIn pin(const GemvPlan& p, const Mat& mt) const {
+    PartIn q{};
+    q.part = part();
+    q.S = p.S;
+    q.ld = (long long)mt.pm.ngroups * mt.pm.G;
+    q.ss = (long long)P.M * q.ld;
+    return q;
+  }
 };
 
-// Attention half of layer l (input fragments already in f_qkva); leaves the
-// o_proj partials in the partial buffer.
-int32_t attn_half(Ctx& C, int l, const void* kv, const int32_t* offs) {
+// Attention half of layer l.  Input: fragments of in_norm * x in f_qkva and
+// the chunk sums of x^2 at workspace offset `x_ssq`.  Leaves the o_proj partials.
+int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t* offs) {
   const dspark_model& m = *C.m;
   const dspark_config& c = m.c;
   const Layer& L = m.L[l];
@@ -443,11 +470,9 @@ int32_t attn_half(Ctx& C, int l, const void* kv, const int32_t* offs) {
   const double* freqs = (const double*)(m.base + m.freqs);
   HIPCHK(run_gemv(L.qkva, P.p_qkva, P.f_qkva, M, C.part(), C.st));
   {
-    QkvaArgs a{};
-    a.part = C.part();
-    a.S = P.p_qkva.S;
-    a.part_ld = L.qkva.pm.G;
-    a.part_ss = (long long)M * a.part_ld;
+    QkvaPost a{};
+    a.p = C.pin(P.p_qkva, L.qkva);
+    a.rs_in = C.rs(x_ssq, c.hidden);
     a.M = M;
     a.q_lora = c.q_lora;
     a.r = c.kv_lora;
@@ -458,19 +483,18 @@ int32_t attn_half(Ctx& C, int l, const void* kv, const int32_t* offs) {
     a.g_kva = (const float*)(m.base + L.kv_a_norm);
     a.eps = c.rms_eps;
     a.fd_qb = P.f_qb.fd;
+    a.ssq_cq = C.ssq(P.ssq_cq);
     a.bkeys = C.ws + P.bkeys;
     a.kv_f32 = P.kv_f32;
     a.offs = offs;
     a.freqs = freqs;
-    HIPCHK(launch_qkva_post(a, C.st));
+    HIPCHK(launch_post_qkva(a, C.st));
   }
   HIPCHK(run_gemv(L.qb, P.p_qb, P.f_qb, M, C.part(), C.st));
   {
-    QbArgs a{};
-    a.part = C.part();
-    a.S = P.p_qb.S;
-    a.part_ld = L.qb.pm.G;
-    a.part_ss = (long long)M * a.part_ld;
+    QbPost a{};
+    a.p = C.pin(P.p_qb, L.qb);
+    a.rs = C.rs(P.ssq_cq, c.q_lora);
     a.M = M;
     a.nh = c.n_heads;
     a.dn = c.qk_nope;
@@ -484,23 +508,17 @@ int32_t attn_half(Ctx& C, int l, const void* kv, const int32_t* offs) {
     a.q_f32 = P.kv_f32;
     a.offs = offs;
     a.freqs = freqs;
-    HIPCHK(launch_qb_post(a, C.st));
+    HIPCHK(launch_post_qb(a, C.st));
   }
-  HIPCHK(run_gemv(L.uk, P.p_uk, P.f_uk, M, C.part(), C.st));
   {
-    AbsorbArgs a{};
-    a.part = C.part();
-    a.part_ld = (long long)L.uk.pm.ngroups * L.uk.pm.G;
-    a.M = M;
-    a.nh = c.n_heads;
-    a.r = c.kv_lora;
-    a.block = c.block;
-    a.DQ = P.DQ;
-    a.rows_pad = P.rows_pad;
+    GemvArgs a = gemv_base(L.uk, P.p_uk, P.f_uk, M);
     a.q = C.ws + P.q;
     a.q_f32 = P.kv_f32;
-    if (P.p_uk.S != 1) return fail(DSPARK_EUNSUPPORTED, "absorb GEMM planned with split-K");
-    HIPCHK(launch_absorb_post(a, C.st));
+    a.DQ = P.DQ;
+    a.rows_pad = P.rows_pad;
+    a.nh = c.n_heads;
+    a.block = c.block;
+    HIPCHK(launch_gemv(a, P.p_uk, GEMV_QLAT, C.st));
   }
   {
     AttnArgs a{};
@@ -529,53 +547,39 @@ int32_t attn_half(Ctx& C, int l, const void* kv, const int32_t* offs) {
       HIPCHK(launch_attn_combine(a, C.st));
     }
   }
-  HIPCHK(run_gemv(L.uv, P.p_uv, P.f_uv, M, C.part(), C.st));
   {
-    FragArgs a{};
-    a.part = C.part();
-    a.S = P.p_uv.S;
-    a.part_ld = (long long)L.uv.pm.ngroups * L.uv.pm.G;
-    a.part_ss = (long long)M * a.part_ld;
-    a.M = M;
-    a.K = c.n_heads * c.v_head;
+    GemvArgs a = gemv_base(L.uv, P.p_uv, P.f_uv, M);
     a.fd = P.f_o.fd;
-    HIPCHK(launch_to_frag(a, C.st));
+    HIPCHK(launch_gemv(a, P.p_uv, GEMV_FRAG, C.st));
   }
   HIPCHK(run_gemv(L.o, P.p_o, P.f_o, M, C.part(), C.st));
   return DSPARK_OK;
 }
 
-// SwiGLU half of layer l (input fragments in f_gu); leaves down partials.
-int32_t mlp_half(Ctx& C, int l) {
+// SwiGLU half of layer l.  Input: fragments of post_norm * x in f_gu and the
+// chunk sums of x^2 at `x_ssq`.  Leaves the down partials.
+int32_t mlp_half(Ctx& C, int l, long long x_ssq) {
   const dspark_model& m = *C.m;
   const Layer& L = m.L[l];
   Plan& P = C.P;
   const int M = P.M;
   HIPCHK(run_gemv(L.gu, P.p_gu, P.f_gu, M, C.part(), C.st));
-  FragArgs a{};
-  a.part = C.part();
-  a.S = P.p_gu.S;
-  a.part_ld = L.gu.pm.G;
-  a.part_ss = (long long)M * a.part_ld;
+  SwigluPost a{};
+  a.p = C.pin(P.p_gu, L.gu);
+  a.rs = C.rs(x_ssq, m.c.hidden);
   a.M = M;
-  a.K = m.c.inter;
+  a.inter = m.c.inter;
   a.fd = P.f_down.fd;
-  a.swiglu = 1;
-  HIPCHK(launch_to_frag(a, C.st));
+  HIPCHK(launch_post_swiglu(a, C.st));
   HIPCHK(run_gemv(L.down, P.p_down, P.f_down, M, C.part(), C.st));
   return DSPARK_OK;
 }
 
-ResidArgs resid_base(Ctx& C, const GemvPlan& p, const Mat& mt) {
-  ResidArgs a{};
-  a.part = C.part();
-  a.S = p.S;
-  a.part_ld = (long long)mt.pm.ngroups * mt.pm.G;
-  a.part_ss = (long long)C.P.M * a.part_ld;
+ResidPost resid_base(Ctx& C) {
+  ResidPost a{};
   a.x_in = C.x();
   a.x_out = C.x();
-  a.mode = RESID_ADD;
-  a.eps = C.m->c.rms_eps;
+  a.mode = RP_ADD;
   a.M = C.P.M;
   a.H = C.m->c.hidden;
   return a;
@@ -736,6 +740,9 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   Plan& P = C.P;
   for (Frag* f : {&P.f_fc, &P.f_qkva, &P.f_qb, &P.f_uk, &P.f_uv, &P.f_o, &P.f_gu, &P.f_down, &P.f_lm}) bind_frag(*f, C.ws);
   const int M = P.M;
+  hipEvent_t* ev = (hipEvent_t*)out->stage_events;
+  auto mark = [&](int idx) -> hipError_t { return ev ? hipEventRecord(ev[idx], C.st) : hipSuccess; };
+  HIPCHK(mark(2 * DSPARK_STAGE_FC));
   {
     InitArgs a{};
     a.zero_ptr = C.ws + P.zero_begin;
@@ -751,40 +758,57 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   }
   HIPCHK(run_gemv(m->fc, P.p_fc, P.f_fc, M, C.part(), C.st));
   {
-    ResidArgs a = resid_base(C, P.p_fc, m->fc);
-    a.mode = RESID_NORM_FIRST;
-    a.x_in = nullptr;
+    ResidPost a = resid_base(C);          // y = fc output, chunk sums of y^2
+    a.mode = RP_SUM;
+    a.p = C.pin(P.p_fc, m->fc);
+    a.ssq_out = C.ssq(P.ssq_a);
+    HIPCHK(launch_post_resid(a, C.st));
+  }
+  {
+    ResidPost a = resid_base(C);          // x = RMSNorm(y; g_fc), fragments of in_norm * x
+    a.mode = RP_NORM;
+    a.rs_in = C.rs(P.ssq_a, c.hidden);
     a.g0 = (const float*)(m->base + m->fc_norm);
     a.g1 = (const float*)(m->base + m->L[0].in_norm);
     a.fd = P.f_qkva.fd;
-    HIPCHK(launch_resid_norm(a, C.st));
+    a.ssq_out = C.ssq(P.ssq_b);
+    HIPCHK(launch_post_resid(a, C.st));
   }
+  HIPCHK(mark(2 * DSPARK_STAGE_FC + 1));
+  HIPCHK(mark(2 * DSPARK_STAGE_LAYERS));
   for (int l = 0; l < c.n_layers; ++l) {
-    if ((rc = attn_half(C, l, in->kv[l], in->kv_offsets))) return rc;
+    if ((rc = attn_half(C, l, P.ssq_b, in->kv[l], in->kv_offsets))) return rc;
     {
-      ResidArgs a = resid_base(C, P.p_o, m->L[l].o);
+      ResidPost a = resid_base(C);        // x += o_proj; fragments of post_norm * x
+      a.p = C.pin(P.p_o, m->L[l].o);
       a.g1 = (const float*)(m->base + m->L[l].post_norm);
       a.fd = P.f_gu.fd;
-      HIPCHK(launch_resid_norm(a, C.st));
+      a.ssq_out = C.ssq(P.ssq_a);
+      HIPCHK(launch_post_resid(a, C.st));
     }
-    if ((rc = mlp_half(C, l))) return rc;
+    if ((rc = mlp_half(C, l, P.ssq_a))) return rc;
     {
-      ResidArgs a = resid_base(C, P.p_down, m->L[l].down);
+      ResidPost a = resid_base(C);        // x += down; fragments of the next norm * x
+      a.p = C.pin(P.p_down, m->L[l].down);
+      a.ssq_out = C.ssq(P.ssq_b);
       if (l + 1 < c.n_layers) {
         a.g1 = (const float*)(m->base + m->L[l + 1].in_norm);
         a.fd = P.f_qkva.fd;
       } else {
         a.g1 = (const float*)(m->base + m->final_norm);
         a.fd = P.f_lm.fd;
-        a.hidden_out = out->hidden;
-        a.conf_wh = (const float*)(m->base + m->conf_w);
-        a.hconf = (float*)(C.ws + P.hconf);
+        a.dotw = (const float*)(m->base + m->conf_w);
+        a.dot_out = C.ssq(P.dot);
       }
-      HIPCHK(launch_resid_norm(a, C.st));
+      HIPCHK(launch_post_resid(a, C.st));
     }
   }
+  HIPCHK(mark(2 * DSPARK_STAGE_LAYERS + 1));
   float* z = (float*)(C.ws + P.z);
-  HIPCHK(run_gemv(m->lm, P.p_lm, P.f_lm, M, z, C.st));
+  HIPCHK(mark(2 * DSPARK_STAGE_LM_HEAD));
+  HIPCHK(run_gemv(m->lm, P.p_lm, P.f_lm, M, z, C.st, C.rs(P.ssq_b, c.hidden)));
+  HIPCHK(mark(2 * DSPARK_STAGE_LM_HEAD + 1));
+  HIPCHK(mark(2 * DSPARK_STAGE_MARKOV));
   for (int i = 0; i < c.block; ++i) {
     GemvArgs a{};
     a.w = m->w2.pm;
@@ -812,7 +836,13 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.R = c.markov_rank;
     a.conf_wm = (const float*)(m->base + m->conf_w) + c.hidden;
     a.conf_b = (const float*)(m->base + m->conf_b);
-    a.hconf = (const float*)(C.ws + P.hconf);
+    a.dot = C.ssq(P.dot);
+    a.nch = (c.hidden + 255) / 256;
+    a.rs_final = C.rs(P.ssq_b, c.hidden);
+    a.x = C.x();
+    a.g_final = (const float*)(m->base + m->final_norm);
+    a.H = c.hidden;
+    a.hidden = out->hidden;
     a.tokens = out->tokens;
     a.conf = out->conf;
     a.n_seq = in->n_seq;
@@ -820,6 +850,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.vocab = c.vocab;
     HIPCHK(launch_markov_final(a, C.st));
   }
+  HIPCHK(mark(2 * DSPARK_STAGE_MARKOV + 1));
   return DSPARK_OK;
 }
 
@@ -855,27 +886,31 @@ int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_
   }
   const Layer& L = m->L[layer];
   {
-    ResidArgs a = resid_base(C, P.p_o, L.o);
-    a.mode = RESID_COPY;
+    ResidPost a = resid_base(C);          // x = x_in, fragments of in_norm * x
+    a.mode = RP_COPY;
     a.x_in = x_in;
     a.g1 = (const float*)(m->base + L.in_norm);
     a.fd = P.f_qkva.fd;
-    HIPCHK(launch_resid_norm(a, C.st));
+    a.ssq_out = C.ssq(P.ssq_b);
+    HIPCHK(launch_post_resid(a, C.st));
   }
-  if ((rc = attn_half(C, layer, kv, kv_offsets))) return rc;
-  ResidArgs a = resid_base(C, P.p_o, L.o);
+  if ((rc = attn_half(C, layer, P.ssq_b, kv, kv_offsets))) return rc;
+  ResidPost a = resid_base(C);
+  a.p = C.pin(P.p_o, L.o);
   if (!with_mlp) {
     a.x_out = x_out;
-    HIPCHK(launch_resid_norm(a, C.st));
+    HIPCHK(launch_post_resid(a, C.st));
     return DSPARK_OK;
   }
   a.g1 = (const float*)(m->base + L.post_norm);
   a.fd = P.f_gu.fd;
-  HIPCHK(launch_resid_norm(a, C.st));
-  if ((rc = mlp_half(C, layer))) return rc;
-  ResidArgs b = resid_base(C, P.p_down, L.down);
+  a.ssq_out = C.ssq(P.ssq_a);
+  HIPCHK(launch_post_resid(a, C.st));
+  if ((rc = mlp_half(C, layer, P.ssq_a))) return rc;
+  ResidPost b = resid_base(C);
+  b.p = C.pin(P.p_down, L.down);
   b.x_out = x_out;
-  HIPCHK(launch_resid_norm(b, C.st));
+  HIPCHK(launch_post_resid(b, C.st));
   return DSPARK_OK;
 }
 

@@ -1,0 +1,535 @@
+// Skinny GEMM for the draft pass: M = 7 activation rows per sequence against a
+// weight matrix streamed once from HBM (weight-only BF16 / Q8_0 / FP8 / F32).
+//
+// Why MFMA for a 7-row product: with packed-fp32 VALU ops unavailable, a VALU
+// dot product costs 7 FMAs plus a decode per weight element, about 700 us of
+// issue time for the full-size pass against a 630 us HBM floor.  The
+// v_mfma_f32_16x16x32_bf16 path costs ~1.5 VALU ops per element (decode only);
+// the 16-row MFMA is mostly padding, so rows 8..15 carry the bf16 residual of
+// the activations (hi/lo split) for near-fp32 accuracy at no extra cost.
+//
+// Work decomposition: each wave owns TPW consecutive 16-row tiles and one
+// k range (split-K over blockIdx.y).  Weight chunks are read with non-temporal
+// 16-byte loads (contiguous 1 KiB per wave per step); the small activation
+// fragments stay L2 resident.  Split-K partial sums go to a workspace slice per
+// split and are reduced, in a fixed order, by the consuming kernel.
+#pragma once
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace dspark {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ T ntload(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+// Markov predecessor of position a.step for sequence m (callers treat values
+// outside [0, vocab) as "no predecessor").
+__device__ __forceinline__ int markov_prev(const GemvArgs& a, int m) {
+  if (a.step == 0) return a.prev_token[m];
+  if (a.forced) return a.forced[m * a.block + a.step - 1];
+  const unsigned long long* k = a.keys + ((long long)m * a.block + a.step - 1) * KEY_SLOTS;
+  unsigned long long best = 0;
+#pragma unroll
+  for (int i = 0; i < KEY_SLOTS; ++i) best = best > k[i] ? best : k[i];
+  return key_index(best);
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, o, 64);
+  hi = __shfl_xor(hi, o, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float gemv_row_scale(const RowScale& s, int m) {
+  if (!s.ssq) return 1.f;
+  const float* p = s.ssq + (long long)m * SSQ_LD;
+  float t = 0.f;
+  for (int c = 0; c < s.nch; ++c) t += p[c];
+  return rsqrtf(t * s.invn + s.eps);
+}
+
+// Shared epilogue.  acc[mt][j] holds D[m][n] of tile t0 + j for this lane:
+// m = 16 mt + 4 (lane >> 4) + r, n = lane & 15 (hi/lo: rows m and m + 8 are
+// first summed, lanes 0..31 then hold rows 0..7).
+template <int MT, int TPW, int MODE>
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT][TPW], bool active,
+                                              int t0, int lane, int wave) {
+  const int TG = a.w.TG, G = a.w.G;
+  const int g = active ? t0 / TG : 0;
+  if (MODE != GEMV_MARKOV) {
+    float* out = a.out + (long long)blockIdx.y * a.out_split_stride;
+    float rsv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mt * 16 + (lane >> 4) * 4 + r;
+        rsv[mt][r] = (active && a.rs.ssq && m < a.M) ? gemv_row_scale(a.rs, m) : 1.f;
+      }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = t0 + j;
+      const int cig = (t % TG) * 16 + (lane & 15);
+      const bool colok = active && cig < G;
+      const long long col = (long long)g * G + cig;
+      float fs = 1.0f;
+      if (a.w.fmt == DT_FP8 && colok) fs = ((const float*)a.w.scales)[(long long)t * 16 + (lane & 15)];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 v = acc[mt][j];
+        if (a.hilo) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], 32, 64);
+        }
+        if (!colok) continue;
+        if (a.hilo && lane >= 32) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mt * 16 + (lane >> 4) * 4 + r;
+          if (m >= a.M) continue;
+          const float val = v[r] * fs * rsv[mt][r];
+          if (MODE == GEMV_STORE) {
+            out[(long long)m * a.out_ld + col] = val;
+          } else if (MODE == GEMV_QLAT) {
+            const int s = m / a.block, i = m % a.block;
+            const long long qi = ((long long)s * a.rows_pad + i * a.nh + g) * a.DQ + cig;
+            if (a.q_f32) ((float*)a.q)[qi] = val;
+            else ((uint16_t*)a.q)[qi] = (uint16_t)f32_to_bf16_bits(val);
+          } else {
+            frag_put(a.fd, 0, m, (int)col, val);
+          }
+        }
+      }
+    }
+  } else {
+    // Markov: l = z + W2 u for M = n_seq rows; argmax over the vocabulary.
+    const long long V = G;
+    unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = t0 + j;
+      const int col = t * 16 + (lane & 15);
+      if (!active || col >= G) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = (lane >> 4) * 4 + r;
+        if (m >= a.M) continue;
+        const long long row = (long long)m * a.block + a.step;
+        const float v = acc[0][j][r] + a.z[row * V + col];
+        if (a.logits) a.logits[row * V + col] = v;
+        const unsigned long long k = argmax_key(v, (uint32_t)col);
+        best[r] = best[r] > k ? best[r] : k;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const unsigned long long other = shfl_xor_u64(best[r], o);
+        best[r] = best[r] > other ? best[r] : other;
+      }
+    }
+    __shared__ unsigned long long red[4][16];
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(lane >> 4) * 4 + r] = best[r];
+    }
+    __syncthreads();
+    const int m = threadIdx.x;
+    if (m < 16 && m < a.M) {
+      unsigned long long k = red[0][m];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) k = k > red[w][m] ? k : red[w][m];
+      if (k) atomicMax(a.keys + ((long long)m * a.block + a.step) * KEY_SLOTS + (blockIdx.x % KEY_SLOTS), k);
+    }
+  }
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2 };
+
+// Eight fp32 activations of row `row` from column k0 (zero outside M x K).
+__device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, int row, int k0, float (&v)[8]) {
+  const int K = a.w.K;
+  if (row < a.M && k0 + 8 <= K && (a.act_ld & 3) == 0) {
+    const f32x4 x0 = *(const f32x4*)(rows + (long long)row * a.act_ld + k0);
+    const f32x4 x1 = *(const f32x4*)(rows + (long long)row * a.act_ld + k0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = x0[e];
+      v[4 + e] = x1[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = (row < a.M && k0 + e < K) ? rows[(long long)row * a.act_ld + k0 + e] : 0.f;
+  }
+}
+
+// bf16-family weights (BF16 / Q8_0 / FP8).
+//
+// AMODE selects the activation operand:
+//  A_GLOBAL:  prepared bf16 fragments read from global memory (L2 resident);
+//  A_ROWS_BF: the workgroup converts its k range of the fp32 activation rows
+//             into bf16 fragments in LDS (hi/lo split when M <= 8);
+//  A_ROWS_I8: Q8_0 with M <= 8: the rows are quantised per (row, 32-block) to
+//             an int8 hi code and an int8 residual code (scale s and s/256),
+//             and the int8 weight codes feed v_mfma_i32_16x16x32_i8 directly:
+//             no weight decode, exact integer products, one fp32 fma per
+//             output per block with the factor d_w * s_a.
+// Weight loads are issued in stages of U k steps x TPW tiles before any of
+// them is consumed.
+template <int FMT, int MT, int TPW, int MODE, int AMODE>
+__global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char gemv_smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int T = a.w.ngroups * a.w.TG;
+  const int t0 = (blockIdx.x * 4 + wave) * TPW;
+  const bool active = t0 < T;
+  const int KB = a.w.KB;
+  const int kb0 = blockIdx.y * a.ksteps_per_split;
+  const int kb1 = min(KB, kb0 + a.ksteps_per_split);
+  const int nkb = kb1 - kb0;
+  const int g = AMODE != A_GLOBAL ? min(blockIdx.x * 4 * TPW, T - 1) / a.w.TG : (active ? t0 / a.w.TG : 0);
+
+  // ---------------------------------------------------------- prologue --
+  bf16x8* alds = (bf16x8*)gemv_smem;            // A_ROWS_BF: [MT][nkb][64]
+  long* icode = (long*)gemv_smem;               // A_ROWS_I8: [nkb][64]
+  float* iscale = (float*)(gemv_smem + (size_t)nkb * 512);  // [nkb][8]
+  const float* rows = (const float*)a.act + (long long)g * a.act_gstride;
+  // Activation staging (all threads, ends with a barrier).  Weight loads do
+  // not depend on it, so each wave issues its first weight stage before.
+  auto stage_activations = [&]() {
+    if (AMODE == A_ROWS_BF) {
+      for (int i = threadIdx.x; i < MT * nkb * 64; i += 256) {
+        const int mt = i / (nkb * 64), rem = i - mt * nkb * 64;
+        const int kbl = rem >> 6, l = rem & 63;
+        const int m16 = l & 15, k0 = 32 * (kb0 + kbl) + 8 * (l >> 4);
+        const int row = a.hilo ? (m16 & 7) : mt * 16 + m16;
+        const bool lo = a.hilo && m16 >= 8;
+        float v[8];
+        load_row8(a, rows, row, k0, v);
+        u32x4 o;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t h0 = f32_to_bf16_bits(v[2 * e]), h1 = f32_to_bf16_bits(v[2 * e + 1]);
+          if (lo) {
+            h0 = f32_to_bf16_bits(v[2 * e] - bf16_bits_to_f32(h0));
+            h1 = f32_to_bf16_bits(v[2 * e + 1] - bf16_bits_to_f32(h1));
+          }
+          o[e] = h0 | (h1 << 16);
+        }
+        alds[i] = __builtin_bit_cast(bf16x8, o);
+      }
+      __syncthreads();
+    } else if (AMODE == A_ROWS_I8) {
+      for (int it = threadIdx.x; it < nkb * 32; it += 256) {
+        const int q = it & 3, row = (it >> 2) & 7, kbl = it >> 5;
+        const int k0 = 32 * (kb0 + kbl) + 8 * q;
+        float v[8];
+        load_row8(a, rows, row, k0, v);
+        float mx = 0.f;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+        const float sc = mx * (1.f / 127.f);
+        const float inv = mx > 0.f ? 127.f / mx : 0.f;
+        uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float qh = fminf(fmaxf(__builtin_rintf(v[e] * inv), -127.f), 127.f);
+          const float ql = fminf(fmaxf(__builtin_rintf((v[e] - qh * sc) * inv * 256.f), -127.f), 127.f);
+          hw[e >> 2] |= ((uint32_t)(int)qh & 0xFFu) << (8 * (e & 3));
+          lw[e >> 2] |= ((uint32_t)(int)ql & 0xFFu) << (8 * (e & 3));
+        }
+        icode[kbl * 64 + q * 16 + row] = (long)(((unsigned long long)hw[1] << 32) | hw[0]);
+        icode[kbl * 64 + q * 16 + 8 + row] = (long)(((unsigned long long)lw[1] << 32) | lw[0]);
+        if (q == 0) iscale[kbl * 8 + row] = sc;
+      }
+      __syncthreads();
+    }
+  };
+
+  f32x4 acc[MT][TPW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bool staged = false;
+  if (active) {
+    const bf16x8* afrag = (const bf16x8*)a.act + (long long)g * (a.act_gstride / 8);
+    const __bf16* gsrc = nullptr;
+    if (MODE == GEMV_MARKOV) {
+      const int m = lane & 15;
+      const int tp = m < a.M ? markov_prev(a, m) : -1;
+      if (tp >= 0 && tp < a.w.G) gsrc = (const __bf16*)a.act + (long long)tp * a.gather_ld + 8 * (lane >> 4);
+    }
+    auto load_a = [&](int mt, int kb) -> bf16x8 {
+      if (MODE == GEMV_MARKOV) {
+        if (!gsrc) return bf16x8{};
+        return *(const bf16x8*)(gsrc + 32 * kb);
+      }
+      if (AMODE == A_ROWS_BF) return alds[(mt * nkb + (kb - kb0)) * 64 + lane];
+      return afrag[((long long)mt * KB + kb) * 64 + lane];
+    };
+
+    // Weight stream, software pipelined: the loads of stage s+1 are issued
+    // before stage s is consumed, so a wave always has loads in flight.
+    if (FMT == DT_BF16) {
+      constexpr int U = (MT == 1 ? 8 : 4) / TPW;  // k blocks per stage
+      const u32x4* wp = (const u32x4*)a.w.codes + (long long)t0 * KB * 64 + lane;
+      auto load_stage = [&](u32x4 (&wr)[U][TPW], int kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (kb + u < kb1)
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+              // W2 is re-read by every Markov step: keep it cacheable
+              const u32x4* src = wp + ((long long)j * KB + kb + u) * 64;
+              wr[u][j] = MODE == GEMV_MARKOV ? *src : ntload(src);
+            }
+      };
+      auto compute_stage = [&](const u32x4 (&wr)[U][TPW], int kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (kb + u >= kb1) break;
+          bf16x8 A[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) A[mt] = load_a(mt, kb + u);
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            const bf16x8 B = __builtin_bit_cast(bf16x8, wr[u][j]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt], B, acc[mt][j], 0, 0, 0);
+          }
+        }
+      };
+      u32x4 wa[U][TPW], wb[U][TPW];
+      load_stage(wa, kb0);
+      stage_activations();
+      staged = true;
+      for (int kb = kb0; kb < kb1; kb += 2 * U) {
+        if (kb + U < kb1) load_stage(wb, kb + U);
+        compute_stage(wa, kb);
+        if (kb + U >= kb1) break;
+        if (kb + 2 * U < kb1) load_stage(wa, kb + 2 * U);
+        compute_stage(wb, kb + U);
+      }
+    } else {
+      constexpr int U = (MT == 1 ? 8 : 4) / TPW;  // pairs of k blocks per stage
+      const int KP = KB >> 1;
+      const u32x4* wp = (const u32x4*)a.w.codes + (long long)t0 * KP * 64 + lane;
+      const uint32_t* sp = (const uint32_t*)a.w.scales + (long long)t0 * KP * 16 + (lane & 15);
+      const float lofac = lane >= 32 ? (1.f / 256.f) : 1.f;  // A_ROWS_I8: rows 8..15 are residual codes
+      auto load_stage = [&](u32x4 (&wr)[U][TPW], uint32_t (&sc)[U][TPW], int kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (kb + 2 * u >= kb1) break;
+          const int p = (kb >> 1) + u;
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            wr[u][j] = ntload(wp + ((long long)j * KP + p) * 64);
+            if (FMT == DT_Q8_0) sc[u][j] = sp[((long long)j * KP + p) * 16];
+          }
+        }
+      };
+      auto compute_stage = [&](const u32x4 (&wr)[U][TPW], const uint32_t (&sc)[U][TPW], int kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int k2 = kb + 2 * u;
+          if (k2 >= kb1) break;
+          if (AMODE == A_ROWS_I8) {
+            const int kl = k2 - kb0;
+            const long A0 = icode[kl * 64 + lane], A1 = icode[(kl + 1) * 64 + lane];
+            const f32x4 s0 = *(const f32x4*)(iscale + kl * 8 + ((lane >> 4) & 1) * 4) * lofac;
+            const f32x4 s1 = *(const f32x4*)(iscale + (kl + 1) * 8 + ((lane >> 4) & 1) * 4) * lofac;
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+              const long B0 = (long)(((unsigned long long)wr[u][j][1] << 32) | wr[u][j][0]);
+              const long B1 = (long)(((unsigned long long)wr[u][j][3] << 32) | wr[u][j][2]);
+              const float d0 = fp16_bits_to_f32(sc[u][j] & 0xFFFFu);
+              const float d1 = fp16_bits_to_f32(sc[u][j] >> 16);
+              const i32x4 z = {0, 0, 0, 0};
+              const i32x4 p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A0, B0, z, 0, 0, 0);
+              const i32x4 p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A1, B1, z, 0, 0, 0);
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[0][j][r] += (float)p0[r] * (d0 * s0[r]) + (float)p1[r] * (d1 * s1[r]);
+            }
+            continue;
+          }
+          bf16x8 A0[MT], A1[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            A0[mt] = load_a(mt, k2);
+            A1[mt] = load_a(mt, k2 + 1);
+          }
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            if (FMT == DT_Q8_0) {
+              const bf16x8 B0 = i8x8_to_bf16x8(wr[u][j][0], wr[u][j][1]);
+              const bf16x8 B1 = i8x8_to_bf16x8(wr[u][j][2], wr[u][j][3]);
+              const float d0 = fp16_bits_to_f32(sc[u][j] & 0xFFFFu);
+              const float d1 = fp16_bits_to_f32(sc[u][j] >> 16);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[mt], B0, z, 0, 0, 0);
+                const f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[mt], B1, z, 0, 0, 0);
+                acc[mt][j] += d0 * p0 + d1 * p1;
+              }
+            } else {
+              const bf16x8 B0 = fp8x8_to_bf16x8(wr[u][j][0], wr[u][j][1]);
+              const bf16x8 B1 = fp8x8_to_bf16x8(wr[u][j][2], wr[u][j][3]);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) {
+                acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[mt], B0, acc[mt][j], 0, 0, 0);
+                acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[mt], B1, acc[mt][j], 0, 0, 0);
+              }
+            }
+          }
+        }
+      };
+      u32x4 wa[U][TPW], wb[U][TPW];
+      uint32_t sa[U][TPW], sb[U][TPW];
+      load_stage(wa, sa, kb0);
+      stage_activations();
+      staged = true;
+      for (int kb = kb0; kb < kb1; kb += 4 * U) {
+        if (kb + 2 * U < kb1) load_stage(wb, sb, kb + 2 * U);
+        compute_stage(wa, sa, kb);
+        if (kb + 2 * U >= kb1) break;
+        if (kb + 4 * U < kb1) load_stage(wa, sa, kb + 4 * U);
+        compute_stage(wb, sb, kb + 2 * U);
+      }
+    }
+  }
+  if (!staged) stage_activations();  // inactive waves still join the barrier
+  gemv_epilogue<MT, TPW, MODE>(a, acc, active, t0, lane, wave);
+}
+
+// F32 weights on v_mfma_f32_16x16x4_f32: four MFMAs per 16-wide k group.
+template <int MT, int TPW, int MODE>
+__global__ __launch_bounds__(256) void k_gemv_f32(GemvArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int T = a.w.ngroups * a.w.TG;
+  const int t0 = (blockIdx.x * 4 + wave) * TPW;
+  const bool active = t0 < T;
+  const int KG = a.w.Kp >> 4;
+  const int g0 = blockIdx.y * a.ksteps_per_split;
+  const int g1 = min(KG, g0 + a.ksteps_per_split);
+
+  f32x4 acc[MT][TPW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (active) {
+    const int g = t0 / a.w.TG;
+    const f32x4* afrag = (const f32x4*)a.act + (long long)g * (a.act_gstride / 4);
+    const float* gsrc = nullptr;
+    if (MODE == GEMV_MARKOV) {
+      const int m = lane & 15;
+      const int tp = m < a.M ? markov_prev(a, m) : -1;
+      if (tp >= 0 && tp < a.w.G) gsrc = (const float*)a.act + (long long)tp * a.gather_ld + 4 * (lane >> 4);
+    }
+    const f32x4* wp = (const f32x4*)a.w.codes + (long long)t0 * KG * 64 + lane;
+    for (int gk = g0; gk < g1; ++gk) {
+      f32x4 W[TPW];
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) W[j] = ntload(wp + ((long long)j * KG + gk) * 64);
+      f32x4 A[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (MODE == GEMV_MARKOV) A[mt] = gsrc ? *(const f32x4*)(gsrc + 16 * gk) : f32x4{0.f, 0.f, 0.f, 0.f};
+        else A[mt] = afrag[((long long)mt * KG + gk) * 64 + lane];
+      }
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[mt][i], W[j][i], acc[mt][j], 0, 0, 0);
+    }
+  }
+  gemv_epilogue<MT, TPW, MODE>(a, acc, active, t0, lane, wave);
+}
+
+// LDS bytes of the activation staging of one workgroup.
+inline size_t gemv_lds_bytes(const GemvPlan& p) {
+  if (p.amode == A_ROWS_BF) return (size_t)p.MT * p.ksteps_per_split * 64 * 16;
+  if (p.amode == A_ROWS_I8) return (size_t)p.ksteps_per_split * (512 + 32);
+  return 0;
+}
+
+template <int FMT, int MT, int TPW, int MODE>
+hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  dim3 grid(p.grid_x, p.S), block(256);
+  const size_t lds = gemv_lds_bytes(p);
+  if (FMT == DT_F32) {
+    hipLaunchKernelGGL((k_gemv_f32<MT, TPW, MODE>), grid, block, 0, st, a);
+  } else if (p.amode == A_ROWS_BF) {
+    hipLaunchKernelGGL((k_gemv_bf<FMT, MT, TPW, MODE, A_ROWS_BF>), grid, block, lds, st, a);
+  } else if (FMT == DT_Q8_0 && MT == 1 && MODE != GEMV_MARKOV && p.amode == A_ROWS_I8) {
+    hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_ROWS_I8>), grid, block, lds, st, a);
+  } else if (p.amode == A_GLOBAL) {
+    hipLaunchKernelGGL((k_gemv_bf<FMT, MT, TPW, MODE, A_GLOBAL>), grid, block, 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, int MODE>
+hipError_t dispatch_out(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  if (p.MT == 1) {
+    if (p.TPW == 4) return go<FMT, 1, 4, MODE>(a, p, st);
+    if (p.TPW == 2) return go<FMT, 1, 2, MODE>(a, p, st);
+    return go<FMT, 1, 1, MODE>(a, p, st);
+  }
+  switch (p.MT) {
+    case 2: return go<FMT, 2, 1, MODE>(a, p, st);
+    case 3: return go<FMT, 3, 1, MODE>(a, p, st);
+    case 4: return go<FMT, 4, 1, MODE>(a, p, st);
+    case 5: return go<FMT, 5, 1, MODE>(a, p, st);
+    case 6: return go<FMT, 6, 1, MODE>(a, p, st);
+    case 7: return go<FMT, 7, 1, MODE>(a, p, st);
+    case 8: return go<FMT, 8, 1, MODE>(a, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+hipError_t dispatch_markov(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  if (p.MT != 1) return hipErrorInvalidValue;
+  if (p.TPW == 4) return go<FMT, 1, 4, GEMV_MARKOV>(a, p, st);
+  if (p.TPW == 2) return go<FMT, 1, 2, GEMV_MARKOV>(a, p, st);
+  return go<FMT, 1, 1, GEMV_MARKOV>(a, p, st);
+}
+
+template <int FMT>
+hipError_t dispatch_fmt(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st) {
+  switch (mode) {
+    case GEMV_STORE: return dispatch_out<FMT, GEMV_STORE>(a, p, st);
+    case GEMV_QLAT: return dispatch_out<FMT, GEMV_QLAT>(a, p, st);
+    case GEMV_FRAG: return dispatch_out<FMT, GEMV_FRAG>(a, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+}  // namespace dspark

@@ -10,13 +10,15 @@
 //
 // bf16 path (split-K, flash-decoding style): a workgroup of 4 waves owns 64
 // query rows and one slot of C keys.  Key tiles of 32 rows are staged in LDS
-// twice: row-major (A operand of S^T = K Q^T, so the probabilities land with
-// one query row per lane column) and transposed (V^T, A operand of
-// O^T = V^T P^T).  Because S^T already has the B-operand lane layout of P^T
-// the probabilities never leave registers: the 32 keys' order inside the
-// MFMA reduction is permuted identically on both operands.  Online softmax
-// state (m, l) is per lane column.  Partials per slot are merged by
-// k_attn_combine in a fixed order.
+// row-major.  S^T = K Q^T takes the key rows as the A operand (16-byte LDS
+// reads), so the probabilities land with one query row per lane column,
+// which is already the B-operand layout of P^T for O^T = V^T P^T: the
+// probabilities never leave registers (the 32 keys' order inside the MFMA
+// reduction is permuted identically on both operands).  The V^T operand is
+// gathered from the same row-major tile with 2-byte LDS reads (the value is
+// c_kv, the first kv_lora columns of the key row), so no transposed copy is
+// staged.  Online softmax state (m, l) is per lane column.  Partials per slot
+// are merged by k_attn_combine in a fixed order.
 #include "kernels.h"
 
 namespace dspark {
@@ -24,6 +26,7 @@ namespace dspark {
 namespace {
 
 constexpr int KT = 32;  // keys per LDS tile
+constexpr int MAX_COMBINE_SLOTS = 4096;
 
 __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s, int& p, int& len,
                                             int& off, int& J) {
@@ -43,13 +46,11 @@ __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s,
 }
 
 template <int NKB, int NDT>
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   constexpr int DQ = NKB * 32;
   constexpr int R = NDT * 16;
-  constexpr int KLD = DQ + 8;   // padded LDS row (elements)
-  constexpr int VLD = KT + 4;   // padded V^T row (elements)
+  constexpr int KLD = DQ + 8;   // padded LDS row (elements), 16-byte aligned rows
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[KT * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[R * VLD];
 
   int s, p, len, off, J;
   slot_lookup(a, blockIdx.y, s, p, len, off, J);
@@ -90,13 +91,6 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
         v = *(const u32x4*)src;
       }
       *(u32x4*)(k_lds + kk * KLD + d8) = v;
-      if (d8 < R) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vt_lds[(d8 + 2 * e) * VLD + kk] = (uint16_t)(v[e] & 0xFFFFu);
-          vt_lds[(d8 + 2 * e + 1) * VLD + kk] = (uint16_t)(v[e] >> 16);
-        }
-      }
     }
     __syncthreads();
 
@@ -148,25 +142,26 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 
     // ---- O^T += V^T P^T: lane's k slots map to keys 4(lane>>4)+{0..3} and
-    //      16 + 4(lane>>4) + {0..3}, matching the P fragment above ----
+    //      16 + 4(lane>>4) + {0..3}, matching the P fragment above; the A
+    //      operand holds V[key][dim = 16d + (lane & 15)] for those keys ----
+    const uint16_t* vbase = k_lds + 4 * (lane >> 4) * KLD + (lane & 15);
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
-      const uint16_t* vrow = vt_lds + (16 * d + (lane & 15)) * VLD + 4 * (lane >> 4);
+      const uint16_t* vcol = vbase + 16 * d;
       u32x4 vv;
-      const u32x2 v0 = *(const u32x2*)vrow;
-      const u32x2 v1 = *(const u32x2*)(vrow + 16);
-      vv[0] = v0[0];
-      vv[1] = v0[1];
-      vv[2] = v1[0];
-      vv[3] = v1[1];
+      vv[0] = (uint32_t)vcol[0] | ((uint32_t)vcol[KLD] << 16);
+      vv[1] = (uint32_t)vcol[2 * KLD] | ((uint32_t)vcol[3 * KLD] << 16);
+      vv[2] = (uint32_t)vcol[16 * KLD] | ((uint32_t)vcol[17 * KLD] << 16);
+      vv[3] = (uint32_t)vcol[18 * KLD] | ((uint32_t)vcol[19 * KLD] << 16);
       acc[d] *= corr;
       acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[d], 0, 0, 0);
     }
     __syncthreads();
   }
 
-  // ---- partials: O^T[dim = 16d + 4(lane>>4) + r][row = myrow] ----
-  const long long prow = (long long)blockIdx.y * a.rows_pad + myrow;
+  // ---- partials: O^T[dim = 16d + 4(lane>>4) + r][row = myrow]; layout
+  //      [row][slot][dim] so the combine of one row reads contiguous memory ----
+  const long long prow = (long long)myrow * a.slots + blockIdx.y;
   float* op = a.o_part + prow * a.r + 4 * (lane >> 4);
 #pragma unroll
   for (int d = 0; d < NDT; ++d) *(f32x4*)(op + 16 * d) = acc[d];
@@ -176,8 +171,11 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   }
 }
 
-// Merge the slots of each (sequence, row) and write the un-absorb fragments.
+// Merge the slots of each (sequence, row) in slot order and write the
+// un-absorb fragments: O = sum_p exp(m_p - M) O_p / sum_p exp(m_p - M) l_p.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+  __shared__ float wgt[MAX_COMBINE_SLOTS];
+  __shared__ float red[4];
   const int row = blockIdx.x;  // i * nh + h
   const int s = blockIdx.y;
   if (row >= a.rows) return;
@@ -188,23 +186,31 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   }
   const int J = a.offs[s + 1] - a.offs[s] + a.block;
   const int ns = (J + a.C - 1) / a.C;
-  float M = -INFINITY;
-  for (int p = 0; p < ns; ++p) M = fmaxf(M, a.ml_part[((long long)(base + p) * a.rows_pad + row) * 2]);
-  float L = 0.f;
-  for (int p = 0; p < ns; ++p) {
-    const long long pr = ((long long)(base + p) * a.rows_pad + row) * 2;
-    L += a.ml_part[pr + 1] * __expf(a.ml_part[pr] - M);
+  const float* ml = a.ml_part + ((long long)row * a.slots + base) * 2;
+  float mx = -INFINITY;
+  for (int p = threadIdx.x; p < ns; p += 256) mx = fmaxf(mx, ml[2 * p]);
+  mx = block_max256(mx, red);
+  float l = 0.f;
+  for (int p = threadIdx.x; p < ns; p += 256) {
+    const float w = __expf(ml[2 * p] - mx);
+    wgt[p] = w;
+    l += ml[2 * p + 1] * w;
   }
-  const float invL = 1.f / L;
+  l = block_sum256(l, red);  // also orders the wgt writes before the reads below
+  const float invL = 1.f / l;
   const int i = row / a.nh, h = row % a.nh;
   const int m = s * a.block + i;
+  const float* op = a.o_part + ((long long)row * a.slots + base) * a.r;
   for (int d = threadIdx.x; d < a.r; d += 256) {
-    float o = 0.f;
-    for (int p = 0; p < ns; ++p) {
-      const long long pr = (long long)(base + p) * a.rows_pad + row;
-      o += a.o_part[pr * a.r + d] * __expf(a.ml_part[pr * 2] - M);
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int p = 0;
+    for (; p + 8 <= ns; p += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] += wgt[p + u] * op[(long long)(p + u) * a.r + d];
     }
-    frag_put(a.fd_uv, h, m, d, o * invL);
+    for (; p < ns; ++p) o[0] += wgt[p] * op[(long long)p * a.r + d];
+    const float t = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
+    frag_put(a.fd_uv, h, m, d, t * invL);
   }
 }
 
@@ -283,6 +289,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st) {
+  if (a.slots > MAX_COMBINE_SLOTS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_attn_combine, dim3(a.rows, a.n_seq), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -1,10 +1,6 @@
-// Row-wise kernels of the draft pass: split-K reduction + residual + RMSNorm,
-// q/kv norms and (YaRN) rope, fragment writers for the next GEMM, the Markov
-// finaliser (tokens, confidence), acceptance length, weight repack / decode.
-//
-// RMSNorm: g * x / sqrt(mean(x^2) + eps) in fp32.  RoPE rotates consecutive
-// pairs (2k, 2k+1) by pos * theta'_k, with theta'_k precomputed on the host in
-// fp64 (YaRN NTK-by-parts) and the angle reduced and evaluated in fp64.
+// Small kernels of the draft pass: workspace init and fc input fragments, the
+// Markov finaliser (tokens, confidence, hidden output), acceptance length, and
+// weight repack / decode.
 #include "kernels.h"
 
 namespace dspark {
@@ -24,8 +20,8 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
   const FragDesc& fd = a.fd_fc;
   const int M = a.n_seq * a.block;
   const int K = a.ncap * a.H;
-  const int Kp = fd.f32 ? fd.KG * 16 : fd.KB * 32;
-  const int rows = fd.hilo ? 8 : fd.MT * 16;
+  const int Kp = fd.rows ? K : fd.f32 ? fd.KG * 16 : fd.KB * 32;
+  const int rows = fd.rows ? M : fd.hilo ? 8 : fd.MT * 16;
   const long long total = (long long)rows * Kp;
   for (long long e = tid; e < total; e += nthr) {
     const int m = (int)(e / Kp), k = (int)(e % Kp);
@@ -40,158 +36,13 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
   }
 }
 
-// ------------------------------------------------------------- residual --
-__global__ __launch_bounds__(256) void k_resid_norm(ResidArgs a) {
-  extern __shared__ float xs[];  // H floats
-  __shared__ float red[4];
-  const int m = blockIdx.x;
-  const int H = a.H;
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < H; k += 256) {
-    float v;
-    if (a.mode == RESID_COPY) {
-      v = a.x_in[(long long)m * H + k];
-    } else {
-      float sum = 0.f;
-      for (int sp = 0; sp < a.S; ++sp) sum += a.part[sp * a.part_ss + (long long)m * a.part_ld + k];
-      v = a.mode == RESID_ADD ? a.x_in[(long long)m * H + k] + sum : sum;
-    }
-    xs[k] = v;
-    ss += v * v;
-  }
-  if (a.mode == RESID_NORM_FIRST) {
-    const float tot = block_sum256(ss, red);
-    const float rs = rsqrtf(tot / H + a.eps);
-    ss = 0.f;
-    for (int k = threadIdx.x; k < H; k += 256) {
-      const float v = a.g0[k] * (xs[k] * rs);
-      xs[k] = v;
-      ss += v * v;
-    }
-  }
-  for (int k = threadIdx.x; k < H; k += 256) a.x_out[(long long)m * H + k] = xs[k];
-  if (!a.g1) return;
-  const float tot = block_sum256(ss, red);
-  const float rs = rsqrtf(tot / H + a.eps);
-  float dot = 0.f;
-  for (int k = threadIdx.x; k < H; k += 256) {
-    const float v = a.g1[k] * (xs[k] * rs);
-    if (a.fd.ptr) frag_put(a.fd, 0, m, k, v);
-    if (a.hidden_out) a.hidden_out[(long long)m * H + k] = v;
-    if (a.conf_wh) dot += v * a.conf_wh[k];
-  }
-  if (a.conf_wh) {
-    dot = block_sum256(dot, red);
-    if (threadIdx.x == 0) a.hconf[m] = dot;
-  }
-}
-
-__device__ __forceinline__ void rope_pair(float x0, float x1, double pos, double f, float& y0, float& y1) {
-  double sn, cs;
-  sincos(pos * f, &sn, &cs);
-  const float c = (float)cs, s = (float)sn;
-  y0 = x0 * c - x1 * s;
-  y1 = x0 * s + x1 * c;
-}
-
-// --------------------------------------------------- fused q_a / kv_a post --
-__global__ __launch_bounds__(256) void k_qkva_post(QkvaArgs a) {
-  extern __shared__ float buf[];  // q_lora + latent
-  __shared__ float red[4];
-  const int m = blockIdx.x;
-  const int N = a.q_lora + a.latent;
-  for (int k = threadIdx.x; k < N; k += 256) {
-    float sum = 0.f;
-    for (int sp = 0; sp < a.S; ++sp) sum += a.part[sp * a.part_ss + (long long)m * a.part_ld + k];
-    buf[k] = sum;
-  }
-  __syncthreads();
-  float sq = 0.f, sc = 0.f;
-  for (int k = threadIdx.x; k < a.q_lora; k += 256) sq += buf[k] * buf[k];
-  for (int k = threadIdx.x; k < a.r; k += 256) sc += buf[a.q_lora + k] * buf[a.q_lora + k];
-  const float rq = rsqrtf(block_sum256(sq, red) / a.q_lora + a.eps);
-  const float rc = rsqrtf(block_sum256(sc, red) / a.r + a.eps);
-  for (int k = threadIdx.x; k < a.q_lora; k += 256) frag_put(a.fd_qb, 0, m, k, a.g_qa[k] * (buf[k] * rq));
-  const int s = m / a.block, i = m % a.block;
-  const double pos = (double)(a.offs[s + 1] - a.offs[s] + i);
-  const long long ob = (long long)m * a.latent;
-  for (int k = threadIdx.x; k < a.latent; k += 256) {
-    float v;
-    if (k < a.r) {
-      v = a.g_kva[k] * (buf[a.q_lora + k] * rc);
-    } else {
-      const int e = k - a.r, pr = e >> 1;
-      float y0, y1;
-      rope_pair(buf[a.q_lora + a.r + 2 * pr], buf[a.q_lora + a.r + 2 * pr + 1], pos, a.freqs[pr], y0, y1);
-      v = (e & 1) ? y1 : y0;
-    }
-    if (a.kv_f32) ((float*)a.bkeys)[ob + k] = v;
-    else ((uint16_t*)a.bkeys)[ob + k] = (uint16_t)f32_to_bf16_bits(v);
-  }
-}
-
-// ------------------------------------------------------------- q_b post --
-__global__ __launch_bounds__(256) void k_qb_post(QbArgs a) {
-  const int m = blockIdx.x;
-  const int s = m / a.block, i = m % a.block;
-  const double pos = (double)(a.offs[s + 1] - a.offs[s] + i);
-  const int hd = a.dn + a.dr;
-  const int N = a.nh * hd;
-  for (int k = threadIdx.x; k < N; k += 256) {
-    const int h = k / hd, e = k % hd;
-    auto val = [&](int kk) {
-      float sum = 0.f;
-      for (int sp = 0; sp < a.S; ++sp) sum += a.part[sp * a.part_ss + (long long)m * a.part_ld + kk];
-      return sum;
-    };
-    if (e < a.dn) {
-      frag_put(a.fd_uk, h, m, e, val(k));
-    } else {
-      const int er = e - a.dn, pr = er >> 1;
-      const int kb = h * hd + a.dn + 2 * pr;
-      float y0, y1;
-      rope_pair(val(kb), val(kb + 1), pos, a.freqs[pr], y0, y1);
-      const float v = (er & 1) ? y1 : y0;
-      const long long qi = ((long long)s * a.rows_pad + i * a.nh + h) * a.DQ + a.r + er;
-      if (a.q_f32) ((float*)a.q)[qi] = v;
-      else ((uint16_t*)a.q)[qi] = (uint16_t)f32_to_bf16_bits(v);
-    }
-  }
-}
-
-// ------------------------------------------------------------ absorb post --
-__global__ __launch_bounds__(256) void k_absorb_post(AbsorbArgs a) {
-  const int m = blockIdx.x;
-  const int s = m / a.block, i = m % a.block;
-  const int N = a.nh * a.r;
-  for (int k = threadIdx.x; k < N; k += 256) {
-    const int h = k / a.r, c = k % a.r;
-    const float v = a.part[(long long)m * a.part_ld + k];
-    const long long qi = ((long long)s * a.rows_pad + i * a.nh + h) * a.DQ + c;
-    if (a.q_f32) ((float*)a.q)[qi] = v;
-    else ((uint16_t*)a.q)[qi] = (uint16_t)f32_to_bf16_bits(v);
-  }
-}
-
-// ------------------------------------------------------ plain / SwiGLU copy --
-__global__ __launch_bounds__(256) void k_to_frag(FragArgs a) {
-  const int m = blockIdx.x;
-  for (int k = threadIdx.x; k < a.K; k += 256) {
-    float v = 0.f, u = 0.f;
-    for (int sp = 0; sp < a.S; ++sp) {
-      const float* p = a.part + sp * a.part_ss + (long long)m * a.part_ld;
-      v += p[k];
-      if (a.swiglu) u += p[a.K + k];
-    }
-    if (a.swiglu) v = v / (1.f + __expf(-v)) * u;
-    frag_put(a.fd, 0, m, k, v);
-  }
-}
-
 // ------------------------------------------------------------ Markov final --
+// Tokens from the argmax keys, confidence sigmoid(w_h . hf_i + w_m . u_i + b)
+// with hf_i = rs_final * g_final * x, and the optional hidden output.
 __global__ __launch_bounds__(256) void k_markov_final(MarkovFinalArgs a) {
   __shared__ float red[4];
   __shared__ int toks[64];
+  __shared__ float rsv[64];
   const int s = blockIdx.x;
   if (threadIdx.x < a.block) {
     const unsigned long long* k = a.keys + ((long long)s * a.block + threadIdx.x) * KEY_SLOTS;
@@ -199,8 +50,19 @@ __global__ __launch_bounds__(256) void k_markov_final(MarkovFinalArgs a) {
     for (int i = 0; i < KEY_SLOTS; ++i) best = best > k[i] ? best : k[i];
     toks[threadIdx.x] = key_index(best);
     a.tokens[s * a.block + threadIdx.x] = key_index(best);
+    const int m = s * a.block + threadIdx.x;
+    const float* p = a.rs_final.ssq + (long long)m * SSQ_LD;
+    float t = 0.f;
+    for (int c = 0; c < a.rs_final.nch; ++c) t += p[c];
+    rsv[threadIdx.x] = rsqrtf(t * a.rs_final.invn + a.rs_final.eps);
   }
   __syncthreads();
+  if (a.hidden) {
+    for (int i = 0; i < a.block; ++i) {
+      const long long row = (long long)(s * a.block + i) * a.H;
+      for (int k = threadIdx.x; k < a.H; k += 256) a.hidden[row + k] = a.g_final[k] * a.x[row + k] * rsv[i];
+    }
+  }
   for (int i = 0; i < a.block; ++i) {
     int tp;
     if (i == 0) tp = a.prev_token[s];
@@ -215,7 +77,10 @@ __global__ __launch_bounds__(256) void k_markov_final(MarkovFinalArgs a) {
     }
     d = block_sum256(d, red);
     if (threadIdx.x == 0) {
-      const float x = a.hconf[s * a.block + i] + d + a.conf_b[0];
+      const float* dp = a.dot + (long long)(s * a.block + i) * SSQ_LD;
+      float hd = 0.f;
+      for (int c = 0; c < a.nch; ++c) hd += dp[c];
+      const float x = rsv[i] * hd + d + a.conf_b[0];
       a.conf[s * a.block + i] = 1.f / (1.f + __expf(-x));
     }
   }
@@ -343,31 +208,6 @@ __global__ __launch_bounds__(256) void k_dequant(PackedMat w, float* out) {
 
 hipError_t launch_init(const InitArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_init, dim3(512), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_resid_norm(const ResidArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_resid_norm, dim3(a.M), dim3(256), a.H * sizeof(float), st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_qkva_post(const QkvaArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_qkva_post, dim3(a.M), dim3(256), (a.q_lora + a.latent) * sizeof(float), st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_qb_post(const QbArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_qb_post, dim3(a.M), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_absorb_post(const AbsorbArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_absorb_post, dim3(a.M), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_to_frag(const FragArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_to_frag, dim3(a.M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

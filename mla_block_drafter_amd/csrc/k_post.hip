@@ -1,0 +1,214 @@
+// Column-parallel kernels between the GEMMs of the draft pass.
+//
+// RMSNorm(x; g) = g * x * rs with one scale rs = 1/sqrt(mean(x^2) + eps) per
+// row.  Because rs is a per-row constant it commutes with the next matrix
+// product: W (g * x * rs) = rs * (W (g * x)).  So a producer never waits for a
+// whole-row reduction: it writes the fragments of g * x for the next GEMM
+// plus one partial sum of squares per (row, 256-column chunk); the consumer
+// sums the chunks in a fixed order (deterministic) and applies rs to the GEMM
+// output.  Every kernel here therefore spreads over column chunks x row
+// groups instead of one workgroup per row.
+#include "kernels.h"
+
+namespace dspark {
+
+namespace {
+
+// One row per workgroup (blockIdx.y), 256 columns per workgroup (blockIdx.x).
+
+__device__ __forceinline__ float row_scale(const RowScale& s, int m) {
+  if (!s.ssq) return 1.f;
+  const float* p = s.ssq + (long long)m * SSQ_LD;
+  float t = 0.f;
+  for (int c = 0; c < s.nch; ++c) t += p[c];
+  return rsqrtf(t * s.invn + s.eps);
+}
+
+// Row scale of row m, broadcast through LDS.
+__device__ __forceinline__ float shared_row_scale(const RowScale& s, int m, float* slot) {
+  if (threadIdx.x == 0) *slot = row_scale(s, m);
+  __syncthreads();
+  return *slot;
+}
+
+// Sum of the split-K partials of element (m, c): four independent chains so
+// the loads are in flight together; fixed order, hence deterministic.
+__device__ __forceinline__ float part_sum(const PartIn& p, int m, long long c) {
+  const float* q = p.part + (long long)m * p.ld + c;
+  float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+  int s = 0;
+  for (; s + 4 <= p.S; s += 4) {
+    v0 += q[s * p.ss];
+    v1 += q[(s + 1) * p.ss];
+    v2 += q[(s + 2) * p.ss];
+    v3 += q[(s + 3) * p.ss];
+  }
+  for (; s < p.S; ++s) v0 += q[s * p.ss];
+  return (v0 + v1) + (v2 + v3);
+}
+
+__device__ __forceinline__ void rope_pair(float x0, float x1, double pos, double f, float& y0, float& y1) {
+  double sn, cs;
+  sincos(pos * f, &sn, &cs);
+  const float c = (float)cs, s = (float)sn;
+  y0 = x0 * c - x1 * s;
+  y1 = x0 * s + x1 * c;
+}
+
+// ------------------------------------------------------------- residual --
+__global__ __launch_bounds__(256) void k_post_resid(ResidPost a) {
+  __shared__ float red[4];
+  __shared__ float rs;
+  const int m = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  float r = 1.f;
+  if (a.mode == RP_NORM) r = shared_row_scale(a.rs_in, m, &rs);
+  float sq = 0.f, dt = 0.f;
+  if (c < a.H) {
+    const long long i = (long long)m * a.H + c;
+    float x;
+    switch (a.mode) {
+      case RP_SUM: x = part_sum(a.p, m, c); break;
+      case RP_ADD: x = a.x_in[i] + part_sum(a.p, m, c); break;
+      case RP_NORM: x = a.g0[c] * (a.x_in[i] * r); break;
+      default: x = a.x_in[i]; break;
+    }
+    a.x_out[i] = x;
+    sq = x * x;
+    if (a.g1) {
+      const float v = a.g1[c] * x;
+      frag_put(a.fd, 0, m, c, v);
+      if (a.dotw) dt = v * a.dotw[c];
+    }
+  }
+  if (a.ssq_out) {
+    sq = block_sum256(sq, red);
+    if (threadIdx.x == 0) a.ssq_out[m * SSQ_LD + blockIdx.x] = sq;
+  }
+  if (a.dot_out) {
+    dt = block_sum256(dt, red);
+    if (threadIdx.x == 0) a.dot_out[m * SSQ_LD + blockIdx.x] = dt;
+  }
+}
+
+// ------------------------------------------------------ fused q_a / kv_a --
+// x-chunks 0..ncq-1: the q_lora columns; chunk ncq: the latent columns of the
+// row (kv_a norm over kv_lora, rope of the rope part) -> block keys.
+__global__ __launch_bounds__(256) void k_post_qkva(QkvaPost a) {
+  __shared__ float red[4];
+  __shared__ float rs;
+  __shared__ float lat[1024];
+  const int m = blockIdx.y;
+  const float r = shared_row_scale(a.rs_in, m, &rs);
+  const int ncq = (a.q_lora + 255) / 256;
+  if ((int)blockIdx.x < ncq) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    float sq = 0.f;
+    if (c < a.q_lora) {
+      const float v = r * part_sum(a.p, m, c);
+      sq = v * v;
+      frag_put(a.fd_qb, 0, m, c, a.g_qa[c] * v);
+    }
+    sq = block_sum256(sq, red);
+    if (threadIdx.x == 0) a.ssq_cq[m * SSQ_LD + blockIdx.x] = sq;
+    return;
+  }
+  float s2 = 0.f;
+  for (int k = threadIdx.x; k < a.latent; k += 256) {
+    const float v = r * part_sum(a.p, m, a.q_lora + k);
+    lat[k] = v;
+    if (k < a.r) s2 += v * v;
+  }
+  const float rc = rsqrtf(block_sum256(s2, red) / a.r + a.eps);  // also orders lat[]
+  const int s = m / a.block, i = m % a.block;
+  const double pos = (double)(a.offs[s + 1] - a.offs[s] + i);
+  for (int k = threadIdx.x; k < a.latent; k += 256) {
+    float v;
+    if (k < a.r) {
+      v = a.g_kva[k] * (lat[k] * rc);
+    } else {
+      const int e = k - a.r, pr = e >> 1;
+      float y0, y1;
+      rope_pair(lat[a.r + 2 * pr], lat[a.r + 2 * pr + 1], pos, a.freqs[pr], y0, y1);
+      v = (e & 1) ? y1 : y0;
+    }
+    const long long o = (long long)m * a.latent + k;
+    if (a.kv_f32) ((float*)a.bkeys)[o] = v;
+    else ((uint16_t*)a.bkeys)[o] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+// ------------------------------------------------------------------ q_b --
+// One thread per column pair: nope pairs -> absorb fragments (group = head),
+// rope pairs -> rotated into the query buffer.
+__global__ __launch_bounds__(256) void k_post_qb(QbPost a) {
+  __shared__ float rs;
+  const int m = blockIdx.y;
+  const float r = shared_row_scale(a.rs, m, &rs);
+  const int hd = a.dn + a.dr;
+  const int c0 = 2 * (blockIdx.x * 256 + threadIdx.x);
+  if (c0 >= a.nh * hd) return;
+  const int h = c0 / hd, e = c0 % hd;
+  const float v0 = r * part_sum(a.p, m, c0);
+  const float v1 = r * part_sum(a.p, m, c0 + 1);
+  if (e < a.dn) {
+    frag_put(a.fd_uk, h, m, e, v0);
+    frag_put(a.fd_uk, h, m, e + 1, v1);
+  } else {
+    const int s = m / a.block, i = m % a.block;
+    const double pos = (double)(a.offs[s + 1] - a.offs[s] + i);
+    const int er = e - a.dn;
+    float y0, y1;
+    rope_pair(v0, v1, pos, a.freqs[er >> 1], y0, y1);
+    const long long qi = ((long long)s * a.rows_pad + i * a.nh + h) * a.DQ + a.r + er;
+    if (a.q_f32) {
+      ((float*)a.q)[qi] = y0;
+      ((float*)a.q)[qi + 1] = y1;
+    } else {
+      ((uint32_t*)a.q)[qi >> 1] = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+    }
+  }
+}
+
+// --------------------------------------------------------------- SwiGLU --
+__global__ __launch_bounds__(256) void k_post_swiglu(SwigluPost a) {
+  __shared__ float rs;
+  const int m = blockIdx.y;
+  const float r = shared_row_scale(a.rs, m, &rs);
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.inter) return;
+  const float g = r * part_sum(a.p, m, c);
+  const float u = r * part_sum(a.p, m, a.inter + c);
+  frag_put(a.fd, 0, m, c, g / (1.f + __expf(-g)) * u);
+}
+
+}  // namespace
+
+hipError_t launch_post_resid(const ResidPost& a, hipStream_t st) {
+  dim3 grid((a.H + 255) / 256, a.M);
+  if (grid.x > SSQ_LD) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_post_resid, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_post_qkva(const QkvaPost& a, hipStream_t st) {
+  if (a.latent > 1024) return hipErrorInvalidValue;
+  dim3 grid((a.q_lora + 255) / 256 + 1, a.M);
+  hipLaunchKernelGGL(k_post_qkva, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_post_qb(const QbPost& a, hipStream_t st) {
+  const int pairs = a.nh * (a.dn + a.dr) / 2;
+  dim3 grid((pairs + 255) / 256, a.M);
+  hipLaunchKernelGGL(k_post_qb, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_post_swiglu(const SwigluPost& a, hipStream_t st) {
+  dim3 grid((a.inter + 255) / 256, a.M);
+  hipLaunchKernelGGL(k_post_swiglu, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -11,19 +11,35 @@ namespace dspark {
 // ------------------------------------------------------------- skinny GEMM --
 // out[split][m][col] = sum over the split's k range of act[m][k] * W[col][k]
 // for the M activation rows (M = 7 per sequence), W streamed once from HBM.
-enum { GEMV_STORE = 0, GEMV_MARKOV = 1 };
+enum { GEMV_STORE = 0, GEMV_MARKOV = 1, GEMV_QLAT = 2, GEMV_FRAG = 3 };
+
+// Partial sums of squares per (row, 256-column chunk), row stride SSQ_LD.
+constexpr int SSQ_LD = 128;
+
+// Per-row RMSNorm scale rs[m] = 1/sqrt(sum_c ssq[m][c] * invn + eps); ssq = null: 1.
+struct RowScale {
+  const float* ssq;
+  int nch;
+  float invn, eps;
+};
 
 struct GemvArgs {
   PackedMat w;
-  const void* act;        // fragment buffer (STORE) or plain gather table (MARKOV)
-  long long act_gstride;  // elements per group in the fragment buffer
+  const void* act;        // input buffer (STORE/QLAT/FRAG) or plain gather table (MARKOV)
+  long long act_gstride;  // elements per group of the input buffer
+  int act_ld;             // fp32 rows: row stride (elements)
   int M;                  // valid activation rows
   int hilo;               // bf16 family with M <= 8
   int ksteps_per_split;   // in 32-wide blocks (bf16 family) or 16-wide groups (f32)
+  RowScale rs;            // optional output row scale (STORE, FRAG)
   // STORE
   float* out;             // [S][M][out_ld]
   long long out_ld;
   long long out_split_stride;
+  // QLAT: output (m, head g, column j) -> query buffer row (m % block) * nh + g
+  void* q; int q_f32, DQ, rows_pad, nh;
+  // FRAG: output (m, col) -> fragments of the next GEMM
+  FragDesc fd;
   // MARKOV: M = n_seq; activation row m = W1[t_prev(m)], t_prev resolved in-kernel
   int gather_ld;          // elements per table row (>= Kp)
   const int32_t* prev_token;
@@ -37,9 +53,12 @@ struct GemvArgs {
 struct GemvPlan {
   int MT, TPW, S, ksteps_per_split, hilo;
   int grid_x;
+  int amode;              // activation operand: 0 prepared global fragments,
+                          // 1 fp32 rows -> bf16 fragments in LDS,
+                          // 2 fp32 rows -> int8 hi/lo codes in LDS (Q8_0, M <= 8)
 };
 
-GemvPlan plan_gemv(const PackedMat& w, int M, bool markov);
+GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather = false);
 hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 
 // --------------------------------------------------------------- attention --
@@ -74,63 +93,66 @@ struct InitArgs {
 };
 hipError_t launch_init(const InitArgs& a, hipStream_t st);
 
-enum { RESID_COPY = 0, RESID_ADD = 1, RESID_NORM_FIRST = 2 };
-struct ResidArgs {
-  const float* part; int S; long long part_ld, part_ss;
-  const float* x_in; float* x_out;
-  int mode;
-  const float* g0;        // NORM_FIRST gain
-  const float* g1;        // gain of the normed output fed to the next GEMM (null: none)
-  float eps;
-  int M, H;
-  FragDesc fd;            // next GEMM input
-  float* hidden_out;      // optional [M][H] normed output
-  const float* conf_wh;   // optional [H]: hconf[m] = normed . conf_wh
-  float* hconf;
+// Split-K partial sums [S][M][ld] of one GEMM.
+struct PartIn {
+  const float* part;
+  int S;
+  long long ld, ss;
 };
-hipError_t launch_resid_norm(const ResidArgs& a, hipStream_t st);
 
-struct QkvaArgs {
-  const float* part; int S; long long part_ld, part_ss;
+enum { RP_COPY = 0, RP_SUM = 1, RP_ADD = 2, RP_NORM = 3 };
+struct ResidPost {
+  PartIn p;
+  int mode;               // COPY: x = x_in; SUM: x = sum p; ADD: x = x_in + sum p;
+                          // NORM: x = g0 * x_in * rs_in
+  const float* x_in; float* x_out;
+  RowScale rs_in; const float* g0;
+  int M, H;
+  const float* g1;        // fragments of g1 * x for the next GEMM (null: none)
+  FragDesc fd;
+  float* ssq_out;         // [M][SSQ_LD] chunk sums of x^2 (null: none)
+  const float* dotw;      // chunk sums of g1 * x * dotw -> dot_out (null: none)
+  float* dot_out;
+};
+hipError_t launch_post_resid(const ResidPost& a, hipStream_t st);
+
+struct QkvaPost {
+  PartIn p; RowScale rs_in;
   int M, q_lora, r, dr, latent, block;
   const float* g_qa; const float* g_kva; float eps;
-  FragDesc fd_qb;
+  FragDesc fd_qb; float* ssq_cq;
   void* bkeys; int kv_f32;   // [M][latent]
   const int32_t* offs;
   const double* freqs;        // [dr/2]
 };
-hipError_t launch_qkva_post(const QkvaArgs& a, hipStream_t st);
+hipError_t launch_post_qkva(const QkvaPost& a, hipStream_t st);
 
-struct QbArgs {
-  const float* part; int S; long long part_ld, part_ss;
+struct QbPost {
+  PartIn p; RowScale rs;
   int M, nh, dn, dr, r, block, DQ, rows_pad;
   FragDesc fd_uk;             // absorb input, groups = heads
   void* q; int q_f32;         // [n_seq][rows_pad][DQ]
   const int32_t* offs;
   const double* freqs;
 };
-hipError_t launch_qb_post(const QbArgs& a, hipStream_t st);
+hipError_t launch_post_qb(const QbPost& a, hipStream_t st);
 
-struct AbsorbArgs {
-  const float* part; long long part_ld;   // [M][nh*r]
-  int M, nh, r, block, DQ, rows_pad;
-  void* q; int q_f32;
-};
-hipError_t launch_absorb_post(const AbsorbArgs& a, hipStream_t st);
-
-struct FragArgs {           // plain copy of GEMM output into the next fragments
-  const float* part; int S; long long part_ld, part_ss;
-  int M, K;
+struct SwigluPost {
+  PartIn p; RowScale rs;
+  int M, inter;
   FragDesc fd;
-  int swiglu;               // 1: value = silu(part[k]) * part[K + k]
 };
-hipError_t launch_to_frag(const FragArgs& a, hipStream_t st);
+hipError_t launch_post_swiglu(const SwigluPost& a, hipStream_t st);
 
 struct MarkovFinalArgs {
   const unsigned long long* keys;
   const int32_t* prev_token; const int32_t* forced;
   const void* w1; int w1_f32; int w1_ld; int R;
-  const float* conf_wm; const float* conf_b; const float* hconf;
+  const float* conf_wm; const float* conf_b;
+  const float* dot; int nch;  // chunk sums of (g_final * x) . w_h, row stride SSQ_LD
+  RowScale rs_final;
+  const float* x; const float* g_final; int H;
+  float* hidden;              // optional [M][H] = rs * g_final * x
   int32_t* tokens; float* conf;
   int n_seq, block, vocab;
 };

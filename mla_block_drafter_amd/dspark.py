@@ -64,7 +64,12 @@ class BlockIn(C.Structure):
 
 
 class BlockOut(C.Structure):
-    _fields_ = [("tokens", C.c_void_p), ("conf", C.c_void_p), ("logits", C.c_void_p), ("hidden", C.c_void_p)]
+    _fields_ = [("tokens", C.c_void_p), ("conf", C.c_void_p), ("logits", C.c_void_p), ("hidden", C.c_void_p),
+                ("stage_events", C.POINTER(C.c_void_p))]
+
+
+N_STAGES = 4
+STAGES = ["fc", "layers", "lm_head", "markov"]
 
 
 class DsparkError(RuntimeError):
@@ -196,7 +201,9 @@ class Model:
         return torch.empty(self.workspace_bytes(n_seq, total_ctx), dtype=torch.uint8, device="cuda")
 
     def draft_block(self, captured, kv: Sequence, kv_offsets, prev_token, total_ctx: int, tokens, conf,
-                    workspace, logits=None, hidden=None, forced_prev=None, stream=None) -> None:
+                    workspace, logits=None, hidden=None, forced_prev=None, stream=None,
+                    stage_events=None) -> None:
+        """stage_events: optional list of 2*N_STAGES torch.cuda.Event (enable_timing)."""
         import torch
         n_seq = int(prev_token.shape[0])
         kv_arr = (C.c_void_p * len(kv))(*[t.data_ptr() if t is not None else None for t in kv])
@@ -210,7 +217,10 @@ class Model:
         bi.kv_offsets = kv_offsets.data_ptr()
         bi.prev_token = prev_token.data_ptr()
         bi.forced_prev = _ptr(forced_prev)
-        bo = BlockOut(tokens.data_ptr(), conf.data_ptr(), _ptr(logits), _ptr(hidden))
+        bo = BlockOut(tokens.data_ptr(), conf.data_ptr(), _ptr(logits), _ptr(hidden), None)
+        if stage_events is not None:
+            evs = (C.c_void_p * (2 * N_STAGES))(*[e.cuda_event for e in stage_events])
+            bo.stage_events = evs
         check(lib().dspark_draft_block(self.handle, C.byref(bi), C.byref(bo), workspace.data_ptr(),
                                        workspace.numel(), _stream_ptr(stream)))
 

@@ -71,11 +71,26 @@ def uniform(shape, seed: int, idx: int, lo: float, hi: float) -> np.ndarray:
 # storage encoders (host-side weight conversion; the device only decodes)
 # ----------------------------------------------------------------------------
 
+def _bf16_chunk(u: np.ndarray) -> np.ndarray:
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return r.astype(np.uint16)
+    if u.size <= CHUNK:
+        return _bf16_chunk(u)
+    flat = u.reshape(-1)
+    out = np.empty(flat.size, dtype=np.uint16)
+
+    def work(j):
+        lo, hi = j * CHUNK, min(flat.size, (j + 1) * CHUNK)
+        out[lo:hi] = _bf16_chunk(flat[lo:hi])
+
+    with _pool() as ex:
+        list(ex.map(work, range((flat.size + CHUNK - 1) // CHUNK)))
+    return out.reshape(u.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

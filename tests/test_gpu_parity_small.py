@@ -70,6 +70,17 @@ def test_small_ragged_all_formats(fmt):
     print(fmt, "near-ties", ties, flush=True)
 
 
+@pytest.mark.parametrize("fmt", ["q8_0", "bf16", "fp8"])
+def test_small_bs1_formats(fmt):
+    """One sequence (7 activation rows): the hi/lo activation paths, including
+    the int8 MFMA path of Q8_0 weights."""
+    from tests.gpu_common import full_parity
+    wl = C.Workload(f"small_bs1_{fmt}", SMALL, FORMATS[fmt], seed=779, kv_lens=(77,), fixture_gains=True)
+    g = _gw(wl)
+    ref = O.draft_block(wl, g.stored, g.inputs)
+    full_parity(g, ref, tol=2e-2, max_ties=1)
+
+
 def test_small_sharp_attention_bf16():
     from tests.gpu_common import full_parity
     wl = C.Workload("small_sharp", SMALL, C.ALL_BF16, seed=778, kv_lens=(129,), fixture_gains=True,
