@@ -10,7 +10,7 @@
 //
 // bf16 path (split-K, flash-decoding style): a workgroup of 4 waves owns 64
 // query rows and one slot of C keys.  Key tiles of 32 rows are staged in LDS
-// row-major.  S^T = K Q^T takes the key rows as the A operand (16-byte LDS
+// row-major, double-buffered.  S^T = K Q^T takes the key rows as the A operand (16-byte LDS
 // reads), so the probabilities land with one query row per lane column,
 // which is already the B-operand layout of P^T for O^T = V^T P^T: the
 // probabilities never leave registers (the 32 keys' order inside the MFMA
@@ -19,6 +19,8 @@
 // c_kv, the first kv_lora columns of the key row), so no transposed copy is
 // staged.  Online softmax state (m, l) is per lane column.  Partials per slot
 // are merged by k_attn_combine in a fixed order.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace dspark {
@@ -26,6 +28,7 @@ namespace dspark {
 namespace {
 
 constexpr int KT = 32;  // keys per LDS tile
+constexpr float RESCALE_SLACK = 8.f;  // natural-log units
 constexpr int MAX_COMBINE_SLOTS = 4096;
 
 __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s, int& p, int& len,
@@ -45,83 +48,238 @@ __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s,
   s = -1;
 }
 
+// ---------------------------------------------------------------- tiles --
+// A key tile (KT = 32 keys) is fetched with gfx950's direct-to-LDS loads
+// (global_load_lds_dwordx4: a wave writes 64 consecutive 16-byte LDS chunks,
+// no registers involved).  Two regions per tile buffer:
+//   A: the value part (first R = 8 CA elements of the key row), one key per
+//      load, rows CA + 1 chunks apart (the pad chunk spreads the banks);
+//   B: the rope part (CB chunks per key), 64 / CB keys per load, chunk p of
+//      key r holding source chunk p ^ (r % CB).
+// Loads that fall past the slot read a valid dummy row (the sequence's first
+// block key); their scores are masked and their probabilities are zero.
+// Two tile buffers: tile t+1 streams in while tile t computes.
+//
+// Inside each 16-key half of a tile, MFMA row m holds key pi(m) =
+// (g & 1) + 8 (g >> 1) + 2 j for m = 4 g + j.  The score fragment of lane
+// group g then covers keys {a, a+2, a+4, a+6}, whose padded rows fall on
+// disjoint banks when the transposing LDS read gathers V for the same keys.
+__device__ __forceinline__ int key_perm(int m) { return (m >> 2 & 1) + 8 * (m >> 3) + 2 * (m & 3); }
+
+template <int CA, int CB>
+struct TileGeom {
+  static constexpr int ROW_A = (CA + 1) * 8;      // elements between region-A rows
+  static constexpr int SIZE_A = KT * ROW_A;       // elements
+  static constexpr int KPB = 64 / CB;             // region-B keys per load
+  static constexpr int NB_A = KT;                 // loads for region A
+  static constexpr int NB_B = KT / KPB;           // loads for region B
+  static constexpr int NBLK = NB_A + NB_B;
+  static constexpr int BUF = SIZE_A + KT * CB * 8;  // elements per tile buffer
+  static constexpr int NMIN = NBLK / 4;           // loads per wave per tile (at least)
+  static_assert(64 % CB == 0 && KT % KPB == 0 && CA <= 64, "tile geometry");
+};
+
+// This wave's share of one key tile: region-A keys wave, wave + 4, ... and
+// region-B load number wave.  Everything but the lane offsets is uniform, so
+// the address selection stays on the scalar unit.
+template <int CA, int CB>
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, int lane, int wave, int kt0, int k_end, int s,
+                                           int len, int off, const uint16_t* cache, const uint16_t* bk,
+                                           const uint16_t* dummy, uint16_t* dst) {
+  using G = TileGeom<CA, CB>;
+  static_assert(G::NB_A % 4 == 0 && G::NB_B <= 4, "load split over four waves");
+  auto row_ptr = [&](int j) {
+    const uint16_t* c = cache + (long long)(off + j) * a.latent;
+    const uint16_t* k = bk + (long long)(s * a.block + (j - len)) * a.latent;
+    const uint16_t* r = j < len ? c : k;
+    return j < k_end ? r : dummy;
+  };
+#pragma unroll
+  for (int i = 0; i < G::NB_A / 4; ++i) {
+    const int b = wave + 4 * i;
+    const uint16_t* src = row_ptr(kt0 + b) + 8 * lane;
+    if (CA == 64 || lane < CA) __builtin_amdgcn_global_load_lds(src, dst + b * G::ROW_A, 16, 0, 0);
+  }
+  if (wave < G::NB_B) {
+    const int r = wave * G::KPB + lane / CB, p = lane % CB;
+    const uint16_t* src = row_ptr(kt0 + r) + 8 * (CA + (p ^ (r % CB)));
+    __builtin_amdgcn_global_load_lds(src, dst + G::SIZE_A + wave * 512, 16, 0, 0);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int QK_AHEAD = 6;  // K fragments in flight ahead of the MFMA using them
+constexpr int PV_AHEAD = 4;  // V fragment pairs in flight ahead of the MFMA using them
+
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
+}
+
+// LDS reads of the tile loop are issued from inline assembly with explicit,
+// register-tied waits.  Two reasons: the compiler makes a transposing LDS read
+// wait for every outstanding direct-to-LDS load (including the prefetch of the
+// next tile), and under this register pressure it keeps only two ordinary LDS
+// reads in flight.  LDS operations complete in issue order, so "at most n
+// outstanding" covers every read issued n or more reads earlier.  Scalar
+// memory loads, which share the counter but complete out of order, are never
+// issued inside the tile loop.
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128(uint32_t addr, u32x4& v) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+
+template <int OFF_LO, int OFF_HI>
+__device__ __forceinline__ void tr_read_pair(uint32_t addr, u32x2& lo, u32x2& hi) {
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+               : "=v"(lo), "=v"(hi)
+               : "v"(addr), "i"(OFF_LO), "i"(OFF_HI));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4& v) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait_pair(u32x2& lo, u32x2& hi) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo), "+v"(hi) : "n"(N));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 template <int NKB, int NDT>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   constexpr int DQ = NKB * 32;
   constexpr int R = NDT * 16;
-  constexpr int KLD = DQ + 8;   // padded LDS row (elements), 16-byte aligned rows
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[KT * KLD];
+  constexpr int CA = R / 8, CB = (DQ - R) / 8;
+  using G = TileGeom<CA, CB>;
+  static_assert(CA % 4 == 0, "each k-step reads one region");
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * G::BUF];
 
   int s, p, len, off, J;
   slot_lookup(a, blockIdx.y, s, p, len, off, J);
   if (s < 0) return;  // uniform over the workgroup
   const int k_begin = p * a.C;
   const int k_end = min(J, k_begin + a.C);
+  const int ntiles = (k_end - k_begin + KT - 1) / KT;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile loads scalar
   const int row0 = blockIdx.x * 64 + wave * 16;
   const int myrow = row0 + (lane & 15);
+  const int grp = lane >> 4;
 
-  // Q fragments (B operand of S^T = K Q^T): row myrow, dims 32kb + 8(lane>>4).
+  const uint16_t* cache = (const uint16_t*)a.cache;
+  const uint16_t* bk = (const uint16_t*)a.bkeys;
+  const uint16_t* dummy = bk + (long long)s * a.block * a.latent;
+  issue_tile<CA, CB>(a, lane, wave, k_begin, k_end, s, len, off, cache, bk, dummy, k_lds);
+
+  // Q fragments (B operand of S^T = K Q^T): row myrow, dims 32kb + 8 grp.
   bf16x8 qf[NKB];
   {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((long long)s * a.rows_pad + myrow) * DQ + 8 * (lane >> 4);
+    const uint16_t* qrow = (const uint16_t*)a.q + ((long long)s * a.rows_pad + myrow) * DQ + 8 * grp;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) qf[kb] = *(const bf16x8*)(qrow + 32 * kb);
   }
+  // LDS element offsets inside a tile buffer
+  const int kA = key_perm(lane & 15);                 // key of this lane's A-operand row
+  const int offA = kA * G::ROW_A + 8 * grp;           // + 16 h ROW_A + 32 kb
+  const int offB = G::SIZE_A + kA * CB * 8;           // + 16 h CB 8 + chunk
+  // byte offsets of chunks 4 k + grp (k < CB / 4) of region B for this lane's key
+  uint32_t bx[CB / 4];
+#pragma unroll
+  for (int k = 0; k < CB / 4; ++k) bx[k] = 16 * ((4 * k + grp) ^ (kA % CB));
+  const int kV = key_perm(4 * grp + ((lane & 15) >> 2));  // key this lane addresses for V
+  const int offV = kV * G::ROW_A + 4 * (lane & 3);    // + 16 h ROW_A + 16 d
+  int keyS[4];                                        // keys of this lane's score entries
+#pragma unroll
+  for (int j = 0; j < 4; ++j) keyS[j] = key_perm(4 * grp + j);
 
   f32x4 acc[NDT];
 #pragma unroll
   for (int d = 0; d < NDT; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const uint16_t* cache = (const uint16_t*)a.cache;
-  const uint16_t* bk = (const uint16_t*)a.bkeys;
-  constexpr int CHUNKS_PER_KEY = DQ / 8;
-
-  for (int kt0 = k_begin; kt0 < k_end; kt0 += KT) {
-    // ---- stage the key tile (row-major) and its transpose (value part) ----
-    for (int c = threadIdx.x; c < KT * CHUNKS_PER_KEY; c += 256) {
-      const int kk = c / CHUNKS_PER_KEY, d8 = (c % CHUNKS_PER_KEY) * 8;
-      const int j = kt0 + kk;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < k_end && d8 < a.latent) {
-        const uint16_t* src = j < len ? cache + (long long)(off + j) * a.latent + d8
-                                      : bk + (long long)(s * a.block + (j - len)) * a.latent + d8;
-        v = *(const u32x4*)src;
-      }
-      *(u32x4*)(k_lds + kk * KLD + d8) = v;
+  for (int t = 0; t < ntiles; ++t) {
+    const int kt0 = k_begin + t * KT;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      issue_tile<CA, CB>(a, lane, wave, kt0 + KT, k_end, s, len, off, cache, bk, dummy,
+                         k_lds + (buf ^ 1) * G::BUF);
+      wait_vmcnt<G::NMIN>();  // all but this wave's newest loads are done: tile t is in LDS
+    } else {
+      wait_vmcnt<0>();
     }
-    __syncthreads();
+    // the barrier intrinsic has no memory semantics of its own, so the
+    // compiler fences keep LDS accesses on their side of it (a __syncthreads
+    // would also drain the prefetch of the next tile)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint16_t* tb = k_lds + buf * G::BUF;
 
-    // ---- S^T for 32 keys x 16 rows: two 16-key MFMA tiles ----
-    f32x4 st[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = k_lds + (16 * h + (lane & 15)) * KLD + 8 * (lane >> 4);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 kf = *(const bf16x8*)(krow + 32 * kb);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kb], c, 0, 0, 0);
-      }
-      st[h] = c;
+    // ---- S^T for 32 keys x 16 rows: two 16-key MFMA tiles, read n = 2 kb + h
+    //      feeding accumulator h; the two chains alternate ----
+    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      constexpr int NR = 2 * NKB;
+      const uint32_t abase = lds_addr(tb + offA), bbase = lds_addr(tb + offB);
+      u32x4 kf[QK_AHEAD + 1];
+      auto issue = [&](auto NI) {
+        constexpr int n = decltype(NI)::value, kb = n / 2, h = n % 2;
+        if constexpr (4 * kb < CA)
+          lds_read_b128<2 * (16 * h * G::ROW_A + 32 * kb)>(abase, kf[n % (QK_AHEAD + 1)]);
+        else
+          lds_read_b128<2 * 16 * h * CB * 8>(bbase + bx[kb - CA / 4], kf[n % (QK_AHEAD + 1)]);
+      };
+      static_for<QK_AHEAD < NR ? QK_AHEAD : NR>(issue);
+      static_for<NR>([&](auto NI) {
+        constexpr int n = decltype(NI)::value;
+        if constexpr (n + QK_AHEAD < NR) issue(std::integral_constant<int, n + QK_AHEAD>{});
+        constexpr int ahead = NR - 1 - n < QK_AHEAD ? NR - 1 - n : QK_AHEAD;
+        u32x4& f = kf[n % (QK_AHEAD + 1)];
+        lds_wait<ahead>(f);
+        st[n % 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f), qf[n / 2], st[n % 2], 0, 0, 0);
+      });
     }
-    // lane holds keys kt0 + 16h + 4(lane>>4) + r for query row myrow
+    // lane holds keys kt0 + 16 h + keyS[r] for query row myrow
     float tmax = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = kt0 + 16 * h + 4 * (lane >> 4) + r;
+        const int j = kt0 + 16 * h + keyS[r];
         const float v = j < k_end ? st[h][r] * a.tau : -INFINITY;
         st[h][r] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float corr = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
+    // Lazy rescaling: the running reference m_run moves only when a score
+    // exceeds it by more than RESCALE_SLACK, so probabilities stay below
+    // e^RESCALE_SLACK and the accumulators are touched by the VALU only on
+    // the (rare, wave-uniform) rescale step.
+    if (__any(tmax > m_run + RESCALE_SLACK)) {
+      const bool up = tmax > m_run + RESCALE_SLACK;
+      const float corr = up ? __expf(m_run - tmax) : 1.f;
+      if (up) m_run = tmax;
+      l_run *= corr;
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) acc[d] *= corr;
+    }
     float psum = 0.f;
     u32x4 pw;
 #pragma unroll
@@ -129,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
       float pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[r] = m_new == -INFINITY ? 0.f : __expf(st[h][r] - m_new);
+        pr[r] = m_run == -INFINITY ? 0.f : __expf(st[h][r] - m_run);
         psum += pr[r];
       }
       pw[2 * h] = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
@@ -137,35 +295,47 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * corr + psum;
-    m_run = m_new;
+    l_run += psum;
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 
-    // ---- O^T += V^T P^T: lane's k slots map to keys 4(lane>>4)+{0..3} and
-    //      16 + 4(lane>>4) + {0..3}, matching the P fragment above; the A
-    //      operand holds V[key][dim = 16d + (lane & 15)] for those keys ----
-    const uint16_t* vbase = k_lds + 4 * (lane >> 4) * KLD + (lane & 15);
-#pragma unroll
-    for (int d = 0; d < NDT; ++d) {
-      const uint16_t* vcol = vbase + 16 * d;
-      u32x4 vv;
-      vv[0] = (uint32_t)vcol[0] | ((uint32_t)vcol[KLD] << 16);
-      vv[1] = (uint32_t)vcol[2 * KLD] | ((uint32_t)vcol[3 * KLD] << 16);
-      vv[2] = (uint32_t)vcol[16 * KLD] | ((uint32_t)vcol[17 * KLD] << 16);
-      vv[3] = (uint32_t)vcol[18 * KLD] | ((uint32_t)vcol[19 * KLD] << 16);
-      acc[d] *= corr;
-      acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[d], 0, 0, 0);
+    // ---- O^T += V^T P^T.  k slots 0..3 of lane group g are keys keyS[] of
+    //      the first half, slots 4..7 those of the second half, matching P.
+    //      The transposing read hands lane 4a + e of each 16-lane group
+    //      element e of the rows addressed by lanes a, a+4, a+8, a+12: lane
+    //      (lane & 15) = 4 j + a addresses key keyS[j], dims 16 d + 4 a, so
+    //      lane 4a + e receives dim 16 d + 4a + e of keys keyS[0..3] ----
+    {
+      const uint32_t vaddr = lds_addr(tb + offV);
+      u32x2 vlo[PV_AHEAD + 1], vhi[PV_AHEAD + 1];
+      auto issue = [&](auto DI) {
+        constexpr int d = decltype(DI)::value;
+        tr_read_pair<32 * d, 32 * d + 2 * 16 * G::ROW_A>(vaddr, vlo[d % (PV_AHEAD + 1)], vhi[d % (PV_AHEAD + 1)]);
+      };
+      static_for<PV_AHEAD < NDT ? PV_AHEAD : NDT>(issue);
+      static_for<NDT>([&](auto DI) {
+        constexpr int d = decltype(DI)::value;
+        if constexpr (d + PV_AHEAD < NDT) issue(std::integral_constant<int, d + PV_AHEAD>{});
+        constexpr int ahead = NDT - 1 - d < PV_AHEAD ? NDT - 1 - d : PV_AHEAD;
+        u32x2& lo = vlo[d % (PV_AHEAD + 1)];
+        u32x2& hi = vhi[d % (PV_AHEAD + 1)];
+        lds_wait_pair<2 * ahead>(lo, hi);
+        const u32x4 v4 = {lo[0], lo[1], hi[0], hi[1]};
+        acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v4), pf, acc[d], 0, 0, 0);
+      });
     }
-    __syncthreads();
+    // every wave is done reading this buffer before it is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
 
   // ---- partials: O^T[dim = 16d + 4(lane>>4) + r][row = myrow]; layout
   //      [row][slot][dim] so the combine of one row reads contiguous memory ----
   const long long prow = (long long)myrow * a.slots + blockIdx.y;
-  float* op = a.o_part + prow * a.r + 4 * (lane >> 4);
+  float* op = a.o_part + prow * a.r + 4 * grp;
 #pragma unroll
   for (int d = 0; d < NDT; ++d) *(f32x4*)(op + 16 * d) = acc[d];
-  if ((lane >> 4) == 0) {
+  if (grp == 0) {
     a.ml_part[prow * 2] = m_run;
     a.ml_part[prow * 2 + 1] = l_run;
   }

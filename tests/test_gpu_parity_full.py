@@ -1,0 +1,147 @@
+"""GPU parity at the full sizes of the draft pass.
+
+* the single full-size MLA attention layer (bf16, context 4096) and a
+  full-size Q8_0 decoder layer with its SwiGLU MLP, each against the oracle
+  run inline (one layer takes the oracle seconds);
+* whole passes (Q8_0 at context 8192; BF16 at context 98,304 with YaRN; FP8
+  per-channel over 16 ragged sequences) against oracle outputs stored by
+  tests/golden/make_golden.py: the hidden state on sampled elements, the
+  logits on each position's 64 largest entries plus a fixed random sample,
+  the confidence, the tokens (exact, or a certified near-tie whose gap is at
+  most twice the largest logit difference seen), and the acceptance length.
+Every case runs in the launch configuration bench.py times.
+"""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import dspark as O
+from synth import configs as C, gen
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mla_block_drafter_amd import dspark as D
+    D.lib()
+
+
+def _rel(g, r):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    return float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
+
+
+def test_single_full_size_mla_layer_bf16_ctx4096():
+    wl = C.CFG2
+    stored = gen.make_weights(wl)
+    inp = gen.make_inputs(wl)
+    x_in = np.ascontiguousarray(inp.x_in, np.float32)
+    _layer_case_with_inputs(wl, stored, x_in, inp, with_mlp=False)
+
+
+def _layer_case_with_inputs(wl, stored, x_in, inp, with_mlp):
+    from mla_block_drafter_amd import dspark as D
+    m = wl.model
+    W = O.Weights(stored)
+    x64 = x_in.astype(np.float64)
+    kv64 = O._decode_input(inp.caches[0], wl.formats.kv_cache)
+    ref = O.layer(m, W, 0, x64, [kv64], inp.kv_offsets, attn_only=not with_mlp)
+    model = D.Model(m, D.upload_stored(stored), layers_only=True)
+    xi = torch.from_numpy(x_in).cuda()
+    xo = torch.empty_like(xi)
+    kv = torch.from_numpy(inp.caches[0].view(np.int16)).cuda().view(torch.bfloat16)
+    ot = torch.from_numpy(inp.kv_offsets.astype(np.int32)).cuda()
+    ws = model.workspace(wl.n_seq, wl.total_ctx)
+    model.layer_forward(0, with_mlp, xi, xo, kv, ot, wl.total_ctx, ws)
+    torch.cuda.synchronize()
+    got = xo.cpu().numpy().astype(np.float64)
+    err = _rel(got - x64, ref - x64)   # compare the layer's update, not the residual
+    print(f"{wl.name} with_mlp={with_mlp}: rel err of the update {err:.2e}", flush=True)
+    assert err <= TOL, err
+
+
+def test_full_size_q8_0_layer_with_mlp_ctx8192():
+    """Layer 0 of the Q8_0 workload (same seeds and formats), MLP included."""
+    full = C.CFG3
+    one = full.replace(model=C.ModelConfig(n_layers=1), attn_only=False)
+    names = [n for n in C.tensor_names(full.model) if n.startswith("L0.")]
+    stored = gen.make_weights(full, names=names)
+    inp = gen.make_inputs(full.replace(model=C.ModelConfig(n_layers=1)))
+    x_in = gen.normal((7, full.model.hidden), full.seed, 4242)
+    _layer_case_with_inputs(one, stored, np.ascontiguousarray(x_in), inp, with_mlp=True)
+
+
+def _golden(k):
+    path = os.path.join(GOLDEN, f"pass_cfg{k}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    return np.load(path)
+
+
+@pytest.mark.parametrize("k", [3, 4, 5])
+def test_full_pass_vs_oracle_golden(k):
+    from tests.gpu_common import GpuWorkload
+    gold = _golden(k)
+    wl = C.PRESETS[k]
+    g = GpuWorkload(wl)
+    g.stored = None
+    n, B, V = wl.n_seq, wl.model.block, wl.model.vocab
+    gt = gold["tokens"]
+    out = g.draft(forced=gt)                      # oracle's tokens as predecessors
+    hid = out["hidden"].reshape(-1)[gold["hidden_idx"]]
+    herr = float(np.max(np.abs(hid - gold["hidden_val"])) / gold["hidden_absmax"])
+    print(f"cfg{k}: hidden rel err {herr:.2e}", flush=True)
+    assert herr <= TOL
+    ties = 0
+    for s in range(n):
+        for i in range(B):
+            idx = np.concatenate([gold["top_idx"][s, i], gold["smp_idx"][s, i]])
+            ref = np.concatenate([gold["top_val"][s, i], gold["smp_val"][s, i]])
+            lg = out["logits"][s, i]
+            delta = float(np.max(np.abs(lg[idx].astype(np.float64) - ref)))
+            assert delta <= TOL * gold["logit_absmax"][s, i], (s, i, delta)
+            t = int(out["tokens"][s, i])
+            assert t == int(np.argmax(lg)), "GPU token is not the argmax of its own logits"
+            if t != int(gt[s, i]):
+                pos = np.flatnonzero(gold["top_idx"][s, i] == t)
+                assert pos.size, (s, i, t, "GPU token outside the oracle's top 64")
+                gap = float(gold["top_val"][s, i, 0] - gold["top_val"][s, i, pos[0]])
+                assert gap <= 2 * delta, (s, i, gap, delta)
+                ties += 1
+    np.testing.assert_allclose(out["conf"], gold["conf"], atol=TOL)
+    print(f"cfg{k}: certified near-ties {ties} of {n * B}", flush=True)
+    assert ties <= max(1, n * B // 20)
+    # free running: same tokens up to the first position where a near-tie may flip
+    free = g.draft(want_logits=False, want_hidden=False)
+    agree = 0
+    for s in range(n):
+        for i in range(B):
+            if free["tokens"][s, i] != gt[s, i]:
+                assert ties > 0, (s, i, "free-running token differs without any near-tie")
+                break
+            agree += 1
+    print(f"cfg{k}: free-running agreement {agree} of {n * B}", flush=True)
+    # acceptance against a verifier planted from the oracle's draft
+    from mla_block_drafter_amd import dspark as D
+    planted = gen.planted_verifier(gt, g.inputs.plant_pos, g.inputs.plant_delta, V)
+    acc = torch.empty(n, dtype=torch.int32, device="cuda")
+    D.accept_len(torch.from_numpy(free["tokens"]).cuda(), torch.from_numpy(planted).cuda(), acc)
+    torch.cuda.synchronize()
+    want = O.accept_len(gt, planted)
+    got = acc.cpu().numpy()
+    # where the free-running draft first leaves the oracle's (B if never), the
+    # planted verifier (the oracle's draft, corrupted at plant_pos) stops matching
+    first_diff = np.array([next((i for i in range(B) if free["tokens"][s, i] != gt[s, i]), B)
+                           for s in range(n)])
+    np.testing.assert_array_equal(got, np.minimum(want, first_diff))
+    if ties == 0:
+        np.testing.assert_array_equal(got, want)
