@@ -112,7 +112,8 @@ struct FragDesc {
   int ld;
   int f32;          // fragments: 1 f32 family, 0 bf16 family
   int hilo;         // bf16 family with M <= 8
-  int KB;           // Kp / 32 (bf16 family)
+  int i8;           // int8 hi/lo codes (M <= 8, Q8_0 consumers): gstride in bytes
+  int KB;           // Kp / 32 (bf16 family, int8)
   int KG;           // Kp / 16 (f32 family)
   int MT;           // m-tiles of 16 rows
   long long gstride;  // elements per group
@@ -141,6 +142,38 @@ __device__ __forceinline__ void frag_put(const FragDesc& fd, int g, int m, int k
   } else {
     const int mt = m >> 4, lane = q * 16 + (m & 15);
     p[((long long)(mt * fd.KB + kb) * 64 + lane) * 8 + i] = (uint16_t)hb;
+  }
+}
+
+// int8 activation fragments (the A operand of v_mfma_i32_16x16x32_i8 for
+// M <= 8 rows): per group, codes [KB][64 lanes][8 bytes] then exponents
+// [KB][8 rows] (int8).  Row m of 32-block kb is v ~ (hi + lo / 256) * 2^e with
+// hi, lo in [-127, 127] and e the smallest exponent with max |v| <= 127 * 2^e
+// over the block; lane q * 16 + m holds the hi codes of k = 8 q .. 8 q + 7,
+// lane q * 16 + 8 + m the lo codes.  bm = max |v| over the block.
+__device__ __forceinline__ void frag_put_i8(const FragDesc& fd, int g, int m, int k, float v, float bm) {
+  int e = 0;
+  if (bm > 0.f) frexpf(bm * (1.f / 127.f), &e);
+  const float qh = fminf(fmaxf(rintf(ldexpf(v, -e)), -127.f), 127.f);
+  const float ql = fminf(fmaxf(rintf(ldexpf(v - ldexpf(qh, e), 8 - e)), -127.f), 127.f);
+  const int kb = k >> 5, q = (k >> 3) & 3, i = k & 7;
+  unsigned char* p = (unsigned char*)fd.ptr + (long long)g * fd.gstride;
+  p[((long long)kb * 64 + q * 16 + m) * 8 + i] = (unsigned char)(int)qh;
+  p[((long long)kb * 64 + q * 16 + 8 + m) * 8 + i] = (unsigned char)(int)ql;
+  if ((k & 31) == 0) p[(long long)fd.KB * 512 + kb * 8 + m] = (unsigned char)(signed char)e;
+}
+
+// Wave-cooperative write: every lane of the wave calls it, lane L holding
+// column k0 + L of row m with k0 a multiple of 64 (so each half wave covers
+// one 32-block); `valid` masks columns outside the matrix.
+__device__ __forceinline__ void frag_put_wave(const FragDesc& fd, int g, int m, int k, float v, bool valid) {
+  if (fd.i8) {
+    float bm = valid ? fabsf(v) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
+    if (valid) frag_put_i8(fd, g, m, k, v, bm);
+  } else if (valid) {
+    frag_put(fd, g, m, k, v);
   }
 }
 

@@ -302,6 +302,13 @@ struct Frag {
 // in LDS (plan.amode != 0), else prepared fragments.
 void frag_geom(Frag& f, const PackedMat& w, int M, const GemvPlan& p) {
   f.fd = FragDesc{};
+  if (p.amode == 3) {  // int8 codes [KB][64][8 B] + exponents [KB][8]
+    f.fd.i8 = 1;
+    f.fd.KB = w.KB;
+    f.fd.gstride = (long long)w.KB * (512 + 8);
+    f.bytes = f.fd.gstride * w.ngroups;
+    return;
+  }
   if (p.amode != 0) {
     f.fd.rows = 1;
     f.fd.ld = w.K;
@@ -347,22 +354,26 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   const Layer& L0 = m.L[0];
   P.x = take((long long)M * c.hidden * 4);
   long long part = 0;
-  auto gp = [&](GemvPlan& gpn, const Mat& mt, bool split) {
-    gpn = plan_gemv(mt.pm, M, split);
+  // i8: whether the producing kernel of the GEMM's input can write int8
+  // fragments (column-per-lane producers always can; the W_UV epilogue can
+  // when its 32-column blocks are pairs of its own 16-row tiles)
+  auto gp = [&](GemvPlan& gpn, const Mat& mt, bool split, bool i8) {
+    gpn = plan_gemv(mt.pm, M, split, false, i8);
     if (split) part = std::max(part, (long long)gpn.S * M * mt.pm.ngroups * mt.pm.G * 4);
   };
-  gp(P.p_qkva, L0.qkva, true);
-  gp(P.p_qb, L0.qb, true);
-  gp(P.p_uk, L0.uk, false);   // epilogue writes the query buffer
-  gp(P.p_uv, L0.uv, false);   // epilogue writes the o_proj fragments
-  gp(P.p_o, L0.o, true);
+  gp(P.p_qkva, L0.qkva, true, true);
+  gp(P.p_qb, L0.qb, true, true);
+  gp(P.p_uk, L0.uk, false, false);  // epilogue writes the query buffer
+  gp(P.p_uv, L0.uv, false, false);  // epilogue writes the o_proj fragments
+  const bool uv_i8 = P.p_uv.MT == 1 && P.p_uv.TPW % 2 == 0 && L0.uv.pm.TG % 2 == 0 && L0.uv.pm.G % 32 == 0;
+  gp(P.p_o, L0.o, true, uv_i8);
   if (m.has_mlp) {
-    gp(P.p_gu, L0.gu, true);
-    gp(P.p_down, L0.down, true);
+    gp(P.p_gu, L0.gu, true, true);
+    gp(P.p_down, L0.down, true, true);
   }
   if (!m.layers_only) {
-    gp(P.p_fc, m.fc, true);
-    P.p_lm = plan_gemv(m.lm.pm, M, false);
+    gp(P.p_fc, m.fc, true, true);
+    P.p_lm = plan_gemv(m.lm.pm, M, false, false, true);
     P.p_w2 = plan_gemv(m.w2.pm, n_seq, false, true);
   }
   frag_geom(P.f_qkva, L0.qkva.pm, M, P.p_qkva);

@@ -63,7 +63,46 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
                                               int t0, int lane, int wave) {
   const int TG = a.w.TG, G = a.w.G;
   const int g = active ? t0 / TG : 0;
-  if (MODE != GEMV_MARKOV) {
+  if (MODE == GEMV_FRAG && MT == 1 && TPW % 2 == 0 && a.fd.i8) {
+    // int8 fragments of the next GEMM: tiles (t, t + 1), t even, are one
+    // 32-column block, whose per-row maximum is taken over lanes 0..15 of
+    // each 16-lane group (one row per group and r after the hi/lo sum).
+    f32x4 v[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      v[j] = acc[0][j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[j][r] += __shfl_xor(v[j][r], 32, 64);
+    }
+#pragma unroll
+    for (int jp = 0; jp < TPW; jp += 2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = (lane >> 4) * 4 + r;
+        const float rsm = (active && a.rs.ssq && m < a.M && lane < 32) ? gemv_row_scale(a.rs, m) : 1.f;
+        float x[2];
+        bool ok[2];
+        long long col[2];
+        float bm = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = t0 + jp + h;
+          const int cig = (t % TG) * 16 + (lane & 15);
+          ok[h] = active && cig < G && lane < 32 && m < a.M;
+          col[h] = (long long)g * G + cig;
+          float fs = 1.f;
+          if (a.w.fmt == DT_FP8 && ok[h]) fs = ((const float*)a.w.scales)[(long long)t * 16 + (lane & 15)];
+          x[h] = v[jp + h][r] * rsm * fs;
+          if (ok[h]) bm = fmaxf(bm, fabsf(x[h]));
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (ok[h]) frag_put_i8(a.fd, 0, m, (int)col[h], x[h], bm);
+      }
+    }
+  } else if (MODE != GEMV_MARKOV) {
     float* out = a.out + (long long)blockIdx.y * a.out_split_stride;
     float rsv[MT][4];
 #pragma unroll
@@ -154,7 +193,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2 };
+enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2, A_GLOBAL_I8 = 3 };
 
 // Eight fp32 activations of row `row` from column k0 (zero outside M x K).
 __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, int row, int k0, float (&v)[8]) {
@@ -180,11 +219,16 @@ __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, 
 //  A_GLOBAL:  prepared bf16 fragments read from global memory (L2 resident);
 //  A_ROWS_BF: the workgroup converts its k range of the fp32 activation rows
 //             into bf16 fragments in LDS (hi/lo split when M <= 8);
-//  A_ROWS_I8: Q8_0 with M <= 8: the rows are quantised per (row, 32-block) to
-//             an int8 hi code and an int8 residual code (scale s and s/256),
-//             and the int8 weight codes feed v_mfma_i32_16x16x32_i8 directly:
-//             no weight decode, exact integer products, one fp32 fma per
-//             output per block with the factor d_w * s_a.
+//  A_GLOBAL_I8: Q8_0 with M <= 8: int8 hi/lo activation codes with one
+//             power-of-two scale per (row, 32-block), written by the producing
+//             kernel (frag_put_i8) and read from global memory with the weight
+//             stream; v_mfma_i32_16x16x32_i8 on the raw weight codes;
+//  A_ROWS_I8: Q8_0 with M <= 8: each row's slice (the workgroup's k range)
+//             is quantised with one scale s to an int8 hi code and an int8
+//             residual code (scale s / 256), and the int8 weight codes feed
+//             v_mfma_i32_16x16x32_i8 directly: no weight decode, exact
+//             integer products, one convert and one fp32 fma per output per
+//             block (factor d_w); s is applied once at the end.
 // Weight loads are issued in stages of U k steps x TPW tiles before any of
 // them is consumed.
 template <int FMT, int MT, int TPW, int MODE, int AMODE>
@@ -198,12 +242,13 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
   const int kb0 = blockIdx.y * a.ksteps_per_split;
   const int kb1 = min(KB, kb0 + a.ksteps_per_split);
   const int nkb = kb1 - kb0;
-  const int g = AMODE != A_GLOBAL ? min(blockIdx.x * 4 * TPW, T - 1) / a.w.TG : (active ? t0 / a.w.TG : 0);
+  const int g = (AMODE == A_ROWS_BF || AMODE == A_ROWS_I8) ? min(blockIdx.x * 4 * TPW, T - 1) / a.w.TG
+                                                             : (active ? t0 / a.w.TG : 0);
 
   // ---------------------------------------------------------- prologue --
   bf16x8* alds = (bf16x8*)gemv_smem;            // A_ROWS_BF: [MT][nkb][64]
   long* icode = (long*)gemv_smem;               // A_ROWS_I8: [nkb][64]
-  float* iscale = (float*)(gemv_smem + (size_t)nkb * 512);  // [nkb][8]
+  float* iscale = (float*)(gemv_smem + (size_t)nkb * 512);  // [8] row maxima, then [4][8] partials
   const float* rows = (const float*)a.act + (long long)g * a.act_gstride;
   // Activation staging (all threads, ends with a barrier).  Weight loads do
   // not depend on it, so each wave issues its first weight stage before.
@@ -231,18 +276,34 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
       }
       __syncthreads();
     } else if (AMODE == A_ROWS_I8) {
+      // One scale per (row, this workgroup's k range): pass 1 finds each
+      // row's largest magnitude, pass 2 writes the codes.  A thread's items
+      // all belong to row (tid >> 2) & 7.
+      float* wpart = iscale + 8;  // [4 waves][8 rows]
+      float mx = 0.f;
       for (int it = threadIdx.x; it < nkb * 32; it += 256) {
         const int q = it & 3, row = (it >> 2) & 7, kbl = it >> 5;
-        const int k0 = 32 * (kb0 + kbl) + 8 * q;
         float v[8];
-        load_row8(a, rows, row, k0, v);
-        float mx = 0.f;
+        load_row8(a, rows, row, 32 * (kb0 + kbl) + 8 * q, v);
   #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
-        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-        const float sc = mx * (1.f / 127.f);
-        const float inv = mx > 0.f ? 127.f / mx : 0.f;
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if ((lane & 0x23) == 0) wpart[wave * 8 + ((lane >> 2) & 7)] = mx;
+      __syncthreads();
+      if (threadIdx.x < 8)
+        iscale[threadIdx.x] = fmaxf(fmaxf(wpart[threadIdx.x], wpart[8 + threadIdx.x]),
+                                    fmaxf(wpart[16 + threadIdx.x], wpart[24 + threadIdx.x]));
+      __syncthreads();
+      const float rmx = iscale[(threadIdx.x >> 2) & 7];
+      const float sc = rmx * (1.f / 127.f);
+      const float inv = rmx > 0.f ? 127.f / rmx : 0.f;
+      for (int it = threadIdx.x; it < nkb * 32; it += 256) {
+        const int q = it & 3, row = (it >> 2) & 7, kbl = it >> 5;
+        float v[8];
+        load_row8(a, rows, row, 32 * (kb0 + kbl) + 8 * q, v);
         uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
   #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -253,7 +314,6 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
         }
         icode[kbl * 64 + q * 16 + row] = (long)(((unsigned long long)hw[1] << 32) | hw[0]);
         icode[kbl * 64 + q * 16 + 8 + row] = (long)(((unsigned long long)lw[1] << 32) | lw[0]);
-        if (q == 0) iscale[kbl * 8 + row] = sc;
       }
       __syncthreads();
     }
@@ -285,7 +345,73 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
 
     // Weight stream, software pipelined: the loads of stage s+1 are issued
     // before stage s is consumed, so a wave always has loads in flight.
-    if (FMT == DT_BF16) {
+    if constexpr (FMT == DT_Q8_0 && AMODE == A_GLOBAL_I8) {
+      // int8 activation fragments from global memory (L2 resident), loaded
+      // with the weights of the same stage; no LDS, no barrier.
+      constexpr int U = 8 / TPW;  // pairs of k blocks per stage
+      const int KP = KB >> 1;
+      const u32x4* wp = (const u32x4*)a.w.codes + (long long)t0 * KP * 64 + lane;
+      const uint32_t* sp = (const uint32_t*)a.w.scales + (long long)t0 * KP * 16 + (lane & 15);
+      const unsigned char* abase = (const unsigned char*)a.act + (long long)g * a.act_gstride;
+      const long* acode = (const long*)abase + lane;                                      // [KB][64]
+      const uint32_t* aexp = (const uint32_t*)(abase + (long long)KB * 512) + ((lane >> 4) & 1);  // [KB][2]
+      struct Stage {
+        u32x4 w[U][TPW];
+        uint32_t s[U][TPW];
+        long c[U][2];
+        uint32_t e[U][2];
+      };
+      auto load_stage = [&](Stage& st, int kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (kb + 2 * u >= kb1) break;
+          const int p = (kb >> 1) + u;
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            st.w[u][j] = ntload(wp + ((long long)j * KP + p) * 64);
+            st.s[u][j] = sp[((long long)j * KP + p) * 16];
+          }
+          st.c[u][0] = acode[(long long)(2 * p) * 64];
+          st.c[u][1] = acode[(long long)(2 * p + 1) * 64];
+          st.e[u][0] = aexp[(2 * p) * 2];
+          st.e[u][1] = aexp[(2 * p + 1) * 2];
+        }
+      };
+      auto compute_stage = [&](const Stage& st, int kb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (kb + 2 * u >= kb1) break;
+          int e0[4], e1[4];  // activation exponents of this lane's 4 rows
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e0[r] = (int)(signed char)(st.e[u][0] >> (8 * r));
+            e1[r] = (int)(signed char)(st.e[u][1] >> (8 * r));
+          }
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            const long B0 = (long)(((unsigned long long)st.w[u][j][1] << 32) | st.w[u][j][0]);
+            const long B1 = (long)(((unsigned long long)st.w[u][j][3] << 32) | st.w[u][j][2]);
+            const float d0 = fp16_bits_to_f32(st.s[u][j] & 0xFFFFu);
+            const float d1 = fp16_bits_to_f32(st.s[u][j] >> 16);
+            const i32x4 z = {0, 0, 0, 0};
+            const i32x4 p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(st.c[u][0], B0, z, 0, 0, 0);
+            const i32x4 p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(st.c[u][1], B1, z, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[0][j][r] += ldexpf(d0, e0[r]) * (float)p0[r] + ldexpf(d1, e1[r]) * (float)p1[r];
+          }
+        }
+      };
+      Stage sa, sb;
+      load_stage(sa, kb0);
+      for (int kb = kb0; kb < kb1; kb += 4 * U) {
+        if (kb + 2 * U < kb1) load_stage(sb, kb + 2 * U);
+        compute_stage(sa, kb);
+        if (kb + 2 * U >= kb1) break;
+        if (kb + 4 * U < kb1) load_stage(sa, kb + 4 * U);
+        compute_stage(sb, kb + 2 * U);
+      }
+    } else if (FMT == DT_BF16) {
       constexpr int U = (MT == 1 ? 8 : 4) / TPW;  // k blocks per stage
       const u32x4* wp = (const u32x4*)a.w.codes + (long long)t0 * KB * 64 + lane;
       auto load_stage = [&](u32x4 (&wr)[U][TPW], int kb) {
@@ -331,7 +457,6 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
       const int KP = KB >> 1;
       const u32x4* wp = (const u32x4*)a.w.codes + (long long)t0 * KP * 64 + lane;
       const uint32_t* sp = (const uint32_t*)a.w.scales + (long long)t0 * KP * 16 + (lane & 15);
-      const float lofac = lane >= 32 ? (1.f / 256.f) : 1.f;  // A_ROWS_I8: rows 8..15 are residual codes
       auto load_stage = [&](u32x4 (&wr)[U][TPW], uint32_t (&sc)[U][TPW], int kb) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -352,8 +477,6 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
           if (AMODE == A_ROWS_I8) {
             const int kl = k2 - kb0;
             const long A0 = icode[kl * 64 + lane], A1 = icode[(kl + 1) * 64 + lane];
-            const f32x4 s0 = *(const f32x4*)(iscale + kl * 8 + ((lane >> 4) & 1) * 4) * lofac;
-            const f32x4 s1 = *(const f32x4*)(iscale + (kl + 1) * 8 + ((lane >> 4) & 1) * 4) * lofac;
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
               const long B0 = (long)(((unsigned long long)wr[u][j][1] << 32) | wr[u][j][0]);
@@ -364,8 +487,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
               const i32x4 p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A0, B0, z, 0, 0, 0);
               const i32x4 p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(A1, B1, z, 0, 0, 0);
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                acc[0][j][r] += (float)p0[r] * (d0 * s0[r]) + (float)p1[r] * (d1 * s1[r]);
+              for (int r = 0; r < 4; ++r) acc[0][j][r] += d0 * (float)p0[r] + d1 * (float)p1[r];
             }
             continue;
           }
@@ -416,6 +538,20 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
     }
   }
   if (!staged) stage_activations();  // inactive waves still join the barrier
+  if (AMODE == A_GLOBAL_I8 && lane >= 32) {
+    // rows 8..15 carry the residual codes (scale 2^e / 256)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) acc[0][j] *= (1.f / 256.f);
+  }
+  if (AMODE == A_ROWS_I8) {
+    // code units -> values: row scale max/127, residual rows (lanes 32..63) / 256
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float f = iscale[((lane >> 4) & 1) * 4 + r] * (lane >= 32 ? 1.f / (127.f * 256.f) : 1.f / 127.f);
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) acc[0][j][r] *= f;
+    }
+  }
   gemv_epilogue<MT, TPW, MODE>(a, acc, active, t0, lane, wave);
 }
 
@@ -471,7 +607,7 @@ __global__ __launch_bounds__(256) void k_gemv_f32(GemvArgs a) {
 // LDS bytes of the activation staging of one workgroup.
 inline size_t gemv_lds_bytes(const GemvPlan& p) {
   if (p.amode == A_ROWS_BF) return (size_t)p.MT * p.ksteps_per_split * 64 * 16;
-  if (p.amode == A_ROWS_I8) return (size_t)p.ksteps_per_split * (512 + 32);
+  if (p.amode == A_ROWS_I8) return (size_t)p.ksteps_per_split * 512 + 256;
   return 0;
 }
 
@@ -485,6 +621,8 @@ hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
     hipLaunchKernelGGL((k_gemv_bf<FMT, MT, TPW, MODE, A_ROWS_BF>), grid, block, lds, st, a);
   } else if (FMT == DT_Q8_0 && MT == 1 && MODE != GEMV_MARKOV && p.amode == A_ROWS_I8) {
     hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_ROWS_I8>), grid, block, lds, st, a);
+  } else if (FMT == DT_Q8_0 && MT == 1 && MODE != GEMV_MARKOV && p.amode == A_GLOBAL_I8) {
+    hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_GLOBAL_I8>), grid, block, 0, st, a);
   } else if (p.amode == A_GLOBAL) {
     hipLaunchKernelGGL((k_gemv_bf<FMT, MT, TPW, MODE, A_GLOBAL>), grid, block, 0, st, a);
   } else {

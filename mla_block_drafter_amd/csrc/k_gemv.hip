@@ -12,16 +12,19 @@ namespace dspark {
 // split-K fills the round.
 constexpr int kMaxWaves = 2048;
 
-GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather) {
+GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, bool i8_in) {
   GemvPlan p{};
   const bool f32 = w.fmt == DT_F32;
   p.hilo = (!f32 && !gather && M <= 8) ? 1 : 0;
   p.MT = p.hilo ? 1 : (M + 15) / 16;
   const int T = w.ngroups * w.TG;
+  // Several tiles per wave share one activation fragment per k step (and,
+  // with LDS staging, one staged slice per workgroup); split-K then restores
+  // the wave count.
   p.TPW = 1;
   if (p.MT == 1) {
     if (w.TG % 4 == 0 && T / 4 >= 256) p.TPW = 4;
-    else if (w.TG % 2 == 0 && T / 2 >= 256) p.TPW = 2;
+    else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 128 : 256)) p.TPW = 2;
   }
   const int waves = T / p.TPW;
   p.grid_x = (waves + 3) / 4;
@@ -31,14 +34,20 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather) {
   if (allow_split) S = std::max(1, std::min(kMaxWaves / std::max(waves, 1), ksteps / 8));
   int per = (ksteps + S - 1) / S;
   per = (per + unit - 1) / unit * unit;
-  // activation staging in LDS: every tile of a workgroup in one group, <= 64 KiB
+  // activation staging in LDS (every tile of a workgroup in one group):
+  // bf16 fragments 1 KiB per k step and 16-row tile, int8 codes 512 B per
+  // k step; at most 64 KiB per workgroup (two workgroups per CU)
   const bool one_group = w.ngroups == 1 || w.TG % (4 * p.TPW) == 0;
+  const bool i8 = w.fmt == DT_Q8_0 && p.hilo;
+  const int cap = i8 ? 126 : 64;
   p.amode = 0;
-  if (!f32 && !gather && one_group) {
+  if (i8 && i8_in && !gather) {
+    p.amode = 3;  // int8 fragments written by the producer: no staging
+  } else if (!f32 && !gather && one_group) {
     if (allow_split) {
-      while ((long long)p.MT * per > 64) per = ((per / 2) + unit - 1) / unit * unit;
+      while ((long long)p.MT * per > cap) per = ((per / 2) + unit - 1) / unit * unit;
     }
-    if ((long long)p.MT * per <= 64) p.amode = (w.fmt == DT_Q8_0 && p.hilo) ? 2 : 1;
+    if ((long long)p.MT * per <= cap) p.amode = i8 ? 2 : 1;
   }
   p.ksteps_per_split = per;
   p.S = (ksteps + per - 1) / per;

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
   const int M = a.n_seq * a.block;
   const int K = a.ncap * a.H;
   const int Kp = fd.rows ? K : fd.f32 ? fd.KG * 16 : fd.KB * 32;
-  const int rows = fd.rows ? M : fd.hilo ? 8 : fd.MT * 16;
+  const int rows = fd.rows ? M : (fd.hilo || fd.i8) ? 8 : fd.MT * 16;
   const long long total = (long long)rows * Kp;
   for (long long e = tid; e < total; e += nthr) {
     const int m = (int)(e / Kp), k = (int)(e % Kp);
@@ -32,7 +32,9 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
       v = a.cap_f32 ? ((const float*)a.captured)[idx]
                     : bf16_bits_to_f32(((const uint16_t*)a.captured)[idx]);
     }
-    frag_put(fd, 0, m, k, v);
+    // int8 fragments: Kp and the thread count are multiples of 64, so every
+    // wave walks whole 64-column runs of one row together
+    frag_put_wave(fd, 0, m, k, v, true);
   }
 }
 

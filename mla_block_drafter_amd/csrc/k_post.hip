@@ -64,9 +64,10 @@ __global__ __launch_bounds__(256) void k_post_resid(ResidPost a) {
   float r = 1.f;
   if (a.mode == RP_NORM) r = shared_row_scale(a.rs_in, m, &rs);
   float sq = 0.f, dt = 0.f;
-  if (c < a.H) {
+  const bool ok = c < a.H;
+  float x = 0.f;
+  if (ok) {
     const long long i = (long long)m * a.H + c;
-    float x;
     switch (a.mode) {
       case RP_SUM: x = part_sum(a.p, m, c); break;
       case RP_ADD: x = a.x_in[i] + part_sum(a.p, m, c); break;
@@ -75,11 +76,11 @@ __global__ __launch_bounds__(256) void k_post_resid(ResidPost a) {
     }
     a.x_out[i] = x;
     sq = x * x;
-    if (a.g1) {
-      const float v = a.g1[c] * x;
-      frag_put(a.fd, 0, m, c, v);
-      if (a.dotw) dt = v * a.dotw[c];
-    }
+  }
+  if (a.g1) {
+    const float v = ok ? a.g1[c] * x : 0.f;
+    frag_put_wave(a.fd, 0, m, c, v, ok);
+    if (a.dotw && ok) dt = v * a.dotw[c];
   }
   if (a.ssq_out) {
     sq = block_sum256(sq, red);
@@ -103,12 +104,13 @@ __global__ __launch_bounds__(256) void k_post_qkva(QkvaPost a) {
   const int ncq = (a.q_lora + 255) / 256;
   if ((int)blockIdx.x < ncq) {
     const int c = blockIdx.x * 256 + threadIdx.x;
-    float sq = 0.f;
-    if (c < a.q_lora) {
-      const float v = r * part_sum(a.p, m, c);
+    const bool ok = c < a.q_lora;
+    float sq = 0.f, v = 0.f;
+    if (ok) {
+      v = r * part_sum(a.p, m, c);
       sq = v * v;
-      frag_put(a.fd_qb, 0, m, c, a.g_qa[c] * v);
     }
+    frag_put_wave(a.fd_qb, 0, m, c, ok ? a.g_qa[c] * v : 0.f, ok);
     sq = block_sum256(sq, red);
     if (threadIdx.x == 0) a.ssq_cq[m * SSQ_LD + blockIdx.x] = sq;
     return;
@@ -176,10 +178,14 @@ __global__ __launch_bounds__(256) void k_post_swiglu(SwigluPost a) {
   const int m = blockIdx.y;
   const float r = shared_row_scale(a.rs, m, &rs);
   const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= a.inter) return;
-  const float g = r * part_sum(a.p, m, c);
-  const float u = r * part_sum(a.p, m, a.inter + c);
-  frag_put(a.fd, 0, m, c, g / (1.f + __expf(-g)) * u);
+  const bool ok = c < a.inter;
+  float h = 0.f;
+  if (ok) {
+    const float g = r * part_sum(a.p, m, c);
+    const float u = r * part_sum(a.p, m, a.inter + c);
+    h = g / (1.f + __expf(-g)) * u;
+  }
+  frag_put_wave(a.fd, 0, m, c, h, ok);
 }
 
 }  // namespace

@@ -56,9 +56,12 @@ struct GemvPlan {
   int amode;              // activation operand: 0 prepared global fragments,
                           // 1 fp32 rows -> bf16 fragments in LDS,
                           // 2 fp32 rows -> int8 hi/lo codes in LDS (Q8_0, M <= 8)
+                          // 3 int8 hi/lo fragments from the producer (Q8_0, M <= 8)
 };
 
-GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather = false);
+// i8_in: the producer of the input can write int8 fragments (frag_put_wave /
+// the int8 FRAG epilogue), which Q8_0 weights with M <= 8 then read directly.
+GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather = false, bool i8_in = false);
 hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 
 // --------------------------------------------------------------- attention --
