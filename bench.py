@@ -36,8 +36,9 @@ def log(*a):
 
 def cpu_baseline(wl, stored, inp):
     """The oracle (float64 numpy) on a bounded sample of the same workload:
-    fc + fc-norm and decoder layer 0 (attention over the full cache + SwiGLU),
-    scaled to a whole pass by algorithmic bytes."""
+    fc + fc-norm and all decoder layers (attention over the full caches +
+    SwiGLU), i.e. everything but lm_head and the Markov rollout, scaled to a
+    whole pass by algorithmic bytes."""
     import numpy as np
     from oracle import dspark as O
     from synth import accounting as A
@@ -47,14 +48,15 @@ def cpu_baseline(wl, stored, inp):
     cap = O._decode_input(inp.captured, wl.formats.captured).reshape(wl.n_seq, m.n_captured, m.block, m.hidden)
     X = cap.transpose(0, 2, 1, 3).reshape(wl.n_seq * m.block, m.n_captured * m.hidden)
     x = O.rmsnorm(X @ W("fc").T, W("fc_norm"), m.rms_eps)
-    caches = [O._decode_input(inp.caches[0], wl.formats.kv_cache)]
-    x = O.layer(m, W, 0, x, caches, inp.kv_offsets)
+    caches = [O._decode_input(c, wl.formats.kv_cache) for c in inp.caches]
+    for layer in range(m.n_layers):
+        x = O.layer(m, W, layer, x, caches, inp.kv_offsets)
     dt = time.perf_counter() - t0
     assert np.isfinite(x).all()
     pb = A.pass_bytes(wl)
-    sample = pb["fc"] + pb["fc_norm"] + pb["captured"] + pb["kv_cache"] // m.n_layers
-    sample += sum(v for k, v in pb.items() if k.startswith("L0."))
     total = sum(pb.values())
+    sample = total - pb["lm_head"] - pb["markov_w1"] - pb["markov_w2"] - pb.get("final_norm", 0) \
+        - pb.get("conf_w", 0) - pb.get("conf_b", 0)
     cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
@@ -63,8 +65,65 @@ def cpu_baseline(wl, stored, inp):
         pass
     return {"value": round(dt * 1e6 * total / sample, 1), "unit": "us/block", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"fc + layer 0 of {wl.name} ({sample / 1e6:.1f} MB of {total / 1e6:.1f} MB "
-                      f"algorithmic bytes) in {dt:.2f} s, float64 numpy, scaled by bytes"}
+            "sample": f"fc + all {m.n_layers} decoder layers of {wl.name} ({sample / 1e6:.1f} MB of "
+                      f"{total / 1e6:.1f} MB algorithmic bytes) in {dt:.2f} s, float64 numpy, scaled by bytes"}
+
+
+KERNEL_SOURCES = ["common.h", "kernels.h", "gemv_impl.h", "k_gemv.hip", "k_gemv_bf16.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_gemv_bf16_q8_0_ctx8192_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources the lm_head GEMM kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mla_block_drafter_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per lm_head launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split("=", 1) for line in f.read().splitlines() if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_hash", "").strip() != kernel_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def copy_calibration():
+    """A plain device copy of known size (for scaling rocprofv3 byte counters)."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def copy_probe_gbs(torch) -> float:
+    """Device copy bandwidth (read + write bytes / time) of a 1 GiB copy."""
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def main():
@@ -75,7 +134,12 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (byte-counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the draft pass is not "
               "sharded across GPUs in this build.", file=sys.stderr)
@@ -120,6 +184,7 @@ def main():
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * D.N_STAGES)] for _ in range(K)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     for row in evs:
         for e in row:
             e.record()
@@ -127,10 +192,13 @@ def main():
     torch.cuda.synchronize()
     t_begin.record()
     for k in range(K):
+        step_ev[k].record()
         run(evs[k])
+    step_ev[K].record()
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_begin.elapsed_time(t_end) / K
+    per_step = np.array([step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(K)])
     stage_ms = np.array([[evs[k][2 * s].elapsed_time(evs[k][2 * s + 1]) for s in range(D.N_STAGES)]
                          for k in range(K)]).mean(axis=0)
     log("[bench] eager: %.1f us/pass; stages (us): %s" % (
@@ -161,6 +229,8 @@ def main():
         except Exception as e:  # graph capture is an extra, never the headline
             log(f"[bench] graph capture skipped: {e!r}")
 
+    copy_gbs = copy_probe_gbs(torch)
+    log(f"[bench] device copy probe: {copy_gbs:.0f} GB/s")
     total_bytes = A.total_bytes(wl)
     blocks = n
     lm_bytes = A.lm_head_launch_bytes(wl)
@@ -191,11 +261,14 @@ def main():
                    "algorithmic_bytes": total_bytes},
         "hbm_gbs": round(pass_gbs, 1),
         "hbm_frac_of_peak": round(pass_gbs / HBM_PEAK_GBS, 4),
+        "hbm_frac_of_copy_probe": round(pass_gbs / copy_gbs, 4),
+        "copy_probe_gbs": round(copy_gbs, 1),
+        "step_us_median_p10_p90": [round(float(np.percentile(per_step, q)) * 1e3, 2) for q in (50, 10, 90)],
         "graph_us_per_block": None if graph_ms is None else round(graph_ms * 1e3 / blocks, 2),
         "stage_us": {nm: round(v * 1e3, 2) for nm, v in zip(D.STAGES, stage_ms)},
         "roofline": {"bound": "hbm", "kernel": "lm_head GEMM (k_gemv_bf, BF16 weights)",
                      "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }
