@@ -32,6 +32,8 @@
 //   * bf16 family, plain (M > 8): per group [MT][KB][64][8], row 16mt + (l & 15).
 //   * f32 family: per group [MT][Kp/16][64][4] fp32, row 16mt + (l & 15),
 //     columns 16g + 4(l >> 4) .. +3.
+//   * int8 hi/lo (Q8_0 consumers, M <= 8): per group [KB][64 lanes][8] int8
+//     codes then [KB][8 rows] int8 exponents (see frag_put_i8).
 #pragma once
 
 #include <hip/hip_runtime.h>
