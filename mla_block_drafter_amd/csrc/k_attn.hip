@@ -10,7 +10,7 @@
 //
 // bf16 path (split-K, flash-decoding style): a workgroup of 4 waves owns 64
 // query rows and one slot of C keys.  Key tiles of 32 rows are staged in LDS
-// row-major, double-buffered.  S^T = K Q^T takes the key rows as the A operand (16-byte LDS
+// row-major, four buffers deep.  S^T = K Q^T takes the key rows as the A operand (16-byte LDS
 // reads), so the probabilities land with one query row per lane column,
 // which is already the B-operand layout of P^T for O^T = V^T P^T: the
 // probabilities never leave registers (the 32 keys' order inside the MFMA
@@ -28,6 +28,7 @@ namespace dspark {
 namespace {
 
 constexpr int KT = 32;  // keys per LDS tile
+constexpr int NBUF = 4;  // key tile buffers: three tiles in flight while one computes
 constexpr float RESCALE_SLACK = 8.f;  // natural-log units
 constexpr int MAX_COMBINE_SLOTS = 4096;
 
@@ -58,7 +59,7 @@ __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s,
 //      key r holding source chunk p ^ (r % CB).
 // Loads that fall past the slot read a valid dummy row (the sequence's first
 // block key); their scores are masked and their probabilities are zero.
-// Two tile buffers: tile t+1 streams in while tile t computes.
+// NBUF tile buffers: tiles t+1 .. t+NBUF-1 stream in while tile t computes.
 //
 // Inside each 16-key half of a tile, MFMA row m holds key pi(m) =
 // (g & 1) + 8 (g >> 1) + 2 j for m = 4 g + j.  The score fragment of lane
@@ -167,7 +168,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   constexpr int CA = R / 8, CB = (DQ - R) / 8;
   using G = TileGeom<CA, CB>;
   static_assert(CA % 4 == 0, "each k-step reads one region");
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * G::BUF];
+  static_assert(NBUF <= 4 && 3 * G::NMIN <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF * G::BUF];
 
   int s, p, len, off, J;
   slot_lookup(a, blockIdx.y, s, p, len, off, J);
@@ -185,7 +187,12 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   const uint16_t* cache = (const uint16_t*)a.cache;
   const uint16_t* bk = (const uint16_t*)a.bkeys;
   const uint16_t* dummy = bk + (long long)s * a.block * a.latent;
-  issue_tile<CA, CB>(a, lane, wave, k_begin, k_end, s, len, off, cache, bk, dummy, k_lds);
+  // prologue: tiles 0 .. NBUF - 2 in flight
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < ntiles)
+      issue_tile<CA, CB>(a, lane, wave, k_begin + i * KT, k_end, s, len, off, cache, bk, dummy,
+                         k_lds + i * G::BUF);
 
   // Q fragments (B operand of S^T = K Q^T): row myrow, dims 32kb + 8 grp.
   bf16x8 qf[NKB];
@@ -215,14 +222,17 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 
   for (int t = 0; t < ntiles; ++t) {
     const int kt0 = k_begin + t * KT;
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      issue_tile<CA, CB>(a, lane, wave, kt0 + KT, k_end, s, len, off, cache, bk, dummy,
-                         k_lds + (buf ^ 1) * G::BUF);
-      wait_vmcnt<G::NMIN>();  // all but this wave's newest loads are done: tile t is in LDS
-    } else {
-      wait_vmcnt<0>();
-    }
+    const int buf = t % NBUF;
+    if (t + NBUF - 1 < ntiles)  // refill the buffer every wave finished reading last iteration
+      issue_tile<CA, CB>(a, lane, wave, kt0 + (NBUF - 1) * KT, k_end, s, len, off, cache, bk, dummy,
+                         k_lds + ((t + NBUF - 1) % NBUF) * G::BUF);
+    // tile t is in LDS once at most the loads of the tiles issued after it
+    // (at least NMIN per tile for every wave) are outstanding
+    const int after = min(NBUF - 1, ntiles - 1 - t);
+    if (after >= 3) wait_vmcnt<3 * G::NMIN>();
+    else if (after == 2) wait_vmcnt<2 * G::NMIN>();
+    else if (after == 1) wait_vmcnt<G::NMIN>();
+    else wait_vmcnt<0>();
     // the barrier intrinsic has no memory semantics of its own, so the
     // compiler fences keep LDS accesses on their side of it (a __syncthreads
     // would also drain the prefetch of the next tile)

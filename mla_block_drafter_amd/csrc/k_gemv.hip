@@ -6,10 +6,10 @@
 
 namespace dspark {
 
-// One launch = one round of resident waves: at most kMaxWaves (8 per CU at
-// the GEMM kernels' occupancy), so no nearly empty second round doubles the
-// time.  Tiles per wave (TPW) shrink when the matrix has few tiles, then
-// split-K fills the round.
+// Split-K fills one round of resident waves: at most kMaxWaves (eight per CU
+// at the GEMM kernels' occupancy), so no nearly empty second round doubles
+// the time.  In the pass this beat a lower target that cold-cache
+// microbenchmarks of single launches preferred.
 constexpr int kMaxWaves = 2048;
 
 GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, bool i8_in) {
@@ -21,9 +21,12 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   // Several tiles per wave share one activation fragment per k step (and,
   // with LDS staging, one staged slice per workgroup); split-K then restores
   // the wave count.
+  // Two tiles per wave streamed best for the M = 7 shapes (the unsplit
+  // 163,840-row lm_head included); the Markov gather GEMM, whose k range is
+  // only 256, keeps four; one when the matrix has too few tiles.
   p.TPW = 1;
   if (p.MT == 1) {
-    if (w.TG % 4 == 0 && T / 4 >= 256) p.TPW = 4;
+    if (gather && w.TG % 4 == 0 && T / 4 >= 256) p.TPW = 4;
     else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 128 : 256)) p.TPW = 2;
   }
   const int waves = T / p.TPW;
@@ -31,7 +34,8 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   const int ksteps = f32 ? (w.Kp >> 4) : w.KB;
   const int unit = (w.fmt == DT_Q8_0 || w.fmt == DT_FP8) ? 2 : 1;
   int S = 1;
-  if (allow_split) S = std::max(1, std::min(kMaxWaves / std::max(waves, 1), ksteps / 8));
+  if (allow_split)
+    S = std::max(1, std::min(kMaxWaves / std::max(waves, 1), ksteps / 8));
   int per = (ksteps + S - 1) / S;
   per = (per + unit - 1) / unit * unit;
   // activation staging in LDS (every tile of a workgroup in one group):
@@ -40,10 +44,13 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   const bool one_group = w.ngroups == 1 || w.TG % (4 * p.TPW) == 0;
   const bool i8 = w.fmt == DT_Q8_0 && p.hilo;
   const int cap = i8 ? 126 : 64;
+  // Producers write the consumer's fragments directly (no staging in the
+  // GEMM): bf16 hi/lo fragments for BF16 / FP8 weights, int8 hi/lo codes for
+  // Q8_0 when the producer supports them; otherwise Q8_0 stages fp32 rows.
   p.amode = 0;
   if (i8 && i8_in && !gather) {
-    p.amode = 3;  // int8 fragments written by the producer: no staging
-  } else if (!f32 && !gather && one_group) {
+    p.amode = 3;
+  } else if (w.fmt == DT_Q8_0 && !gather && one_group) {
     if (allow_split) {
       while ((long long)p.MT * per > cap) per = ((per / 2) + unit - 1) / unit * unit;
     }
