@@ -29,7 +29,7 @@ namespace {
 
 constexpr int KT = 32;  // keys per LDS tile
 constexpr int NBUF = 4;  // key tile buffers: three tiles in flight while one computes
-constexpr float RESCALE_SLACK = 8.f;  // natural-log units
+constexpr float REDO_SLACK = 60.f;  // natural-log units: e^60 * 256 keys stays far below fp32 max
 constexpr int MAX_COMBINE_SLOTS = 4096;
 
 __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s, int& p, int& len,
@@ -58,7 +58,9 @@ __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s,
 //   B: the rope part (CB chunks per key), 64 / CB keys per load, chunk p of
 //      key r holding source chunk p ^ (r % CB).
 // Loads that fall past the slot read a valid dummy row (the sequence's first
-// block key); their scores are masked and their probabilities are zero.
+// block key); their scores are masked and their probabilities are zero.  So do
+// the rope-region chunks past the stored row when the query width is padded
+// beyond the latent (their query dims are zero).
 // NBUF tile buffers: tiles t+1 .. t+NBUF-1 stream in while tile t computes.
 //
 // Inside each 16-key half of a tile, MFMA row m holds key pi(m) =
@@ -89,6 +91,21 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, int lane, int wave
                                            const uint16_t* dummy, uint16_t* dst) {
   using G = TileGeom<CA, CB>;
   static_assert(G::NB_A % 4 == 0 && G::NB_B <= 4, "load split over four waves");
+  if (kt0 + KT <= min(len, k_end)) {
+    // common case: the whole tile is valid cache rows (uniform row pointer)
+    const long long ld = a.latent;
+    const uint16_t* src = cache + (off + kt0 + wave) * ld + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < G::NB_A / 4; ++i, src += 4 * ld)
+      if (CA == 64 || lane < CA) __builtin_amdgcn_global_load_lds(src, dst + (wave + 4 * i) * G::ROW_A, 16, 0, 0);
+    if (wave < G::NB_B) {
+      const int r = wave * G::KPB + lane / CB, c = CA + ((lane % CB) ^ (r % CB));
+      // chunks past the stored row (query padding, zero) read the dummy row
+      const uint16_t* sb = 8 * c < a.latent ? cache + (off + kt0 + r) * ld + 8 * c : dummy;
+      __builtin_amdgcn_global_load_lds(sb, dst + G::SIZE_A + wave * 512, 16, 0, 0);
+    }
+    return;
+  }
   auto row_ptr = [&](int j) {
     const uint16_t* c = cache + (long long)(off + j) * a.latent;
     const uint16_t* k = bk + (long long)(s * a.block + (j - len)) * a.latent;
@@ -102,8 +119,9 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, int lane, int wave
     if (CA == 64 || lane < CA) __builtin_amdgcn_global_load_lds(src, dst + b * G::ROW_A, 16, 0, 0);
   }
   if (wave < G::NB_B) {
-    const int r = wave * G::KPB + lane / CB, p = lane % CB;
-    const uint16_t* src = row_ptr(kt0 + r) + 8 * (CA + (p ^ (r % CB)));
+    const int r = wave * G::KPB + lane / CB, c = CA + ((lane % CB) ^ (r % CB));
+    // chunks past the stored row (query padding, zero) read the dummy row
+    const uint16_t* src = 8 * c < a.latent ? row_ptr(kt0 + r) + 8 * c : dummy;
     __builtin_amdgcn_global_load_lds(src, dst + G::SIZE_A + wave * 512, 16, 0, 0);
   }
 }
@@ -187,12 +205,6 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   const uint16_t* cache = (const uint16_t*)a.cache;
   const uint16_t* bk = (const uint16_t*)a.bkeys;
   const uint16_t* dummy = bk + (long long)s * a.block * a.latent;
-  // prologue: tiles 0 .. NBUF - 2 in flight
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (i < ntiles)
-      issue_tile<CA, CB>(a, lane, wave, k_begin + i * KT, k_end, s, len, off, cache, bk, dummy,
-                         k_lds + i * G::BUF);
 
   // Q fragments (B operand of S^T = K Q^T): row myrow, dims 32kb + 8 grp.
   bf16x8 qf[NKB];
@@ -215,10 +227,25 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) keyS[j] = key_perm(4 * grp + j);
 
+  // Softmax reference: the first tile's row maximum (pass 0).  The tile loop
+  // never rescales the accumulators (they stay in AGPRs untouched by the
+  // VALU); if a later score exceeds the reference by more than REDO_SLACK,
+  // where exp() could approach the fp32 range, the workgroup redoes the slot
+  // once with the exact row maximum as the reference (pass 1).
+  __shared__ int redo_flag;
   f32x4 acc[NDT];
+  float m_run = -INFINITY, l_run = 0.f, m_all = -INFINITY;
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
   for (int d = 0; d < NDT; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  l_run = 0.f;
+  if (pass == 1) m_run = m_all;
+  // prologue: tiles 0 .. NBUF - 2 in flight
+#pragma unroll 1
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < ntiles)
+      issue_tile<CA, CB>(a, lane, wave, k_begin + i * KT, k_end, s, len, off, cache, bk, dummy,
+                         k_lds + i * G::BUF);
 
   for (int t = 0; t < ntiles; ++t) {
     const int kt0 = k_begin + t * KT;
@@ -278,18 +305,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // Lazy rescaling: the running reference m_run moves only when a score
-    // exceeds it by more than RESCALE_SLACK, so probabilities stay below
-    // e^RESCALE_SLACK and the accumulators are touched by the VALU only on
-    // the (rare, wave-uniform) rescale step.
-    if (__any(tmax > m_run + RESCALE_SLACK)) {
-      const bool up = tmax > m_run + RESCALE_SLACK;
-      const float corr = up ? __expf(m_run - tmax) : 1.f;
-      if (up) m_run = tmax;
-      l_run *= corr;
-#pragma unroll
-      for (int d = 0; d < NDT; ++d) acc[d] *= corr;
-    }
+    m_all = fmaxf(m_all, tmax);
+    if (pass == 0 && t == 0) m_run = tmax;  // finite: tile 0 holds a valid key
     float psum = 0.f;
     u32x4 pw;
 #pragma unroll
@@ -337,6 +354,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+  }
+
+    if (pass == 1) break;
+    // every wave has passed the loop's last barrier; decide the redo together
+    if (threadIdx.x == 0) redo_flag = 0;
+    __syncthreads();
+    if (__any(m_all > m_run + REDO_SLACK) && lane == 0) atomicOr(&redo_flag, 1);
+    __syncthreads();
+    if (!redo_flag) break;
   }
 
   // ---- partials: O^T[dim = 16d + 4(lane>>4) + r][row = myrow]; layout
