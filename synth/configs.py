@@ -88,6 +88,7 @@ class Workload:
     sharp_attention: bool = False  # kv_b rows for W_UK scaled x10
     markov_dominant: bool = False  # W1, W2 ~ N(0, R^-1/2); lm_head = 0
     weight_std: float = 0.02
+    spike: tuple = ()        # (cache row, factor): that row of every cache scaled (a far-away dominant key)
 
     @property
     def n_seq(self) -> int:

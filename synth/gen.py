@@ -248,6 +248,8 @@ def make_inputs(wl: C.Workload) -> Inputs:
     caches = []
     for l in range(m.n_layers):
         c = normal((total, latent), wl.seed, base + 1 + l)
+        if wl.spike:
+            c[wl.spike[0]] *= np.float32(wl.spike[1])
         caches.append(as_fmt(c, wl.formats.kv_cache))
     rng = np.random.default_rng(np.random.SeedSequence(wl.seed, spawn_key=(base + 500,)))
     prev = rng.integers(0, m.vocab, size=n_seq).astype(np.int32)

@@ -48,6 +48,17 @@ def test_single_full_size_mla_layer_bf16_ctx4096():
     _layer_case_with_inputs(wl, stored, x_in, inp, with_mlp=False)
 
 
+def test_single_full_size_mla_layer_far_dominant_key():
+    """As above with cache row 3000 scaled x200 (it dominates every query row
+    whose score with it is positive): the exact-reference second pass of the
+    attention kernel at full size."""
+    wl = C.CFG2.replace(spike=(3000, 200.0))
+    stored = gen.make_weights(wl)
+    inp = gen.make_inputs(wl)
+    x_in = np.ascontiguousarray(inp.x_in, np.float32)
+    _layer_case_with_inputs(wl, stored, x_in, inp, with_mlp=False)
+
+
 def _layer_case_with_inputs(wl, stored, x_in, inp, with_mlp):
     from mla_block_drafter_amd import dspark as D
     m = wl.model

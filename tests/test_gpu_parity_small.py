@@ -90,6 +90,18 @@ def test_small_sharp_attention_bf16():
     full_parity(g, ref, tol=2e-2, max_ties=2)
 
 
+def test_small_far_dominant_key_bf16():
+    """One cache row scaled x200 far from the first key tile of its slot: its
+    scores exceed the slot's first-tile maximum by far more than 60, so the
+    attention workgroup takes its exact-reference second pass."""
+    from tests.gpu_common import full_parity
+    wl = C.Workload("small_spike", SMALL, C.ALL_BF16, seed=780, kv_lens=(300,), fixture_gains=True,
+                    spike=(200, 200.0))
+    g = _gw(wl)
+    ref = O.draft_block(wl, g.stored, g.inputs)
+    full_parity(g, ref, tol=2e-2, max_ties=2)
+
+
 def test_dequant_bit_exact():
     """Decoding the repacked planes gives exactly the oracle's decoded values
     (Q8_0 d*q and bf16 exact in fp32; FP8 s*e4m3(q) correctly rounded)."""
