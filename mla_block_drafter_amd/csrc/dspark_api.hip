@@ -330,7 +330,8 @@ struct Plan {
   int n_seq = 0, M = 0;
   long long total_ctx = 0;
   bool kv_f32 = false;
-  long long x = 0, part = 0, q = 0, bkeys = 0, opart = 0, mlpart = 0, z = 0, keys = 0, total = 0;
+  long long x = 0, part = 0, q = 0, bkeys = 0, opart = 0, mlpart = 0, z = 0, keys = 0, mslots = 0, merr = 0, total = 0;
+  int mwgs = 0;
   long long ssq_a = 0, ssq_b = 0, ssq_cq = 0, dot = 0;
   long long zero_begin = 0, zero_end = 0;
   Frag f_fc, f_qkva, f_qb, f_uk, f_uv, f_o, f_gu, f_down, f_lm;
@@ -395,6 +396,11 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   for (Frag* f : {&P.f_qkva, &P.f_qb, &P.f_uk, &P.f_uv, &P.f_o, &P.f_gu, &P.f_down, &P.f_lm})
     if (f->bytes) f->off = take(f->bytes);
   P.keys = take((long long)n_seq * c.block * KEY_SLOTS * 8);
+  if (!m.layers_only) {  // Markov rollout argmax slots and error flag
+    P.mwgs = markov_rollout_wgs(m.w2.pm.ngroups * m.w2.pm.TG);
+    P.mslots = take((long long)c.block * n_seq * P.mwgs * 8);
+    P.merr = take(16);
+  }
   P.rows = c.block * c.n_heads;
   P.rows_pad = (int)rup(P.rows, 64);
   P.DQ = (int)rup(c.kv_lora + c.qk_rope, 32);
@@ -820,7 +826,26 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   HIPCHK(run_gemv(m->lm, P.p_lm, P.f_lm, M, z, C.st, C.rs(P.ssq_b, c.hidden)));
   HIPCHK(mark(2 * DSPARK_STAGE_LM_HEAD + 1));
   HIPCHK(mark(2 * DSPARK_STAGE_MARKOV));
-  for (int i = 0; i < c.block; ++i) {
+  const bool rollout = m->w2.pm.fmt == DT_BF16 && markov_rollout_supported(m->w2.pm.KB, in->n_seq);
+  if (rollout) {
+    MarkovArgs a{};
+    a.w2 = m->w2.pm.codes;
+    a.tiles = m->w2.pm.ngroups * m->w2.pm.TG;
+    a.w1 = m->base + m->w1;
+    a.w1_ld = m->w1_ld;
+    a.vocab = c.vocab;
+    a.M = in->n_seq;
+    a.block = c.block;
+    a.prev_token = in->prev_token;
+    a.forced = in->forced_prev;
+    a.z = z;
+    a.logits = out->logits;
+    a.slots = (unsigned long long*)(C.ws + P.mslots);
+    a.max_wgs = P.mwgs;
+    a.err = (unsigned*)(C.ws + P.merr);
+    HIPCHK(launch_markov_rollout(a, m->w2.pm.KB, C.st));
+  }
+  for (int i = 0; !rollout && i < c.block; ++i) {
     GemvArgs a{};
     a.w = m->w2.pm;
     a.act = m->base + m->w1;
@@ -859,6 +884,9 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.n_seq = in->n_seq;
     a.block = c.block;
     a.vocab = c.vocab;
+    a.slots = rollout ? (const unsigned long long*)(C.ws + P.mslots) : nullptr;
+    a.nwg = rollout ? markov_rollout_wgs(m->w2.pm.ngroups * m->w2.pm.TG) : 0;
+    a.rollout_err = rollout ? (const unsigned*)(C.ws + P.merr) : nullptr;
     HIPCHK(launch_markov_final(a, C.st));
   }
   HIPCHK(mark(2 * DSPARK_STAGE_MARKOV + 1));

@@ -43,48 +43,60 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
 // with hf_i = rs_final * g_final * x, and the optional hidden output.
 __global__ __launch_bounds__(256) void k_markov_final(MarkovFinalArgs a) {
   __shared__ float red[4];
-  __shared__ int toks[64];
-  __shared__ float rsv[64];
-  const int s = blockIdx.x;
-  if (threadIdx.x < a.block) {
-    const unsigned long long* k = a.keys + ((long long)s * a.block + threadIdx.x) * KEY_SLOTS;
+  __shared__ unsigned long long kred[4];
+  const int s = blockIdx.x, i = blockIdx.y;  // one workgroup per (sequence, position)
+  const long long m = (long long)s * a.block + i;
+  // argmax key of position pos (all threads take part)
+  auto token_at = [&](int pos) {
     unsigned long long best = 0;
-    for (int i = 0; i < KEY_SLOTS; ++i) best = best > k[i] ? best : k[i];
-    toks[threadIdx.x] = key_index(best);
-    a.tokens[s * a.block + threadIdx.x] = key_index(best);
-    const int m = s * a.block + threadIdx.x;
-    const float* p = a.rs_final.ssq + (long long)m * SSQ_LD;
+    if (a.slots) {
+      const unsigned long long* sl = a.slots + ((long long)pos * a.n_seq + s) * a.nwg;
+      for (int w = threadIdx.x; w < a.nwg; w += 256) best = best > sl[w] ? best : sl[w];
+    } else if (threadIdx.x < KEY_SLOTS) {
+      best = a.keys[((long long)s * a.block + pos) * KEY_SLOTS + threadIdx.x];
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long other = ((unsigned long long)__shfl_xor((unsigned)(best >> 32), o, 64) << 32) |
+                                       (unsigned)__shfl_xor((unsigned)best, o, 64);
+      best = best > other ? best : other;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) kred[threadIdx.x >> 6] = best;
+    __syncthreads();
+    for (int q = 0; q < 4; ++q) best = best > kred[q] ? best : kred[q];
+    return key_index(best);
+  };
+  const bool failed = a.rollout_err && *a.rollout_err;
+  int tp;
+  if (i == 0) tp = a.prev_token[s];
+  else if (a.forced) tp = a.forced[s * a.block + i - 1];
+  else tp = token_at(i - 1);
+  const int ti = token_at(i);
+  float rs;
+  {
+    const float* p = a.rs_final.ssq + m * SSQ_LD;
     float t = 0.f;
     for (int c = 0; c < a.rs_final.nch; ++c) t += p[c];
-    rsv[threadIdx.x] = rsqrtf(t * a.rs_final.invn + a.rs_final.eps);
+    rs = rsqrtf(t * a.rs_final.invn + a.rs_final.eps);
   }
-  __syncthreads();
-  if (a.hidden) {
-    for (int i = 0; i < a.block; ++i) {
-      const long long row = (long long)(s * a.block + i) * a.H;
-      for (int k = threadIdx.x; k < a.H; k += 256) a.hidden[row + k] = a.g_final[k] * a.x[row + k] * rsv[i];
+  if (a.hidden)
+    for (int k = threadIdx.x; k < a.H; k += 256) a.hidden[m * a.H + k] = a.g_final[k] * a.x[m * a.H + k] * rs;
+  float d = 0.f;
+  if (tp >= 0 && tp < a.vocab) {
+    for (int k = threadIdx.x; k < a.R; k += 256) {
+      const long long idx = (long long)tp * a.w1_ld + k;
+      const float u = a.w1_f32 ? ((const float*)a.w1)[idx] : bf16_bits_to_f32(((const uint16_t*)a.w1)[idx]);
+      d += u * a.conf_wm[k];
     }
   }
-  for (int i = 0; i < a.block; ++i) {
-    int tp;
-    if (i == 0) tp = a.prev_token[s];
-    else tp = a.forced ? a.forced[s * a.block + i - 1] : toks[i - 1];
-    float d = 0.f;
-    if (tp >= 0 && tp < a.vocab) {
-      for (int k = threadIdx.x; k < a.R; k += 256) {
-        const long long idx = (long long)tp * a.w1_ld + k;
-        const float u = a.w1_f32 ? ((const float*)a.w1)[idx] : bf16_bits_to_f32(((const uint16_t*)a.w1)[idx]);
-        d += u * a.conf_wm[k];
-      }
-    }
-    d = block_sum256(d, red);
-    if (threadIdx.x == 0) {
-      const float* dp = a.dot + (long long)(s * a.block + i) * SSQ_LD;
-      float hd = 0.f;
-      for (int c = 0; c < a.nch; ++c) hd += dp[c];
-      const float x = rsv[i] * hd + d + a.conf_b[0];
-      a.conf[s * a.block + i] = 1.f / (1.f + __expf(-x));
-    }
+  d = block_sum256(d, red);
+  if (threadIdx.x == 0) {
+    a.tokens[m] = failed ? -1 : ti;
+    const float* dp = a.dot + m * SSQ_LD;
+    float hd = 0.f;
+    for (int c = 0; c < a.nch; ++c) hd += dp[c];
+    const float x = rs * hd + d + a.conf_b[0];
+    a.conf[m] = 1.f / (1.f + __expf(-x));
   }
 }
 
@@ -214,7 +226,7 @@ hipError_t launch_init(const InitArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_markov_final(const MarkovFinalArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_markov_final, dim3(a.n_seq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_markov_final, dim3(a.n_seq, a.block), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

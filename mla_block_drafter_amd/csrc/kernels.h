@@ -147,6 +147,24 @@ struct SwigluPost {
 };
 hipError_t launch_post_swiglu(const SwigluPost& a, hipStream_t st);
 
+// Persistent Markov rollout (k_markov.hip): W2 held in registers across the
+// block's positions; one launch for all of them.
+struct MarkovArgs {
+  const void* w2;             // packed bf16 W2, tiles of 16 vocabulary rows, KB k blocks each
+  int tiles;                  // ceil(vocab / 16)
+  const void* w1; int w1_ld;  // bf16 W1 rows (gather table)
+  int vocab, M, block;        // M = n_seq <= 16
+  const int32_t* prev_token; const int32_t* forced;
+  const float* z;             // lm_head logits [n_seq * block][vocab]
+  float* logits;              // optional [n_seq][block][vocab]
+  unsigned long long* slots;  // [block][M][workgroups] argmax keys, zeroed
+  int max_wgs;                // workgroups the slot array was sized for
+  unsigned* err;              // error flag, zeroed
+};
+int markov_rollout_wgs(int tiles);
+bool markov_rollout_supported(int KB, int M);
+hipError_t launch_markov_rollout(const MarkovArgs& a, int KB, hipStream_t st);
+
 struct MarkovFinalArgs {
   const unsigned long long* keys;
   const int32_t* prev_token; const int32_t* forced;
@@ -158,6 +176,10 @@ struct MarkovFinalArgs {
   float* hidden;              // optional [M][H] = rs * g_final * x
   int32_t* tokens; float* conf;
   int n_seq, block, vocab;
+  // rollout mode: argmax keys come from the rollout's slots [block][n_seq][nwg]
+  // instead of keys; nonzero *rollout_err (an expired poll) gives tokens of -1
+  const unsigned long long* slots; int nwg;
+  const unsigned* rollout_err;
 };
 hipError_t launch_markov_final(const MarkovFinalArgs& a, hipStream_t st);
 
