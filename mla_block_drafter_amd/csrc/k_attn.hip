@@ -54,9 +54,15 @@ __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s,
 // (global_load_lds_dwordx4: a wave writes 64 consecutive 16-byte LDS chunks,
 // no registers involved).  Two regions per tile buffer:
 //   A: the value part (first R = 8 CA elements of the key row), one key per
-//      load, rows CA + 1 chunks apart (the pad chunk spreads the banks);
+//      load, rows CA + 2 chunks apart: with 1056-byte rows both the 16-byte
+//      reads of S^T (16 keys per 16 lanes) and the transposing reads of V
+//      (8 keys per 32 lanes) hit each of the 64 LDS banks at most once per
+//      phase (with one pad chunk, 1040-byte rows, both were two-way
+//      conflicts);
 //   B: the rope part (CB chunks per key), 64 / CB keys per load, chunk p of
-//      key r holding source chunk p ^ (r % CB).
+//      key r holding source chunk p ^ bswz(r).  Rows are 128 bytes, so keys
+//      of equal parity use the same half of the banks; bswz gives the 8 such
+//      keys of a 16-lane read 8 different chunk orders.
 // Loads that fall past the slot read a valid dummy row (the sequence's first
 // block key); their scores are masked and their probabilities are zero.  So do
 // the rope-region chunks past the stored row when the query width is padded
@@ -69,9 +75,14 @@ __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s,
 // disjoint banks when the transposing LDS read gathers V for the same keys.
 __device__ __forceinline__ int key_perm(int m) { return (m >> 2 & 1) + 8 * (m >> 3) + 2 * (m & 3); }
 
+// Chunk order of region-B row r (depends on r mod 16 only, so key r of a
+// tile and key r - 16 of its second half agree).
+template <int CB>
+__device__ __forceinline__ int bswz(int r) { return (r >> 1) % CB; }
+
 template <int CA, int CB>
 struct TileGeom {
-  static constexpr int ROW_A = (CA + 1) * 8;      // elements between region-A rows
+  static constexpr int ROW_A = (CA + 2) * 8;      // elements between region-A rows
   static constexpr int SIZE_A = KT * ROW_A;       // elements
   static constexpr int KPB = 64 / CB;             // region-B keys per load
   static constexpr int NB_A = KT;                 // loads for region A
@@ -99,7 +110,7 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, int lane, int wave
     for (int i = 0; i < G::NB_A / 4; ++i, src += 4 * ld)
       if (CA == 64 || lane < CA) __builtin_amdgcn_global_load_lds(src, dst + (wave + 4 * i) * G::ROW_A, 16, 0, 0);
     if (wave < G::NB_B) {
-      const int r = wave * G::KPB + lane / CB, c = CA + ((lane % CB) ^ (r % CB));
+      const int r = wave * G::KPB + lane / CB, c = CA + ((lane % CB) ^ bswz<CB>(r));
       // chunks past the stored row (query padding, zero) read the dummy row
       const uint16_t* sb = 8 * c < a.latent ? cache + (off + kt0 + r) * ld + 8 * c : dummy;
       __builtin_amdgcn_global_load_lds(sb, dst + G::SIZE_A + wave * 512, 16, 0, 0);
@@ -119,11 +130,21 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, int lane, int wave
     if (CA == 64 || lane < CA) __builtin_amdgcn_global_load_lds(src, dst + b * G::ROW_A, 16, 0, 0);
   }
   if (wave < G::NB_B) {
-    const int r = wave * G::KPB + lane / CB, c = CA + ((lane % CB) ^ (r % CB));
+    const int r = wave * G::KPB + lane / CB, c = CA + ((lane % CB) ^ bswz<CB>(r));
     // chunks past the stored row (query padding, zero) read the dummy row
     const uint16_t* src = 8 * c < a.latent ? row_ptr(kt0 + r) + 8 * c : dummy;
     __builtin_amdgcn_global_load_lds(src, dst + G::SIZE_A + wave * 512, 16, 0, 0);
   }
+}
+
+// Workgroups go to the 8 XCDs round-robin (linear id L to XCD L % 8), and
+// each XCD has its own L2.  Each XCD gets a contiguous run of (slot, row
+// group) pairs, so the row groups of a slot, which read the same key tiles,
+// mostly share one L2 and the tiles come from HBM once per slot instead of
+// once per row group.  Placement only: any mapping would be correct.
+__device__ __forceinline__ int xcd_pair(int L, int ntot) {
+  const int x = L % 8, j = L / 8;
+  return x * (ntot / 8) + min(x, ntot % 8) + j;
 }
 
 template <int N>
@@ -189,8 +210,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   static_assert(NBUF <= 4 && 3 * G::NMIN <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF * G::BUF];
 
+  const int ngrp = a.rows_pad / 64;
+  const int pair = xcd_pair(blockIdx.x, gridDim.x);
+  const int slot = pair / ngrp, rgrp = pair % ngrp;
   int s, p, len, off, J;
-  slot_lookup(a, blockIdx.y, s, p, len, off, J);
+  slot_lookup(a, slot, s, p, len, off, J);
   if (s < 0) return;  // uniform over the workgroup
   const int k_begin = p * a.C;
   const int k_end = min(J, k_begin + a.C);
@@ -198,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile loads scalar
-  const int row0 = blockIdx.x * 64 + wave * 16;
+  const int row0 = rgrp * 64 + wave * 16;
   const int myrow = row0 + (lane & 15);
   const int grp = lane >> 4;
 
@@ -220,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   // byte offsets of chunks 4 k + grp (k < CB / 4) of region B for this lane's key
   uint32_t bx[CB / 4];
 #pragma unroll
-  for (int k = 0; k < CB / 4; ++k) bx[k] = 16 * ((4 * k + grp) ^ (kA % CB));
+  for (int k = 0; k < CB / 4; ++k) bx[k] = 16 * ((4 * k + grp) ^ bswz<CB>(kA));
   const int kV = key_perm(4 * grp + ((lane & 15) >> 2));  // key this lane addresses for V
   const int offV = kV * G::ROW_A + 4 * (lane & 3);    // + 16 h ROW_A + 16 d
   int keyS[4];                                        // keys of this lane's score entries
@@ -367,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 
   // ---- partials: O^T[dim = 16d + 4(lane>>4) + r][row = myrow]; layout
   //      [row][slot][dim] so the combine of one row reads contiguous memory ----
-  const long long prow = (long long)myrow * a.slots + blockIdx.y;
+  const long long prow = (long long)myrow * a.slots + slot;
   float* op = a.o_part + prow * a.r + 4 * grp;
 #pragma unroll
   for (int d = 0; d < NDT; ++d) *(f32x4*)(op + 16 * d) = acc[d];
@@ -484,7 +508,8 @@ bool attn_bf16_supported(int DQ, int r) {
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.rows_pad / 64, a.slots), block(256);
+  if (a.rows_pad % 64 || (long long)(a.rows_pad / 64) * a.slots > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((a.rows_pad / 64) * a.slots), block(256);
   if (a.DQ == 576 && a.r == 512)
     hipLaunchKernelGGL((k_attn_bf16<18, 32>), grid, block, 0, st, a);
   else if (a.DQ == 96 && a.r == 64)

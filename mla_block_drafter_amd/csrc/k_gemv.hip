@@ -21,12 +21,14 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   // Several tiles per wave share one activation fragment per k step (and,
   // with LDS staging, one staged slice per workgroup); split-K then restores
   // the wave count.
-  // Two tiles per wave streamed best for the M = 7 shapes (the unsplit
-  // 163,840-row lm_head included); the Markov gather GEMM, whose k range is
-  // only 256, keeps four; one when the matrix has too few tiles.
+  // Two tiles per wave streamed best for most M = 7 shapes (the unsplit
+  // 163,840-row lm_head included).  Four won where split-K still leaves
+  // enough waves: the Markov gather GEMM (k range only 256) and split
+  // matrices of at least 1792 tiles (the fused 28,672-row gate/up).  One
+  // when the matrix has too few tiles.
   p.TPW = 1;
   if (p.MT == 1) {
-    if (gather && w.TG % 4 == 0 && T / 4 >= 256) p.TPW = 4;
+    if (w.TG % 4 == 0 && ((gather && T / 4 >= 256) || (allow_split && T / 4 >= 448))) p.TPW = 4;
     else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 128 : 256)) p.TPW = 2;
   }
   const int waves = T / p.TPW;
