@@ -62,6 +62,10 @@ __device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // ------------------------------------------------------------ weight decode --
 // Two int8 codes (bytes sh/8 and sh/8 + 1 of w) -> two bf16 in one dword.  Codes
 // are integers of magnitude <= 127, exact in bf16; the fp32 conversion is exact

@@ -411,7 +411,7 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   P.C = 256;
   P.slots = (int)(cdiv(total_ctx + (long long)n_seq * c.block, P.C) + n_seq);
   if (!kv_f32) {
-    P.opart = take((long long)P.slots * P.rows_pad * c.kv_lora * 4);
+    P.opart = take((long long)P.slots * P.rows_pad * c.kv_lora * 2);
     P.mlpart = take((long long)P.slots * P.rows_pad * 2 * 4);
   }
   const long long ssq = (long long)M * SSQ_LD * 4;
@@ -558,7 +558,7 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
     if (P.kv_f32) {
       HIPCHK(launch_attn_f32(a, C.st));
     } else {
-      a.o_part = (float*)(C.ws + P.opart);
+      a.o_part = (uint16_t*)(C.ws + P.opart);
       a.ml_part = (float*)(C.ws + P.mlpart);
       HIPCHK(launch_attn_bf16(a, C.st));
       HIPCHK(launch_attn_combine(a, C.st));

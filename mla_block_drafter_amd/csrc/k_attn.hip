@@ -389,12 +389,21 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
     if (!redo_flag) break;
   }
 
-  // ---- partials: O^T[dim = 16d + 4(lane>>4) + r][row = myrow]; layout
-  //      [row][slot][dim] so the combine of one row reads contiguous memory ----
+  // ---- partials: O^T[dim = 16d + 4(lane>>4) + r][row = myrow] divided by
+  //      l, a convex combination of value rows, stored as fp16 (half the
+  //      bytes of fp32; 11-bit significand, finer than the bf16 operands).
+  //      Layout [row][slot][dim] so the combine of one row reads contiguous
+  //      memory.  l >= 1: the reference key of the slot contributes exp(0). ----
   const long long prow = (long long)myrow * a.slots + slot;
-  float* op = a.o_part + prow * a.r + 4 * grp;
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+  uint16_t* op = a.o_part + prow * a.r + 4 * grp;
 #pragma unroll
-  for (int d = 0; d < NDT; ++d) *(f32x4*)(op + 16 * d) = acc[d];
+  for (int d = 0; d < NDT; ++d) {
+    u32x2 h;
+    h[0] = f32_to_f16_bits(acc[d][0] * inv_l) | (f32_to_f16_bits(acc[d][1] * inv_l) << 16);
+    h[1] = f32_to_f16_bits(acc[d][2] * inv_l) | (f32_to_f16_bits(acc[d][3] * inv_l) << 16);
+    *(u32x2*)(op + 16 * d) = h;
+  }
   if (grp == 0) {
     a.ml_part[prow * 2] = m_run;
     a.ml_part[prow * 2 + 1] = l_run;
@@ -402,7 +411,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 }
 
 // Merge the slots of each (sequence, row) in slot order and write the
-// un-absorb fragments: O = sum_p exp(m_p - M) O_p / sum_p exp(m_p - M) l_p.
+// un-absorb fragments: with w_p = exp(m_p - M) l_p and the stored
+// Ohat_p = O_p / l_p, O = sum_p w_p Ohat_p / sum_p w_p.  Each thread owns two
+// adjacent dims (one 32-bit word of the fp16 row).
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   __shared__ float wgt[MAX_COMBINE_SLOTS];
   __shared__ float red[4];
@@ -422,25 +433,34 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   mx = block_max256(mx, red);
   float l = 0.f;
   for (int p = threadIdx.x; p < ns; p += 256) {
-    const float w = __expf(ml[2 * p] - mx);
+    const float w = __expf(ml[2 * p] - mx) * ml[2 * p + 1];
     wgt[p] = w;
-    l += ml[2 * p + 1] * w;
+    l += w;
   }
   l = block_sum256(l, red);  // also orders the wgt writes before the reads below
   const float invL = 1.f / l;
   const int i = row / a.nh, h = row % a.nh;
   const int m = s * a.block + i;
-  const float* op = a.o_part + ((long long)row * a.slots + base) * a.r;
-  for (int d = threadIdx.x; d < a.r; d += 256) {
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int rw = a.r / 2;  // 32-bit words per stored row
+  const uint32_t* op = (const uint32_t*)(a.o_part + ((long long)row * a.slots + base) * a.r);
+  for (int d2 = threadIdx.x; d2 < rw; d2 += 256) {
+    float o0[4] = {0.f, 0.f, 0.f, 0.f}, o1[4] = {0.f, 0.f, 0.f, 0.f};
     int p = 0;
-    for (; p + 8 <= ns; p += 8) {
+    for (; p + 4 <= ns; p += 4) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) o[u] += wgt[p + u] * op[(long long)(p + u) * a.r + d];
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t v = op[(long long)(p + u) * rw + d2];
+        o0[u] += wgt[p + u] * fp16_bits_to_f32(v & 0xFFFFu);
+        o1[u] += wgt[p + u] * fp16_bits_to_f32(v >> 16);
+      }
     }
-    for (; p < ns; ++p) o[0] += wgt[p] * op[(long long)p * a.r + d];
-    const float t = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
-    frag_put(a.fd_uv, h, m, d, t * invL);
+    for (; p < ns; ++p) {
+      const uint32_t v = op[(long long)p * rw + d2];
+      o0[0] += wgt[p] * fp16_bits_to_f32(v & 0xFFFFu);
+      o1[0] += wgt[p] * fp16_bits_to_f32(v >> 16);
+    }
+    frag_put(a.fd_uv, h, m, 2 * d2, ((o0[0] + o0[1]) + (o0[2] + o0[3])) * invL);
+    frag_put(a.fd_uv, h, m, 2 * d2 + 1, ((o1[0] + o1[1]) + (o1[2] + o1[3])) * invL);
   }
 }
 
@@ -520,7 +540,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st) {
-  if (a.slots > MAX_COMBINE_SLOTS) return hipErrorInvalidValue;
+  if (a.slots > MAX_COMBINE_SLOTS || a.r % 2) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_attn_combine, dim3(a.rows, a.n_seq), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -74,8 +74,8 @@ struct AttnArgs {
   int C;                  // keys per split (multiple of 32)
   int slots;              // slot bound (grid.y)
   float tau;
-  float* o_part;          // [slots][rows_pad][r]
-  float* ml_part;         // [slots][rows_pad][2]
+  uint16_t* o_part;       // [rows_pad][slots][r] fp16: each slot's O / l
+  float* ml_part;         // [rows_pad][slots][2]: each slot's (m, l)
   FragDesc fd_uv;         // output fragments (un-absorb input, grouped by head)
 };
 
