@@ -332,7 +332,7 @@ struct Plan {
   bool kv_f32 = false;
   long long x = 0, part = 0, q = 0, bkeys = 0, opart = 0, mlpart = 0, z = 0, keys = 0, mslots = 0, merr = 0, total = 0;
   int mwgs = 0;
-  long long ssq_a = 0, ssq_b = 0, ssq_cq = 0, dot = 0;
+  long long ssq_a = 0, ssq_b = 0, ssq_cq = 0, dot = 0, rope = 0;
   long long zero_begin = 0, zero_end = 0;
   Frag f_fc, f_qkva, f_qb, f_uk, f_uv, f_o, f_gu, f_down, f_lm;
   GemvPlan p_fc{}, p_qkva{}, p_qb{}, p_uk{}, p_uv{}, p_o{}, p_gu{}, p_down{}, p_lm{}, p_w2{};
@@ -419,6 +419,7 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   P.ssq_b = take(ssq);
   P.ssq_cq = take(ssq);
   P.dot = take(ssq);
+  P.rope = take((long long)M * (c.qk_rope / 2) * 8);
   if (!m.layers_only) P.z = take((long long)M * c.vocab * 4);
   P.total = off;
 }
@@ -476,6 +477,14 @@ struct Ctx {
   }
 };
 
+// RoPE table of the pass (cos, sin per row and frequency), built by k_init.
+void set_rope(const Ctx& C, InitArgs& a, const int32_t* offs) {
+  a.rope = (float*)(C.ws + C.P.rope);
+  a.offs = offs;
+  a.freqs = (const double*)(C.m->base + C.m->freqs);
+  a.npairs = C.m->c.qk_rope / 2;
+}
+
 // Attention half of layer l.  Input: fragments of in_norm * x in f_qkva and
 // the chunk sums of x^2 at workspace offset `x_ssq`.  Leaves the o_proj partials.
 int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t* offs) {
@@ -484,7 +493,6 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
   const Layer& L = m.L[l];
   Plan& P = C.P;
   const int M = P.M;
-  const double* freqs = (const double*)(m.base + m.freqs);
   HIPCHK(run_gemv(L.qkva, P.p_qkva, P.f_qkva, M, C.part(), C.st));
   {
     QkvaPost a{};
@@ -503,8 +511,7 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
     a.ssq_cq = C.ssq(P.ssq_cq);
     a.bkeys = C.ws + P.bkeys;
     a.kv_f32 = P.kv_f32;
-    a.offs = offs;
-    a.freqs = freqs;
+    a.rope = (const float*)(C.ws + P.rope);
     HIPCHK(launch_post_qkva(a, C.st));
   }
   HIPCHK(run_gemv(L.qb, P.p_qb, P.f_qb, M, C.part(), C.st));
@@ -523,8 +530,7 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
     a.fd_uk = P.f_uk.fd;
     a.q = C.ws + P.q;
     a.q_f32 = P.kv_f32;
-    a.offs = offs;
-    a.freqs = freqs;
+    a.rope = (const float*)(C.ws + P.rope);
     HIPCHK(launch_post_qb(a, C.st));
   }
   {
@@ -771,6 +777,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.block = c.block;
     a.H = c.hidden;
     a.fd_fc = P.f_fc.fd;
+    set_rope(C, a, in->kv_offsets);
     HIPCHK(launch_init(a, C.st));
   }
   HIPCHK(run_gemv(m->fc, P.p_fc, P.f_fc, M, C.part(), C.st));
@@ -921,6 +928,9 @@ int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_
     InitArgs a{};
     a.zero_ptr = C.ws + P.zero_begin;
     a.zero_bytes = P.zero_end - P.zero_begin;
+    a.n_seq = n_seq;
+    a.block = c.block;
+    set_rope(C, a, kv_offsets);
     HIPCHK(launch_init(a, C.st));
   }
   const Layer& L = m->L[layer];

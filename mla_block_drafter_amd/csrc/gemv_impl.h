@@ -47,12 +47,31 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return ((unsigned long long)hi << 32) | lo;
 }
 
-__device__ __forceinline__ float gemv_row_scale(const RowScale& s, int m) {
-  if (!s.ssq) return 1.f;
-  const float* p = s.ssq + (long long)m * SSQ_LD;
-  float t = 0.f;
-  for (int c = 0; c < s.nch; ++c) t += p[c];
-  return rsqrtf(t * s.invn + s.eps);
+// Row scales of this lane's output rows 16 mt + 4 (lane >> 4) + r, by the
+// whole wave: the chunk sums of all 16 rows of an m-tile are loaded together
+// (one memory round trip) and reduced in a fixed butterfly order.
+template <int MT>
+__device__ __forceinline__ void gemv_row_scales(const RowScale& s, int M, int lane, float (&rsv)[MT][4]) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    float t[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int m = mt * 16 + j;
+      const float* p = s.ssq + (long long)m * SSQ_LD;
+      t[j] = m < M ? (lane < s.nch ? p[lane] : 0.f) + (lane + 64 < s.nch ? p[lane + 64] : 0.f) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) t[j] += __shfl_xor(t[j], o, 64);
+    const int q = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = q == 0 ? t[r] : q == 1 ? t[4 + r] : q == 2 ? t[8 + r] : t[12 + r];
+      rsv[mt][r] = rsqrtf(x * s.invn + s.eps);
+    }
+  }
 }
 
 // Shared epilogue.  acc[mt][j] holds D[m][n] of tile t0 + j for this lane:
@@ -67,6 +86,8 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
     // int8 fragments of the next GEMM: tiles (t, t + 1), t even, are one
     // 32-column block, whose per-row maximum is taken over lanes 0..15 of
     // each 16-lane group (one row per group and r after the hi/lo sum).
+    float rsv[1][4] = {{1.f, 1.f, 1.f, 1.f}};
+    if (a.rs.ssq) gemv_row_scales<1>(a.rs, a.M, lane, rsv);
     f32x4 v[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -79,7 +100,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = (lane >> 4) * 4 + r;
-        const float rsm = (active && a.rs.ssq && m < a.M && lane < 32) ? gemv_row_scale(a.rs, m) : 1.f;
+        const float rsm = rsv[0][r];
         float x[2];
         bool ok[2];
         long long col[2];
@@ -108,10 +129,8 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mt * 16 + (lane >> 4) * 4 + r;
-        rsv[mt][r] = (active && a.rs.ssq && m < a.M) ? gemv_row_scale(a.rs, m) : 1.f;
-      }
+      for (int r = 0; r < 4; ++r) rsv[mt][r] = 1.f;
+    if (a.rs.ssq) gemv_row_scales<MT>(a.rs, a.M, lane, rsv);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int t = t0 + j;

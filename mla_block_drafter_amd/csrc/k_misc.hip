@@ -14,6 +14,18 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
   u32x4* z = (u32x4*)a.zero_ptr;
   const long long n16 = a.zero_bytes / 16;
   for (long long i = tid; i < n16; i += nthr) z[i] = u32x4{0u, 0u, 0u, 0u};
+  if (a.rope) {
+    // angles in float64 (positions reach 2^20 and more), stored as fp32 pairs
+    const long long nr = (long long)a.n_seq * a.block * a.npairs;
+    for (long long e = tid; e < nr; e += nthr) {
+      const int m = (int)(e / a.npairs), p = (int)(e % a.npairs);
+      const int s = m / a.block, i = m % a.block;
+      double sn, cs;
+      sincos((double)(a.offs[s + 1] - a.offs[s] + i) * a.freqs[p], &sn, &cs);
+      a.rope[2 * e] = (float)cs;
+      a.rope[2 * e + 1] = (float)sn;
+    }
+  }
   if (!a.captured) return;
   // fc input: row m = s*block + i, column k = c*H + h of captured[s][c][i][h];
   // every element of the fragment buffer is written (zeros outside M x K).
@@ -72,13 +84,9 @@ __global__ __launch_bounds__(256) void k_markov_final(MarkovFinalArgs a) {
   else if (a.forced) tp = a.forced[s * a.block + i - 1];
   else tp = token_at(i - 1);
   const int ti = token_at(i);
-  float rs;
-  {
-    const float* p = a.rs_final.ssq + m * SSQ_LD;
-    float t = 0.f;
-    for (int c = 0; c < a.rs_final.nch; ++c) t += p[c];
-    rs = rsqrtf(t * a.rs_final.invn + a.rs_final.eps);
-  }
+  // every wave computes the row scale and the dot-chunk sum (same bits in all)
+  const float rs = row_scale_wave(a.rs_final, (int)m);
+  const float hd = chunk_sum_wave(a.dot + m * SSQ_LD, a.nch);
   if (a.hidden)
     for (int k = threadIdx.x; k < a.H; k += 256) a.hidden[m * a.H + k] = a.g_final[k] * a.x[m * a.H + k] * rs;
   float d = 0.f;
@@ -92,9 +100,6 @@ __global__ __launch_bounds__(256) void k_markov_final(MarkovFinalArgs a) {
   d = block_sum256(d, red);
   if (threadIdx.x == 0) {
     a.tokens[m] = failed ? -1 : ti;
-    const float* dp = a.dot + m * SSQ_LD;
-    float hd = 0.f;
-    for (int c = 0; c < a.nch; ++c) hd += dp[c];
     const float x = rs * hd + d + a.conf_b[0];
     a.conf[m] = 1.f / (1.f + __expf(-x));
   }

@@ -16,41 +16,55 @@ namespace {
 
 // One row per workgroup (blockIdx.y), 256 columns per workgroup (blockIdx.x).
 
-__device__ __forceinline__ float row_scale(const RowScale& s, int m) {
-  if (!s.ssq) return 1.f;
-  const float* p = s.ssq + (long long)m * SSQ_LD;
-  float t = 0.f;
-  for (int c = 0; c < s.nch; ++c) t += p[c];
-  return rsqrtf(t * s.invn + s.eps);
-}
-
-// Row scale of row m, broadcast through LDS.
+// Row scale of row m (computed by wave 0), broadcast through LDS.
 __device__ __forceinline__ float shared_row_scale(const RowScale& s, int m, float* slot) {
-  if (threadIdx.x == 0) *slot = row_scale(s, m);
+  if (threadIdx.x < 64) {
+    const float v = row_scale_wave(s, m);
+    if (threadIdx.x == 0) *slot = v;
+  }
   __syncthreads();
   return *slot;
 }
 
-// Sum of the split-K partials of element (m, c): four independent chains so
-// the loads are in flight together; fixed order, hence deterministic.
-__device__ __forceinline__ float part_sum(const PartIn& p, int m, long long c) {
-  const float* q = p.part + (long long)m * p.ld + c;
-  float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-  int s = 0;
-  for (; s + 4 <= p.S; s += 4) {
-    v0 += q[s * p.ss];
-    v1 += q[(s + 1) * p.ss];
-    v2 += q[(s + 2) * p.ss];
-    v3 += q[(s + 3) * p.ss];
+// Sums of the split-K partials of elements (m, c[u]), u < N, columns with
+// c[u] < 0 skipped: eight splits per column are loaded together (every load
+// of a round, all N columns, is in flight at once; the loads are
+// unconditional, at clamped in-range addresses, so none waits on a branch),
+// each column summed in a fixed order, hence deterministic.
+template <int N>
+__device__ __forceinline__ void part_sum_n(const PartIn& p, int m, const int (&c)[N], float (&out)[N]) {
+  const float* q = p.part + (long long)m * p.ld;
+  float v[N][8];
+#pragma unroll
+  for (int n = 0; n < N; ++n)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[n][u] = 0.f;
+  for (int s = 0; s < p.S; s += 8) {
+    float x[N][8];
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[n][u] = q[(long long)min(s + u, p.S - 1) * p.ss + max(c[n], 0)];
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[n][u] += (c[n] >= 0 && s + u < p.S) ? x[n][u] : 0.f;
   }
-  for (; s < p.S; ++s) v0 += q[s * p.ss];
-  return (v0 + v1) + (v2 + v3);
+#pragma unroll
+  for (int n = 0; n < N; ++n)
+    out[n] = ((v[n][0] + v[n][1]) + (v[n][2] + v[n][3])) + ((v[n][4] + v[n][5]) + (v[n][6] + v[n][7]));
 }
 
-__device__ __forceinline__ void rope_pair(float x0, float x1, double pos, double f, float& y0, float& y1) {
-  double sn, cs;
-  sincos(pos * f, &sn, &cs);
-  const float c = (float)cs, s = (float)sn;
+__device__ __forceinline__ float part_sum(const PartIn& p, int m, int c) {
+  const int cc[1] = {c};
+  float o[1];
+  part_sum_n<1>(p, m, cc, o);
+  return o[0];
+}
+
+// Rotation of the pair (x0, x1) by the angle whose (cos, sin) is cs.
+__device__ __forceinline__ void rope_pair(float x0, float x1, const float* cs, float& y0, float& y1) {
+  const float c = cs[0], s = cs[1];
   y0 = x0 * c - x1 * s;
   y1 = x0 * s + x1 * c;
 }
@@ -115,15 +129,23 @@ __global__ __launch_bounds__(256) void k_post_qkva(QkvaPost a) {
     if (threadIdx.x == 0) a.ssq_cq[m * SSQ_LD + blockIdx.x] = sq;
     return;
   }
+  // latent columns k = tid + 256 u (latent <= 1024), all partial loads in flight together
   float s2 = 0.f;
-  for (int k = threadIdx.x; k < a.latent; k += 256) {
-    const float v = r * part_sum(a.p, m, a.q_lora + k);
-    lat[k] = v;
-    if (k < a.r) s2 += v * v;
+  {
+    int cc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cc[u] = (int)threadIdx.x + 256 * u < a.latent ? a.q_lora + (int)threadIdx.x + 256 * u : -1;
+    float v[4];
+    part_sum_n<4>(a.p, m, cc, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = threadIdx.x + 256 * u;
+      if (k >= a.latent) continue;
+      lat[k] = r * v[u];
+      if (k < a.r) s2 += lat[k] * lat[k];
+    }
   }
   const float rc = rsqrtf(block_sum256(s2, red) / a.r + a.eps);  // also orders lat[]
-  const int s = m / a.block, i = m % a.block;
-  const double pos = (double)(a.offs[s + 1] - a.offs[s] + i);
   for (int k = threadIdx.x; k < a.latent; k += 256) {
     float v;
     if (k < a.r) {
@@ -131,7 +153,7 @@ __global__ __launch_bounds__(256) void k_post_qkva(QkvaPost a) {
     } else {
       const int e = k - a.r, pr = e >> 1;
       float y0, y1;
-      rope_pair(lat[a.r + 2 * pr], lat[a.r + 2 * pr + 1], pos, a.freqs[pr], y0, y1);
+      rope_pair(lat[a.r + 2 * pr], lat[a.r + 2 * pr + 1], a.rope + ((long long)m * (a.dr / 2) + pr) * 2, y0, y1);
       v = (e & 1) ? y1 : y0;
     }
     const long long o = (long long)m * a.latent + k;
@@ -151,17 +173,20 @@ __global__ __launch_bounds__(256) void k_post_qb(QbPost a) {
   const int c0 = 2 * (blockIdx.x * 256 + threadIdx.x);
   if (c0 >= a.nh * hd) return;
   const int h = c0 / hd, e = c0 % hd;
-  const float v0 = r * part_sum(a.p, m, c0);
-  const float v1 = r * part_sum(a.p, m, c0 + 1);
+  float v[2];
+  {
+    const int cc[2] = {c0, c0 + 1};
+    part_sum_n<2>(a.p, m, cc, v);
+  }
+  const float v0 = r * v[0], v1 = r * v[1];
   if (e < a.dn) {
     frag_put(a.fd_uk, h, m, e, v0);
     frag_put(a.fd_uk, h, m, e + 1, v1);
   } else {
     const int s = m / a.block, i = m % a.block;
-    const double pos = (double)(a.offs[s + 1] - a.offs[s] + i);
     const int er = e - a.dn;
     float y0, y1;
-    rope_pair(v0, v1, pos, a.freqs[er >> 1], y0, y1);
+    rope_pair(v0, v1, a.rope + ((long long)m * (a.dr / 2) + (er >> 1)) * 2, y0, y1);
     const long long qi = ((long long)s * a.rows_pad + i * a.nh + h) * a.DQ + a.r + er;
     if (a.q_f32) {
       ((float*)a.q)[qi] = y0;
@@ -181,8 +206,10 @@ __global__ __launch_bounds__(256) void k_post_swiglu(SwigluPost a) {
   const bool ok = c < a.inter;
   float h = 0.f;
   if (ok) {
-    const float g = r * part_sum(a.p, m, c);
-    const float u = r * part_sum(a.p, m, a.inter + c);
+    float gu[2];
+    const int cc[2] = {c, a.inter + c};
+    part_sum_n<2>(a.p, m, cc, gu);
+    const float g = r * gu[0], u = r * gu[1];
     h = g / (1.f + __expf(-g)) * u;
   }
   frag_put_wave(a.fd, 0, m, c, h, ok);
@@ -198,7 +225,7 @@ hipError_t launch_post_resid(const ResidPost& a, hipStream_t st) {
 }
 
 hipError_t launch_post_qkva(const QkvaPost& a, hipStream_t st) {
-  if (a.latent > 1024) return hipErrorInvalidValue;
+  if (a.latent > 1024 || (a.q_lora + 255) / 256 > SSQ_LD) return hipErrorInvalidValue;
   dim3 grid((a.q_lora + 255) / 256 + 1, a.M);
   hipLaunchKernelGGL(k_post_qkva, grid, dim3(256), 0, st, a);
   return hipGetLastError();

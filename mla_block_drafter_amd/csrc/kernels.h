@@ -23,6 +23,23 @@ struct RowScale {
   float invn, eps;
 };
 
+// Sum of the nch <= SSQ_LD chunk values of one row, by a whole wave (all 64
+// lanes call it with the same arguments): every chunk is loaded at once and
+// added in a fixed butterfly order, so the cost is one memory round trip and
+// every lane returns the same bits.
+__device__ __forceinline__ float chunk_sum_wave(const float* row, int nch) {
+  const int lane = threadIdx.x & 63;
+  float t = (lane < nch ? row[lane] : 0.f) + (lane + 64 < nch ? row[lane + 64] : 0.f);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+  return t;
+}
+
+__device__ __forceinline__ float row_scale_wave(const RowScale& s, int m) {
+  if (!s.ssq) return 1.f;
+  return rsqrtf(chunk_sum_wave(s.ssq + (long long)m * SSQ_LD, s.nch) * s.invn + s.eps);
+}
+
 struct GemvArgs {
   PackedMat w;
   const void* act;        // input buffer (STORE/QLAT/FRAG) or plain gather table (MARKOV)
@@ -93,6 +110,12 @@ struct InitArgs {
   int cap_f32;
   int n_seq, ncap, block, H;
   FragDesc fd_fc;
+  // RoPE table (optional: rope == nullptr to skip): rope[m][p] = (cos, sin) of
+  // pos(m) * freqs[p] for row m = s * block + i at position kv_len(s) + i
+  float* rope;            // [n_seq * block][npairs][2]
+  const int32_t* offs;    // [n_seq + 1] cache offsets
+  const double* freqs;    // [npairs]
+  int npairs;
 };
 hipError_t launch_init(const InitArgs& a, hipStream_t st);
 
@@ -125,8 +148,7 @@ struct QkvaPost {
   const float* g_qa; const float* g_kva; float eps;
   FragDesc fd_qb; float* ssq_cq;
   void* bkeys; int kv_f32;   // [M][latent]
-  const int32_t* offs;
-  const double* freqs;        // [dr/2]
+  const float* rope;          // [M][dr/2][2] (cos, sin), written by k_init
 };
 hipError_t launch_post_qkva(const QkvaPost& a, hipStream_t st);
 
@@ -135,8 +157,7 @@ struct QbPost {
   int M, nh, dn, dr, r, block, DQ, rows_pad;
   FragDesc fd_uk;             // absorb input, groups = heads
   void* q; int q_f32;         // [n_seq][rows_pad][DQ]
-  const int32_t* offs;
-  const double* freqs;
+  const float* rope;          // [M][dr/2][2] (cos, sin), written by k_init
 };
 hipError_t launch_post_qb(const QbPost& a, hipStream_t st);
 
