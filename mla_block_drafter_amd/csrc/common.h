@@ -58,6 +58,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {  // round to nea
   return u >> 16;
 }
 
+// Two fp32 to packed bf16 (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 __device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   constexpr int CA = R / 8, CB = (DQ - R) / 8;
   using G = TileGeom<CA, CB>;
   static_assert(CA % 4 == 0, "each k-step reads one region");
-  static_assert(NBUF <= 4 && 3 * G::NMIN <= 63, "vmcnt range");
+  static_assert(NBUF == 4 && 2 * G::NMIN <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF * G::BUF];
 
   const int ngrp = a.rows_pad / 64;
@@ -256,7 +256,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   // VALU); if a later score exceeds the reference by more than REDO_SLACK,
   // where exp() could approach the fp32 range, the workgroup redoes the slot
   // once with the exact row maximum as the reference (pass 1).
+  // The running maximum and sum stay per lane inside the tile loop (no
+  // cross-lane traffic there); the four lanes of a row are combined after it.
   __shared__ int redo_flag;
+  const float c2 = a.tau * 1.4426950408889634f;  // base-2 score scale
   f32x4 acc[NDT];
   float m_run = -INFINITY, l_run = 0.f, m_all = -INFINITY;
   for (int pass = 0; pass < 2; ++pass) {
@@ -271,25 +274,26 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
       issue_tile<CA, CB>(a, lane, wave, k_begin + i * KT, k_end, s, len, off, cache, bk, dummy,
                          k_lds + i * G::BUF);
 
+  // One barrier per tile.  Tile t is in LDS once at most the loads of the
+  // tiles issued after it (t + 1 .. t + NBUF - 2, at least NMIN loads per
+  // tile for every wave) are outstanding; after the barrier every wave has
+  // also finished tile t - 1, whose buffer then receives tile t + NBUF - 1.
   for (int t = 0; t < ntiles; ++t) {
     const int kt0 = k_begin + t * KT;
     const int buf = t % NBUF;
-    if (t + NBUF - 1 < ntiles)  // refill the buffer every wave finished reading last iteration
-      issue_tile<CA, CB>(a, lane, wave, kt0 + (NBUF - 1) * KT, k_end, s, len, off, cache, bk, dummy,
-                         k_lds + ((t + NBUF - 1) % NBUF) * G::BUF);
-    // tile t is in LDS once at most the loads of the tiles issued after it
-    // (at least NMIN per tile for every wave) are outstanding
-    const int after = min(NBUF - 1, ntiles - 1 - t);
-    if (after >= 3) wait_vmcnt<3 * G::NMIN>();
-    else if (after == 2) wait_vmcnt<2 * G::NMIN>();
+    const int after = min(NBUF - 2, ntiles - 1 - t);
+    if (after >= 2) wait_vmcnt<2 * G::NMIN>();
     else if (after == 1) wait_vmcnt<G::NMIN>();
     else wait_vmcnt<0>();
     // the barrier intrinsic has no memory semantics of its own, so the
     // compiler fences keep LDS accesses on their side of it (a __syncthreads
-    // would also drain the prefetch of the next tile)
+    // would also drain the prefetch of the next tiles)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if (t + NBUF - 1 < ntiles)
+      issue_tile<CA, CB>(a, lane, wave, kt0 + (NBUF - 1) * KT, k_end, s, len, off, cache, bk, dummy,
+                         k_lds + ((t + NBUF - 1) % NBUF) * G::BUF);
     const uint16_t* tb = k_lds + buf * G::BUF;
 
     // ---- S^T for 32 keys x 16 rows: two 16-key MFMA tiles, read n = 2 kb + h
@@ -316,37 +320,51 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
         st[n % 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f), qf[n / 2], st[n % 2], 0, 0, 0);
       });
     }
-    // lane holds keys kt0 + 16 h + keyS[r] for query row myrow
-    float tmax = -INFINITY;
+    // the first V fragments do not depend on P: their reads go out now and
+    // arrive while the probabilities are computed
+    const uint32_t vaddr = lds_addr(tb + offV);
+    u32x2 vlo[PV_AHEAD + 1], vhi[PV_AHEAD + 1];
+    auto issue_v = [&](auto DI) {
+      constexpr int d = decltype(DI)::value;
+      tr_read_pair<32 * d, 32 * d + 2 * 16 * G::ROW_A>(vaddr, vlo[d % (PV_AHEAD + 1)], vhi[d % (PV_AHEAD + 1)]);
+    };
+    static_for<PV_AHEAD < NDT ? PV_AHEAD : NDT>(issue_v);
+
+    // lane holds keys kt0 + 16 h + keyS[r] for query row myrow.  Scores are
+    // kept in base-2 units x = s * tau * log2(e) (tau > 0, so the maximum of
+    // the raw products gives the maximum of x); keys past the slot (last
+    // tile only) get -inf.
+    if (kt0 + KT > k_end) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = kt0 + 16 * h + keyS[r];
-        const float v = j < k_end ? st[h][r] * a.tau : -INFINITY;
-        st[h][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    m_all = fmaxf(m_all, tmax);
-    if (pass == 0 && t == 0) m_run = tmax;  // finite: tile 0 holds a valid key
-    float psum = 0.f;
+        for (int r = 0; r < 4; ++r)
+          if (kt0 + 16 * h + keyS[r] >= k_end) st[h][r] = -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
+                       fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3]))) * c2;
+    m_all = fmaxf(m_all, tmax);  // this lane's keys only
+    if (pass == 0 && t == 0) {
+      // the reference: the row maximum over tile 0 (finite: tile 0 holds a
+      // valid key).  These shuffles are LDS operations issued after the V
+      // reads above; the compiler waits for them (and so for the V reads)
+      // before m_run is used.
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      m_run = tmax;
+    }
     u32x4 pw;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[r] = m_run == -INFINITY ? 0.f : __expf(st[h][r] - m_run);
-        psum += pr[r];
+        pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[h][r], c2, -m_run));
+        l_run += pr[r];  // this lane's keys only
       }
-      pw[2 * h] = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
-      pw[2 * h + 1] = f32_to_bf16_bits(pr[2]) | (f32_to_bf16_bits(pr[3]) << 16);
+      pw[2 * h] = pack_bf16x2(pr[0], pr[1]);
+      pw[2 * h + 1] = pack_bf16x2(pr[2], pr[3]);
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run += psum;
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 
     // ---- O^T += V^T P^T.  k slots 0..3 of lane group g are keys keyS[] of
@@ -356,16 +374,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
     //      (lane & 15) = 4 j + a addresses key keyS[j], dims 16 d + 4 a, so
     //      lane 4a + e receives dim 16 d + 4a + e of keys keyS[0..3] ----
     {
-      const uint32_t vaddr = lds_addr(tb + offV);
-      u32x2 vlo[PV_AHEAD + 1], vhi[PV_AHEAD + 1];
-      auto issue = [&](auto DI) {
-        constexpr int d = decltype(DI)::value;
-        tr_read_pair<32 * d, 32 * d + 2 * 16 * G::ROW_A>(vaddr, vlo[d % (PV_AHEAD + 1)], vhi[d % (PV_AHEAD + 1)]);
-      };
-      static_for<PV_AHEAD < NDT ? PV_AHEAD : NDT>(issue);
       static_for<NDT>([&](auto DI) {
         constexpr int d = decltype(DI)::value;
-        if constexpr (d + PV_AHEAD < NDT) issue(std::integral_constant<int, d + PV_AHEAD>{});
+        if constexpr (d + PV_AHEAD < NDT) issue_v(std::integral_constant<int, d + PV_AHEAD>{});
         constexpr int ahead = NDT - 1 - d < PV_AHEAD ? NDT - 1 - d : PV_AHEAD;
         u32x2& lo = vlo[d % (PV_AHEAD + 1)];
         u32x2& hi = vhi[d % (PV_AHEAD + 1)];
@@ -374,17 +385,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
         acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v4), pf, acc[d], 0, 0, 0);
       });
     }
-    // every wave is done reading this buffer before it is refilled
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
   }
-
+    // combine the four lanes of each row (fixed butterfly: same bits in all)
+    m_all = fmaxf(m_all, __shfl_xor(m_all, 16, 64));
+    m_all = fmaxf(m_all, __shfl_xor(m_all, 32, 64));
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
     if (pass == 1) break;
-    // every wave has passed the loop's last barrier; decide the redo together
+    // every wave has finished its tile reads; decide the redo together (the
+    // barriers also keep the redo's tile loads off buffers still being read)
     if (threadIdx.x == 0) redo_flag = 0;
     __syncthreads();
-    if (__any(m_all > m_run + REDO_SLACK) && lane == 0) atomicOr(&redo_flag, 1);
+    if (__any(m_all > m_run + REDO_SLACK * 1.4426950408889634f) && lane == 0) atomicOr(&redo_flag, 1);
     __syncthreads();
     if (!redo_flag) break;
   }
@@ -405,7 +417,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
     *(u32x2*)(op + 16 * d) = h;
   }
   if (grp == 0) {
-    a.ml_part[prow * 2] = m_run;
+    a.ml_part[prow * 2] = m_run * 0.6931471805599453f;  // back to natural-log units
     a.ml_part[prow * 2 + 1] = l_run;
   }
 }
