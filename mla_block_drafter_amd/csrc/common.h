@@ -66,13 +66,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
+// Two fp32 to packed fp16 (low half = a), round to nearest even.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
+
 __device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {  // round to nearest even
-  return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
 
 // ------------------------------------------------------------ weight decode --
 // Two int8 codes (bytes sh/8 and sh/8 + 1 of w) -> two bf16 in one dword.  Codes

@@ -406,15 +406,28 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   //      bytes of fp32; 11-bit significand, finer than the bf16 operands).
   //      Layout [row][slot][dim] so the combine of one row reads contiguous
   //      memory.  l >= 1: the reference key of the slot contributes exp(0). ----
+  //      Each wave stages its 16 rows in LDS and stores them as whole rows
+  //      (one 1 KiB row per store instead of 16 scattered 32-byte pieces).
   const long long prow = (long long)myrow * a.slots + slot;
   const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-  uint16_t* op = a.o_part + prow * a.r + 4 * grp;
+  __syncthreads();  // every wave is done with the tile buffers
+  constexpr int RB = R * 2 + 16;  // bytes per staged row (the pad spreads the banks)
+  unsigned char* stage = (unsigned char*)k_lds + wave * 16 * RB;
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     u32x2 h;
-    h[0] = f32_to_f16_bits(acc[d][0] * inv_l) | (f32_to_f16_bits(acc[d][1] * inv_l) << 16);
-    h[1] = f32_to_f16_bits(acc[d][2] * inv_l) | (f32_to_f16_bits(acc[d][3] * inv_l) << 16);
-    *(u32x2*)(op + 16 * d) = h;
+    h[0] = pack_f16x2(acc[d][0] * inv_l, acc[d][1] * inv_l);
+    h[1] = pack_f16x2(acc[d][2] * inv_l, acc[d][3] * inv_l);
+    *(u32x2*)(stage + (lane & 15) * RB + (16 * d + 4 * grp) * 2) = h;
+  }
+  constexpr int LPR = R / 8;     // lanes per row, 16 bytes each
+  constexpr int RPI = 64 / LPR;  // rows per store
+  static_assert(64 % LPR == 0 && 16 % RPI == 0, "row staging");
+#pragma unroll
+  for (int it = 0; it < 16 / RPI; ++it) {
+    const int rr = it * RPI + lane / LPR, cb = (lane % LPR) * 16;
+    const u32x4 v = *(const u32x4*)(stage + rr * RB + cb);
+    *(u32x4*)((unsigned char*)(a.o_part + ((long long)(row0 + rr) * a.slots + slot) * a.r) + cb) = v;
   }
   if (grp == 0) {
     a.ml_part[prow * 2] = m_run * 0.6931471805599453f;  // back to natural-log units
