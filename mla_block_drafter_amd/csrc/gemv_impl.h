@@ -28,6 +28,20 @@ __device__ __forceinline__ T ntload(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// Buffer loads for the k loops.  Every stage issues the same loads whatever
+// the k range: a load past the range (the last stage of a wave's k range
+// may be partial) gets offset BUF_OOB, beyond the resource's size, so it
+// returns zeros without touching memory.  The stage loop then has no
+// conditional loads, and the compiler's wait counts stay exact (after a
+// conditionally skipped load it must wait for every load in flight, which
+// drains the prefetched stage).
+constexpr uint32_t BUF_OOB = 0x80000000u;
+constexpr int BUF_NT = 2;  // cache policy: non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Markov predecessor of position a.step for sequence m (callers treat values
 // outside [0, vocab) as "no predecessor").
 __device__ __forceinline__ int markov_prev(const GemvArgs& a, int m) {
@@ -253,7 +267,9 @@ __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, 
 template <int FMT, int MT, int TPW, int MODE, int AMODE>
 __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gemv_smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index made wave-uniform (scalar): tile bases and buffer resources
+  // derived from it live in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = a.w.ngroups * a.w.TG;
   const int t0 = (blockIdx.x * 4 + wave) * TPW;
   const bool active = t0 < T;
@@ -366,40 +382,47 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
     // before stage s is consumed, so a wave always has loads in flight.
     if constexpr (FMT == DT_Q8_0 && AMODE == A_GLOBAL_I8) {
       // int8 activation fragments from global memory (L2 resident), loaded
-      // with the weights of the same stage; no LDS, no barrier.
-      constexpr int U = 8 / TPW;  // pairs of k blocks per stage
-      const int KP = KB >> 1;
-      const u32x4* wp = (const u32x4*)a.w.codes + (long long)t0 * KP * 64 + lane;
-      const uint32_t* sp = (const uint32_t*)a.w.scales + (long long)t0 * KP * 16 + (lane & 15);
-      const unsigned char* abase = (const unsigned char*)a.act + (long long)g * a.act_gstride;
-      const long* acode = (const long*)abase + lane;                                      // [KB][64]
-      const uint32_t* aexp = (const uint32_t*)(abase + (long long)KB * 512) + ((lane >> 4) & 1);  // [KB][2]
+      // with the weights of the same stage; no LDS, no barrier.  Stage = U
+      // pairs of k blocks; pair p of tile j: 1 KiB of codes, 64 B of scales.
+      constexpr int U = 8 / TPW;
+      const int KP = KB >> 1, P0 = kb0 >> 1, P1 = kb1 >> 1;
+      const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)t0 * KP * 1024,
+                                                 (uint32_t)(TPW * KP * 1024));
+      const __amdgpu_buffer_rsrc_t sr = buf_rsrc((const unsigned char*)a.w.scales + (long long)t0 * KP * 64,
+                                                 (uint32_t)(TPW * KP * 64));
+      const __amdgpu_buffer_rsrc_t ar = buf_rsrc((const unsigned char*)a.act + (long long)g * a.act_gstride,
+                                                 (uint32_t)(KB * 520));
+      const uint32_t lw = lane * 16, ls = (lane & 15) * 4, la = lane * 8;
+      const uint32_t le = KB * 512 + ((lane >> 4) & 1) * 4;  // this lane's exponent word, k block 0
       struct Stage {
         u32x4 w[U][TPW];
         uint32_t s[U][TPW];
         long c[U][2];
         uint32_t e[U][2];
       };
-      auto load_stage = [&](Stage& st, int kb) {
+      auto load_stage = [&](Stage& st, int q0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          if (kb + 2 * u >= kb1) break;
-          const int p = (kb >> 1) + u;
+          const int p = q0 + u;
+          const bool ok = p < P1;
 #pragma unroll
           for (int j = 0; j < TPW; ++j) {
-            st.w[u][j] = ntload(wp + ((long long)j * KP + p) * 64);
-            st.s[u][j] = sp[((long long)j * KP + p) * 16];
+            st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                wr, ok ? (uint32_t)((j * KP + p) * 1024) + lw : BUF_OOB, 0, BUF_NT));
+            st.s[u][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, ok ? (uint32_t)((j * KP + p) * 64) + ls : BUF_OOB, 0, 0);
           }
-          st.c[u][0] = acode[(long long)(2 * p) * 64];
-          st.c[u][1] = acode[(long long)(2 * p + 1) * 64];
-          st.e[u][0] = aexp[(2 * p) * 2];
-          st.e[u][1] = aexp[(2 * p + 1) * 2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            st.c[u][h] = __builtin_bit_cast(long, __builtin_amdgcn_raw_buffer_load_b64(
+                ar, ok ? (uint32_t)((2 * p + h) * 512) + la : BUF_OOB, 0, 0));
+            st.e[u][h] = __builtin_amdgcn_raw_buffer_load_b32(ar, ok ? (uint32_t)((2 * p + h) * 8) + le : BUF_OOB, 0, 0);
+          }
         }
       };
-      auto compute_stage = [&](const Stage& st, int kb) {
+      auto compute_stage = [&](const Stage& st, int q0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          if (kb + 2 * u >= kb1) break;
+          if (q0 + u >= P1) break;
           int e0[4], e1[4];  // activation exponents of this lane's 4 rows
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -422,13 +445,80 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
         }
       };
       Stage sa, sb;
+      const int nst = (P1 - P0 + U - 1) / U;
+      load_stage(sa, P0);
+      int q = P0, st = 0;
+      for (; st + 2 < nst; st += 2, q += 2 * U) {
+        load_stage(sb, q + U);
+        compute_stage(sa, q);
+        load_stage(sa, q + 2 * U);
+        compute_stage(sb, q + U);
+      }
+      if (st + 1 < nst) {
+        load_stage(sb, q + U);
+        compute_stage(sa, q);
+        compute_stage(sb, q + U);
+      } else {
+        compute_stage(sa, q);
+      }
+    } else if (FMT == DT_BF16 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
+      // bf16 weights, prepared bf16 activation fragments: both loaded per
+      // stage of U k blocks (tile j, k block kb: 1 KiB of weights; m-tile mt:
+      // 1 KiB of activations).
+      constexpr int U = (MT == 1 ? 8 : 4) / TPW;
+      const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)t0 * KB * 1024,
+                                                 (uint32_t)(TPW * KB * 1024));
+      const __amdgpu_buffer_rsrc_t ar = buf_rsrc(afrag, (uint32_t)(MT * KB * 1024));
+      const uint32_t l16 = lane * 16;
+      struct Stage {
+        u32x4 w[U][TPW];
+        u32x4 x[U][MT];
+      };
+      auto load_stage = [&](Stage& st, int k0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int kb = k0 + u;
+          const bool ok = kb < kb1;
+#pragma unroll
+          for (int j = 0; j < TPW; ++j)
+            st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                wr, ok ? (uint32_t)((j * KB + kb) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            st.x[u][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                ar, ok ? (uint32_t)((mt * KB + kb) * 1024) + l16 : BUF_OOB, 0, 0));
+        }
+      };
+      auto compute_stage = [&](const Stage& st, int k0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (k0 + u >= kb1) break;
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            const bf16x8 B = __builtin_bit_cast(bf16x8, st.w[u][j]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.x[u][mt]), B,
+                                                                    acc[mt][j], 0, 0, 0);
+          }
+        }
+      };
+      Stage sa, sb;
+      const int nst = (kb1 - kb0 + U - 1) / U;
       load_stage(sa, kb0);
-      for (int kb = kb0; kb < kb1; kb += 4 * U) {
-        if (kb + 2 * U < kb1) load_stage(sb, kb + 2 * U);
+      int kb = kb0, st = 0;
+      for (; st + 2 < nst; st += 2, kb += 2 * U) {
+        load_stage(sb, kb + U);
         compute_stage(sa, kb);
-        if (kb + 2 * U >= kb1) break;
-        if (kb + 4 * U < kb1) load_stage(sa, kb + 4 * U);
-        compute_stage(sb, kb + 2 * U);
+        load_stage(sa, kb + 2 * U);
+        compute_stage(sb, kb + U);
+      }
+      if (st + 1 < nst) {
+        load_stage(sb, kb + U);
+        compute_stage(sa, kb);
+        compute_stage(sb, kb + U);
+      } else {
+        compute_stage(sa, kb);
       }
     } else if (FMT == DT_BF16) {
       constexpr int U = (MT == 1 ? 8 : 4) / TPW;  // k blocks per stage
