@@ -226,7 +226,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2, A_GLOBAL_I8 = 3 };
+enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2, A_GLOBAL_I8 = 3, A_LDS_I8 = 4 };
 
 // Eight fp32 activations of row `row` from column k0 (zero outside M x K).
 __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, int row, int k0, float (&v)[8]) {
@@ -256,6 +256,10 @@ __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, 
 //             power-of-two scale per (row, 32-block), written by the producing
 //             kernel (frag_put_i8) and read from global memory with the weight
 //             stream; v_mfma_i32_16x16x32_i8 on the raw weight codes;
+//  A_LDS_I8:  as A_GLOBAL_I8, but the workgroup first copies its k range of
+//             the fragments into LDS (direct-to-LDS loads, overlapped with
+//             the first weight stage) and the k loop reads them from there:
+//             the weight stream keeps the memory pipeline to itself.
 //  A_ROWS_I8: Q8_0 with M <= 8: each row's slice (the workgroup's k range)
 //             is quantised with one scale s to an int8 hi code and an int8
 //             residual code (scale s / 256), and the int8 weight codes feed
@@ -361,7 +365,130 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
     for (int j = 0; j < TPW; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   bool staged = false;
-  if (active) {
+  if constexpr (FMT == DT_Q8_0 && (AMODE == A_GLOBAL_I8 || AMODE == A_LDS_I8)) {
+    // Every wave runs this loop (inactive waves' loads fall outside their
+    // buffer resources and read zeros), so all waves reach the barrier of the
+    // LDS staging.  Stage = U pairs of k blocks; pair p of tile j: 1 KiB of
+    // codes, 64 B of scales.
+    constexpr bool SL = AMODE == A_LDS_I8;
+    constexpr int U = 8 / TPW;
+    const int KP = KB >> 1, P0 = kb0 >> 1, P1 = kb1 >> 1;
+    const uint32_t wbytes = active ? (uint32_t)(TPW * KP * 1024) : 0u;
+    const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)(active ? t0 : 0) * KP * 1024, wbytes);
+    const __amdgpu_buffer_rsrc_t sr = buf_rsrc((const unsigned char*)a.w.scales + (long long)(active ? t0 : 0) * KP * 64,
+                                               active ? (uint32_t)(TPW * KP * 64) : 0u);
+    const unsigned char* abase = (const unsigned char*)a.act + (long long)g * a.act_gstride;
+    const __amdgpu_buffer_rsrc_t ar = buf_rsrc(abase, (uint32_t)(KB * 520));
+    const uint32_t lw = lane * 16, ls = (lane & 15) * 4, la = lane * 8;
+    const uint32_t le = KB * 512 + ((lane >> 4) & 1) * 4;  // this lane's exponent word, k block 0
+    const int nkb = max(kb1 - kb0, 0);
+    if constexpr (SL) {
+      // codes [kb0, kb1) x 512 B, then exponents [kb0, kb1) x 8 B, 1 KiB per load
+      const int ncode = nkb / 2, ebytes = nkb * 8;
+      for (int ch = wave; ch < ncode; ch += 4)
+        __builtin_amdgcn_global_load_lds(abase + (long long)kb0 * 512 + ch * 1024 + lane * 16, gemv_smem + ch * 1024, 16, 0, 0);
+      for (int ch = wave; ch * 1024 < ebytes; ch += 4)
+        if (ch * 1024 + lane * 16 < ebytes)
+          __builtin_amdgcn_global_load_lds(abase + (long long)KB * 512 + kb0 * 8 + ch * 1024 + lane * 16,
+                                           gemv_smem + nkb * 512 + ch * 1024, 16, 0, 0);
+    }
+    struct Stage {
+      u32x4 w[U][TPW];
+      uint32_t s[U][TPW];
+      long c[U][2];
+      uint32_t e[U][2];
+    };
+    auto load_stage = [&](Stage& st, int q0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = q0 + u;
+        const bool ok = p < P1;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+              wr, ok ? (uint32_t)((j * KP + p) * 1024) + lw : BUF_OOB, 0, BUF_NT));
+          st.s[u][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, ok ? (uint32_t)((j * KP + p) * 64) + ls : BUF_OOB, 0, 0);
+        }
+        if constexpr (!SL) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            st.c[u][h] = __builtin_bit_cast(long, __builtin_amdgcn_raw_buffer_load_b64(
+                ar, ok ? (uint32_t)((2 * p + h) * 512) + la : BUF_OOB, 0, 0));
+            st.e[u][h] = __builtin_amdgcn_raw_buffer_load_b32(ar, ok ? (uint32_t)((2 * p + h) * 8) + le : BUF_OOB, 0, 0);
+          }
+        }
+      }
+    };
+    auto compute_stage = [&](const Stage& st, int q0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = q0 + u;
+        if (p >= P1) break;
+        long c[2];
+        uint32_t e[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if constexpr (SL) {
+            const int kl = 2 * p + h - kb0;
+            c[h] = *(const long*)(gemv_smem + kl * 512 + lane * 8);
+            e[h] = *(const uint32_t*)(gemv_smem + nkb * 512 + kl * 8 + ((lane >> 4) & 1) * 4);
+          } else {
+            c[h] = st.c[u][h];
+            e[h] = st.e[u][h];
+          }
+        }
+        int e0[4], e1[4];  // activation exponents of this lane's 4 rows
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e0[r] = (int)(signed char)(e[0] >> (8 * r));
+          e1[r] = (int)(signed char)(e[1] >> (8 * r));
+        }
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          const long B0 = (long)(((unsigned long long)st.w[u][j][1] << 32) | st.w[u][j][0]);
+          const long B1 = (long)(((unsigned long long)st.w[u][j][3] << 32) | st.w[u][j][2]);
+          const float d0 = fp16_bits_to_f32(st.s[u][j] & 0xFFFFu);
+          const float d1 = fp16_bits_to_f32(st.s[u][j] >> 16);
+          const i32x4 z = {0, 0, 0, 0};
+          const i32x4 p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(c[0], B0, z, 0, 0, 0);
+          const i32x4 p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(c[1], B1, z, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[0][j][r] += ldexpf(d0, e0[r]) * (float)p0[r] + ldexpf(d1, e1[r]) * (float)p1[r];
+        }
+      }
+    };
+    Stage sa, sb;
+    const int nst = (P1 - P0 + U - 1) / U;
+    load_stage(sa, P0);
+    if constexpr (SL) {
+      // this wave's copies are done once at most the first stage's loads are
+      // outstanding; the barrier then covers every wave's copies.  The wait
+      // is the builtin (gfx9 encoding: vmcnt split over bits 3:0 and 15:14,
+      // expcnt and lgkmcnt left at their maxima) so that the compiler knows
+      // the copies are complete and adds no wait for them in the loop.
+      constexpr int NV = 2 * U * TPW;
+      static_assert(NV < 64, "vmcnt range");
+      __builtin_amdgcn_s_waitcnt((NV & 15) | (7 << 4) | (15 << 8) | ((NV >> 4) << 14));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    int q = P0, st = 0;
+    for (; st + 2 < nst; st += 2, q += 2 * U) {
+      load_stage(sb, q + U);
+      compute_stage(sa, q);
+      load_stage(sa, q + 2 * U);
+      compute_stage(sb, q + U);
+    }
+    if (st + 1 < nst) {
+      load_stage(sb, q + U);
+      compute_stage(sa, q);
+      compute_stage(sb, q + U);
+    } else if (nst > 0) {
+      compute_stage(sa, q);
+    }
+    staged = true;
+  } else if (active) {
     const bf16x8* afrag = (const bf16x8*)a.act + (long long)g * (a.act_gstride / 8);
     const __bf16* gsrc = nullptr;
     if (MODE == GEMV_MARKOV) {
@@ -380,88 +507,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
 
     // Weight stream, software pipelined: the loads of stage s+1 are issued
     // before stage s is consumed, so a wave always has loads in flight.
-    if constexpr (FMT == DT_Q8_0 && AMODE == A_GLOBAL_I8) {
-      // int8 activation fragments from global memory (L2 resident), loaded
-      // with the weights of the same stage; no LDS, no barrier.  Stage = U
-      // pairs of k blocks; pair p of tile j: 1 KiB of codes, 64 B of scales.
-      constexpr int U = 8 / TPW;
-      const int KP = KB >> 1, P0 = kb0 >> 1, P1 = kb1 >> 1;
-      const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)t0 * KP * 1024,
-                                                 (uint32_t)(TPW * KP * 1024));
-      const __amdgpu_buffer_rsrc_t sr = buf_rsrc((const unsigned char*)a.w.scales + (long long)t0 * KP * 64,
-                                                 (uint32_t)(TPW * KP * 64));
-      const __amdgpu_buffer_rsrc_t ar = buf_rsrc((const unsigned char*)a.act + (long long)g * a.act_gstride,
-                                                 (uint32_t)(KB * 520));
-      const uint32_t lw = lane * 16, ls = (lane & 15) * 4, la = lane * 8;
-      const uint32_t le = KB * 512 + ((lane >> 4) & 1) * 4;  // this lane's exponent word, k block 0
-      struct Stage {
-        u32x4 w[U][TPW];
-        uint32_t s[U][TPW];
-        long c[U][2];
-        uint32_t e[U][2];
-      };
-      auto load_stage = [&](Stage& st, int q0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int p = q0 + u;
-          const bool ok = p < P1;
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) {
-            st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                wr, ok ? (uint32_t)((j * KP + p) * 1024) + lw : BUF_OOB, 0, BUF_NT));
-            st.s[u][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, ok ? (uint32_t)((j * KP + p) * 64) + ls : BUF_OOB, 0, 0);
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            st.c[u][h] = __builtin_bit_cast(long, __builtin_amdgcn_raw_buffer_load_b64(
-                ar, ok ? (uint32_t)((2 * p + h) * 512) + la : BUF_OOB, 0, 0));
-            st.e[u][h] = __builtin_amdgcn_raw_buffer_load_b32(ar, ok ? (uint32_t)((2 * p + h) * 8) + le : BUF_OOB, 0, 0);
-          }
-        }
-      };
-      auto compute_stage = [&](const Stage& st, int q0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (q0 + u >= P1) break;
-          int e0[4], e1[4];  // activation exponents of this lane's 4 rows
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            e0[r] = (int)(signed char)(st.e[u][0] >> (8 * r));
-            e1[r] = (int)(signed char)(st.e[u][1] >> (8 * r));
-          }
-#pragma unroll
-          for (int j = 0; j < TPW; ++j) {
-            const long B0 = (long)(((unsigned long long)st.w[u][j][1] << 32) | st.w[u][j][0]);
-            const long B1 = (long)(((unsigned long long)st.w[u][j][3] << 32) | st.w[u][j][2]);
-            const float d0 = fp16_bits_to_f32(st.s[u][j] & 0xFFFFu);
-            const float d1 = fp16_bits_to_f32(st.s[u][j] >> 16);
-            const i32x4 z = {0, 0, 0, 0};
-            const i32x4 p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(st.c[u][0], B0, z, 0, 0, 0);
-            const i32x4 p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(st.c[u][1], B1, z, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[0][j][r] += ldexpf(d0, e0[r]) * (float)p0[r] + ldexpf(d1, e1[r]) * (float)p1[r];
-          }
-        }
-      };
-      Stage sa, sb;
-      const int nst = (P1 - P0 + U - 1) / U;
-      load_stage(sa, P0);
-      int q = P0, st = 0;
-      for (; st + 2 < nst; st += 2, q += 2 * U) {
-        load_stage(sb, q + U);
-        compute_stage(sa, q);
-        load_stage(sa, q + 2 * U);
-        compute_stage(sb, q + U);
-      }
-      if (st + 1 < nst) {
-        load_stage(sb, q + U);
-        compute_stage(sa, q);
-        compute_stage(sb, q + U);
-      } else {
-        compute_stage(sa, q);
-      }
-    } else if (FMT == DT_BF16 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
+    if constexpr (FMT == DT_BF16 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
       // bf16 weights, prepared bf16 activation fragments: both loaded per
       // stage of U k blocks (tile j, k block kb: 1 KiB of weights; m-tile mt:
       // 1 KiB of activations).
@@ -647,7 +693,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
     }
   }
   if (!staged) stage_activations();  // inactive waves still join the barrier
-  if (AMODE == A_GLOBAL_I8 && lane >= 32) {
+  if ((AMODE == A_GLOBAL_I8 || AMODE == A_LDS_I8) && lane >= 32) {
     // rows 8..15 carry the residual codes (scale 2^e / 256)
 #pragma unroll
     for (int j = 0; j < TPW; ++j) acc[0][j] *= (1.f / 256.f);
@@ -717,8 +763,12 @@ __global__ __launch_bounds__(256) void k_gemv_f32(GemvArgs a) {
 inline size_t gemv_lds_bytes(const GemvPlan& p) {
   if (p.amode == A_ROWS_BF) return (size_t)p.MT * p.ksteps_per_split * 64 * 16;
   if (p.amode == A_ROWS_I8) return (size_t)p.ksteps_per_split * 512 + 256;
+  if (p.amode == A_GLOBAL_I8) return (size_t)p.ksteps_per_split * 520;  // the A_LDS_I8 copy
   return 0;
 }
+
+// int8 fragments staged in LDS when a workgroup's k range fits 32 KiB
+inline bool gemv_lds_i8(const GemvPlan& p) { return p.ksteps_per_split * 520 <= 32768; }
 
 template <int FMT, int MT, int TPW, int MODE>
 hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
@@ -731,7 +781,10 @@ hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
   } else if (FMT == DT_Q8_0 && MT == 1 && MODE != GEMV_MARKOV && p.amode == A_ROWS_I8) {
     hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_ROWS_I8>), grid, block, lds, st, a);
   } else if (FMT == DT_Q8_0 && MT == 1 && MODE != GEMV_MARKOV && p.amode == A_GLOBAL_I8) {
-    hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_GLOBAL_I8>), grid, block, 0, st, a);
+    if (gemv_lds_i8(p))
+      hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_LDS_I8>), grid, block, lds, st, a);
+    else
+      hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_GLOBAL_I8>), grid, block, 0, st, a);
   } else if (p.amode == A_GLOBAL) {
     hipLaunchKernelGGL((k_gemv_bf<FMT, MT, TPW, MODE, A_GLOBAL>), grid, block, 0, st, a);
   } else {
