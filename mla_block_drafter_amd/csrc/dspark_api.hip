@@ -559,6 +559,7 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
     a.DQ = P.DQ;
     a.C = P.C;
     a.slots = P.slots;
+    a.len1 = P.n_seq == 1 ? (int)P.total_ctx : -1;  // the contract: kv_offsets = {0, total_ctx}
     a.tau = m.tau;
     a.fd_uv = P.f_uv.fd;
     if (P.kv_f32) {
@@ -739,7 +740,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   const dspark_config& c = m->c;
   if (in->n_seq < 1) return fail(DSPARK_EINVAL, "n_seq < 1");
   if (in->n_seq > 16) return fail(DSPARK_EUNSUPPORTED, "n_seq > 16");
-  if (in->total_ctx < 0) return fail(DSPARK_EINVAL, "total_ctx < 0");
+  if (in->total_ctx < 0 || in->total_ctx > (1ll << 30)) return fail(DSPARK_EINVAL, "total_ctx out of range");
   if (!in->captured || !in->kv || !in->kv_offsets || !in->prev_token || !out->tokens || !out->conf)
     return fail(DSPARK_EINVAL, "a required pointer is NULL");
   if (in->act_dtype != DSPARK_DT_F32 && in->act_dtype != DSPARK_DT_BF16)
@@ -911,7 +912,7 @@ int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_
   if (n_seq < 1) return fail(DSPARK_EINVAL, "n_seq < 1");
   if (!x_in || !x_out || !kv_offsets || (!kv && total_ctx > 0)) return fail(DSPARK_EINVAL, "a required pointer is NULL");
   if (kv_dtype != DSPARK_DT_F32 && kv_dtype != DSPARK_DT_BF16) return fail(DSPARK_EINVAL, "bad kv_dtype");
-  if (total_ctx < 0) return fail(DSPARK_EINVAL, "total_ctx < 0");
+  if (total_ctx < 0 || total_ctx > (1ll << 30)) return fail(DSPARK_EINVAL, "total_ctx out of range");
   const bool kv_f32 = kv_dtype == DSPARK_DT_F32;
   Ctx C;
   C.m = m;

@@ -34,6 +34,15 @@ constexpr int MAX_COMBINE_SLOTS = 4096;
 
 __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s, int& p, int& len,
                                             int& off, int& J) {
+  if (a.len1 >= 0) {  // one sequence: no memory round trip
+    s = 0;
+    p = slot;
+    off = 0;
+    len = a.len1;
+    J = len + a.block;
+    if (slot >= (J + a.C - 1) / a.C) s = -1;
+    return;
+  }
   int base = 0;
   for (s = 0; s < a.n_seq; ++s) {
     off = a.offs[s];
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
     const int J = a.offs[t + 1] - a.offs[t] + a.block;
     base += (J + a.C - 1) / a.C;
   }
-  const int J = a.offs[s + 1] - a.offs[s] + a.block;
+  const int J = (a.len1 >= 0 ? a.len1 : a.offs[s + 1] - a.offs[s]) + a.block;
   const int ns = (J + a.C - 1) / a.C;
   const float* ml = a.ml_part + ((long long)row * a.slots + base) * 2;
   float mx = -INFINITY;

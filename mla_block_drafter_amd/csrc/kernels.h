@@ -90,6 +90,7 @@ struct AttnArgs {
   int n_seq, block, nh, rows, rows_pad, latent, r, DQ;
   int C;                  // keys per split (multiple of 32)
   int slots;              // slot bound (grid.y)
+  int len1;               // n_seq == 1: the cache length (== offs[1]), so no lookup; else -1
   float tau;
   uint16_t* o_part;       // [rows_pad][slots][r] fp16: each slot's O / l
   float* ml_part;         // [rows_pad][slots][2]: each slot's (m, l)
