@@ -562,19 +562,33 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
     a.len1 = P.n_seq == 1 ? (int)P.total_ctx : -1;  // the contract: kv_offsets = {0, total_ctx}
     a.tau = m.tau;
     a.fd_uv = P.f_uv.fd;
+    GemvArgs g = gemv_base(L.uv, P.p_uv, P.f_uv, M);
+    g.fd = P.f_o.fd;
+    bool fused = false;
     if (P.kv_f32) {
       HIPCHK(launch_attn_f32(a, C.st));
     } else {
       a.o_part = (uint16_t*)(C.ws + P.opart);
       a.ml_part = (float*)(C.ws + P.mlpart);
       HIPCHK(launch_attn_bf16(a, C.st));
-      HIPCHK(launch_attn_combine(a, C.st));
+      if (a.len1 >= 0 && uv_combine_supported(g, P.n_seq, P.slots)) {
+        UvCombineArgs u{};  // combine fused with the un-absorb GEMM
+        u.g = g;
+        u.o_part = a.o_part;
+        u.ml_part = a.ml_part;
+        u.slots = P.slots;
+        u.C = P.C;
+        u.block = c.block;
+        u.nh = c.n_heads;
+        u.r = c.kv_lora;
+        u.len1 = a.len1;
+        HIPCHK(launch_uv_combine(u, C.st));
+        fused = true;
+      } else {
+        HIPCHK(launch_attn_combine(a, C.st));
+      }
     }
-  }
-  {
-    GemvArgs a = gemv_base(L.uv, P.p_uv, P.f_uv, M);
-    a.fd = P.f_o.fd;
-    HIPCHK(launch_gemv(a, P.p_uv, GEMV_FRAG, C.st));
+    if (!fused) HIPCHK(launch_gemv(g, P.p_uv, GEMV_FRAG, C.st));
   }
   HIPCHK(run_gemv(L.o, P.p_o, P.f_o, M, C.part(), C.st));
   return DSPARK_OK;

@@ -97,6 +97,19 @@ struct AttnArgs {
   FragDesc fd_uv;         // output fragments (un-absorb input, grouped by head)
 };
 
+// Attention combine fused with the un-absorb GEMM (one sequence, M <= 8,
+// at most UVC_MAX_SLOTS slots).
+constexpr int UVC_MAX_SLOTS = 256;
+struct UvCombineArgs {
+  GemvArgs g;               // W_UV grouped by head, M, fd = o_proj fragments, hilo
+  const uint16_t* o_part;   // attention partials [rows_pad][slots][r] fp16 (O / l)
+  const float* ml_part;     // [rows_pad][slots][2] (m, l)
+  int slots, C, block, nh, r;
+  int len1;                 // the sequence's cache length
+};
+bool uv_combine_supported(const GemvArgs& g, int n_seq, int slots);
+hipError_t launch_uv_combine(const UvCombineArgs& a, hipStream_t st);
+
 bool attn_bf16_supported(int DQ, int r);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);
