@@ -129,8 +129,8 @@ def copy_probe_gbs(torch) -> float:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -183,21 +183,28 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # the timed passes: back to back, nothing else in the stream
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record()
+    for k in range(K):
+        run()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_begin.elapsed_time(t_end) / K
+    # per-pass spread and per-stage times, from a second set of passes with
+    # events between them (the events themselves cost a little)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * D.N_STAGES)] for _ in range(K)]
     step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     for row in evs:
         for e in row:
             e.record()
-    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_begin.record()
     for k in range(K):
         step_ev[k].record()
         run(evs[k])
     step_ev[K].record()
-    t_end.record()
     torch.cuda.synchronize()
-    ms_step = t_begin.elapsed_time(t_end) / K
     per_step = np.array([step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(K)])
     stage_ms = np.array([[evs[k][2 * s].elapsed_time(evs[k][2 * s + 1]) for s in range(D.N_STAGES)]
                          for k in range(K)]).mean(axis=0)
