@@ -6,7 +6,7 @@ Markov rollout, confidence) over one 7-token block of the full-size Q8_0
 workload at context 8192 (seeded synthetic weights ~N(0, 0.02) and inputs),
 with every input already resident in HBM.  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 3]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 3]
 
 value = draft-pass latency in microseconds per 7-token block (lower is
 better); the JSON also carries the achieved algorithmic HBM bandwidth of the

@@ -168,16 +168,88 @@ __device__ __forceinline__ void frag_put(const FragDesc& fd, int g, int m, int k
 // hi, lo in [-127, 127] and e the smallest exponent with max |v| <= 127 * 2^e
 // over the block; lane q * 16 + m holds the hi codes of k = 8 q .. 8 q + 7,
 // lane q * 16 + 8 + m the lo codes.  bm = max |v| over the block.
-__device__ __forceinline__ void frag_put_i8(const FragDesc& fd, int g, int m, int k, float v, float bm) {
+__device__ __forceinline__ int frag_i8_exp(float bm) {
   int e = 0;
   if (bm > 0.f) frexpf(bm * (1.f / 127.f), &e);
+  return e;
+}
+__device__ __forceinline__ void frag_i8_codes(float v, int e, int& hi, int& lo) {
   const float qh = fminf(fmaxf(rintf(ldexpf(v, -e)), -127.f), 127.f);
   const float ql = fminf(fmaxf(rintf(ldexpf(v - ldexpf(qh, e), 8 - e)), -127.f), 127.f);
+  hi = (int)qh;
+  lo = (int)ql;
+}
+__device__ __forceinline__ void frag_put_i8(const FragDesc& fd, int g, int m, int k, float v, float bm) {
+  const int e = frag_i8_exp(bm);
+  int qh, ql;
+  frag_i8_codes(v, e, qh, ql);
   const int kb = k >> 5, q = (k >> 3) & 3, i = k & 7;
   unsigned char* p = (unsigned char*)fd.ptr + (long long)g * fd.gstride;
-  p[((long long)kb * 64 + q * 16 + m) * 8 + i] = (unsigned char)(int)qh;
-  p[((long long)kb * 64 + q * 16 + 8 + m) * 8 + i] = (unsigned char)(int)ql;
+  p[((long long)kb * 64 + q * 16 + m) * 8 + i] = (unsigned char)qh;
+  p[((long long)kb * 64 + q * 16 + 8 + m) * 8 + i] = (unsigned char)ql;
   if ((k & 31) == 0) p[(long long)fd.KB * 512 + kb * 8 + m] = (unsigned char)(signed char)e;
+}
+// The same codes for eight consecutive columns k0 .. k0 + 7 of row m (k0 a
+// multiple of 8), written as one 8-byte word per code row; e is the block's
+// exponent, written by the thread that holds the block's first column.
+__device__ __forceinline__ void frag_put_i8_x8(const FragDesc& fd, int g, int m, int k0, const float (&v)[8], int e) {
+  uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int qh, ql;
+    frag_i8_codes(v[i], e, qh, ql);
+    hw[i >> 2] |= ((uint32_t)qh & 0xFFu) << (8 * (i & 3));
+    lw[i >> 2] |= ((uint32_t)ql & 0xFFu) << (8 * (i & 3));
+  }
+  const int kb = k0 >> 5, q = (k0 >> 3) & 3;
+  unsigned char* p = (unsigned char*)fd.ptr + (long long)g * fd.gstride;
+  *(u32x2*)(p + ((long long)kb * 64 + q * 16 + m) * 8) = u32x2{hw[0], hw[1]};
+  *(u32x2*)(p + ((long long)kb * 64 + q * 16 + 8 + m) * 8) = u32x2{lw[0], lw[1]};
+  if (q == 0) p[(long long)fd.KB * 512 + kb * 8 + m] = (unsigned char)(signed char)e;
+}
+
+// ------------------------------------------------------------- reductions --
+// Cross-lane reductions without the LDS crossbar (a ds_bpermute per step,
+// each followed by a wait on its result).  Inside each 16-lane DPP row, four
+// DPP moves pair lane i with i ^ 1, i ^ 2 (quad permutes), 7 - i (half-row
+// mirror) and 15 - i (row mirror); each step combines a lane with a partner
+// that holds the other half of the lanes reduced so far, so after the four
+// steps every lane holds the row total, bit-identical across the row (the
+// operations are commutative).  Row totals are then read with v_readlane
+// from lanes 0, 16, 32 and 48.  Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<DPP_XOR1>(v);
+  v += dpp_mov<DPP_XOR2>(v);
+  v += dpp_mov<DPP_HALF_MIRROR>(v);
+  return v + dpp_mov<DPP_MIRROR>(v);
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_mov<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_mov<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_mov<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+// Maximum over each 32-lane half of the wave.
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = row16_max(v);
+  const float h0 = fmaxf(lane_value(v, 0), lane_value(v, 16)), h1 = fmaxf(lane_value(v, 32), lane_value(v, 48));
+  return (threadIdx.x & 32) ? h1 : h0;
 }
 
 // Wave-cooperative write: every lane of the wave calls it, lane L holding
@@ -185,25 +257,11 @@ __device__ __forceinline__ void frag_put_i8(const FragDesc& fd, int g, int m, in
 // one 32-block); `valid` masks columns outside the matrix.
 __device__ __forceinline__ void frag_put_wave(const FragDesc& fd, int g, int m, int k, float v, bool valid) {
   if (fd.i8) {
-    float bm = valid ? fabsf(v) : 0.f;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
+    const float bm = half_wave_max(valid ? fabsf(v) : 0.f);
     if (valid) frag_put_i8(fd, g, m, k, v, bm);
   } else if (valid) {
     frag_put(fd, g, m, k, v);
   }
-}
-
-// ------------------------------------------------------------- reductions --
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
 }
 
 // Sum over a 256-thread block; `red` is __shared__ float[4].

@@ -63,7 +63,8 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
 
 // Row scales of this lane's output rows 16 mt + 4 (lane >> 4) + r, by the
 // whole wave: the chunk sums of all 16 rows of an m-tile are loaded together
-// (one memory round trip) and reduced in a fixed butterfly order.
+// (one memory round trip) and each is reduced by wave_sum (the same order,
+// hence the same bits, as every other consumer of these chunk sums).
 template <int MT>
 __device__ __forceinline__ void gemv_row_scales(const RowScale& s, int M, int lane, float (&rsv)[MT][4]) {
 #pragma unroll
@@ -76,9 +77,7 @@ __device__ __forceinline__ void gemv_row_scales(const RowScale& s, int M, int la
       t[j] = m < M ? (lane < s.nch ? p[lane] : 0.f) + (lane + 64 < s.nch ? p[lane + 64] : 0.f) : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) t[j] += __shfl_xor(t[j], o, 64);
+    for (int j = 0; j < 16; ++j) t[j] = wave_sum(t[j]);
     const int q = lane >> 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -102,6 +101,16 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
     // each 16-lane group (one row per group and r after the hi/lo sum).
     float rsv[1][4] = {{1.f, 1.f, 1.f, 1.f}};
     if (a.rs.ssq) gemv_row_scales<1>(a.rs, a.M, lane, rsv);
+    // FP8 column scales first: a load after the first store would make the
+    // following wait cover the stores too
+    float fsv[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) fsv[j] = 1.f;
+    if (a.w.fmt == DT_FP8 && active) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+        fsv[j] = ((const float*)a.w.scales)[(long long)min(t0 + j, g * TG + TG - 1) * 16 + (lane & 15)];
+    }
     f32x4 v[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -125,13 +134,10 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
           const int cig = (t % TG) * 16 + (lane & 15);
           ok[h] = active && cig < G && lane < 32 && m < a.M;
           col[h] = (long long)g * G + cig;
-          float fs = 1.f;
-          if (a.w.fmt == DT_FP8 && ok[h]) fs = ((const float*)a.w.scales)[(long long)t * 16 + (lane & 15)];
-          x[h] = v[jp + h][r] * rsm * fs;
+          x[h] = v[jp + h][r] * rsm * fsv[jp + h];
           if (ok[h]) bm = fmaxf(bm, fabsf(x[h]));
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 64));
+        bm = row16_max(bm);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           if (ok[h]) frag_put_i8(a.fd, 0, m, (int)col[h], x[h], bm);
@@ -145,14 +151,22 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
 #pragma unroll
       for (int r = 0; r < 4; ++r) rsv[mt][r] = 1.f;
     if (a.rs.ssq) gemv_row_scales<MT>(a.rs, a.M, lane, rsv);
+    // FP8 column scales before the first store (see the fragment branch)
+    float fsv[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) fsv[j] = 1.f;
+    if (a.w.fmt == DT_FP8 && active) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+        fsv[j] = ((const float*)a.w.scales)[(long long)min(t0 + j, g * TG + TG - 1) * 16 + (lane & 15)];
+    }
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int t = t0 + j;
       const int cig = (t % TG) * 16 + (lane & 15);
       const bool colok = active && cig < G;
       const long long col = (long long)g * G + cig;
-      float fs = 1.0f;
-      if (a.w.fmt == DT_FP8 && colok) fs = ((const float*)a.w.scales)[(long long)t * 16 + (lane & 15)];
+      const float fs = fsv[j];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 v = acc[mt][j];

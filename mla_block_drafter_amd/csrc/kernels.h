@@ -29,10 +29,8 @@ struct RowScale {
 // every lane returns the same bits.
 __device__ __forceinline__ float chunk_sum_wave(const float* row, int nch) {
   const int lane = threadIdx.x & 63;
-  float t = (lane < nch ? row[lane] : 0.f) + (lane + 64 < nch ? row[lane + 64] : 0.f);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
-  return t;
+  const float t = (lane < nch ? row[lane] : 0.f) + (lane + 64 < nch ? row[lane + 64] : 0.f);
+  return wave_sum(t);
 }
 
 __device__ __forceinline__ float row_scale_wave(const RowScale& s, int m) {
