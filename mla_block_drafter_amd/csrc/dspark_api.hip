@@ -531,17 +531,19 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
     a.q = C.ws + P.q;
     a.q_f32 = P.kv_f32;
     a.rope = (const float*)(C.ws + P.rope);
-    HIPCHK(launch_post_qb(a, C.st));
-  }
-  {
-    GemvArgs a = gemv_base(L.uk, P.p_uk, P.f_uk, M);
-    a.q = C.ws + P.q;
-    a.q_f32 = P.kv_f32;
-    a.DQ = P.DQ;
-    a.rows_pad = P.rows_pad;
-    a.nh = c.n_heads;
-    a.block = c.block;
-    HIPCHK(launch_gemv(a, P.p_uk, GEMV_QLAT, C.st));
+    GemvArgs u = gemv_base(L.uk, P.p_uk, P.f_uk, M);
+    u.q = C.ws + P.q;
+    u.q_f32 = P.kv_f32;
+    u.DQ = P.DQ;
+    u.rows_pad = P.rows_pad;
+    u.nh = c.n_heads;
+    u.block = c.block;
+    if (qb_absorb_supported(u, a)) {
+      HIPCHK(launch_qb_absorb(QbAbsorbArgs{u, a}, C.st));  // post fused with the absorb GEMM
+    } else {
+      HIPCHK(launch_post_qb(a, C.st));
+      HIPCHK(launch_gemv(u, P.p_uk, GEMV_QLAT, C.st));
+    }
   }
   {
     AttnArgs a{};

@@ -27,32 +27,41 @@ __device__ __forceinline__ float shared_row_scale(const RowScale& s, int m, floa
 }
 
 // Sums of the split-K partials of elements (m, c[u]), u < N, columns with
-// c[u] < 0 skipped: eight splits per column are loaded together (every load
-// of a round, all N columns, is in flight at once; the loads are
-// unconditional, at clamped in-range addresses, so none waits on a branch),
-// each column summed in a fixed order, hence deterministic.
-template <int N>
-__device__ __forceinline__ void part_sum_n(const PartIn& p, int m, const int (&c)[N], float (&out)[N]) {
+// c[u] < 0 skipped: R splits per column are loaded together (every load of a
+// round, all N columns, is in flight at once; the loads are unconditional, at
+// clamped in-range addresses, so none waits on a branch), each column summed
+// in a fixed order, hence deterministic.
+template <int N, int R>
+__device__ __forceinline__ void part_sum_r(const PartIn& p, int m, const int (&c)[N], float (&out)[N]) {
   const float* q = p.part + (long long)m * p.ld;
-  float v[N][8];
+  float v[N][R];
 #pragma unroll
   for (int n = 0; n < N; ++n)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[n][u] = 0.f;
-  for (int s = 0; s < p.S; s += 8) {
-    float x[N][8];
+    for (int u = 0; u < R; ++u) v[n][u] = 0.f;
+  for (int s = 0; s < p.S; s += R) {
+    float x[N][R];
 #pragma unroll
     for (int n = 0; n < N; ++n)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[n][u] = q[(long long)min(s + u, p.S - 1) * p.ss + max(c[n], 0)];
+      for (int u = 0; u < R; ++u) x[n][u] = q[(long long)min(s + u, p.S - 1) * p.ss + max(c[n], 0)];
 #pragma unroll
     for (int n = 0; n < N; ++n)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[n][u] += (c[n] >= 0 && s + u < p.S) ? x[n][u] : 0.f;
+      for (int u = 0; u < R; ++u) v[n][u] += (c[n] >= 0 && s + u < p.S) ? x[n][u] : 0.f;
   }
 #pragma unroll
-  for (int n = 0; n < N; ++n)
-    out[n] = ((v[n][0] + v[n][1]) + (v[n][2] + v[n][3])) + ((v[n][4] + v[n][5]) + (v[n][6] + v[n][7]));
+  for (int n = 0; n < N; ++n) {
+#pragma unroll
+    for (int w = R / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int u = 0; u < w; ++u) v[n][u] += v[n][u + w];
+    out[n] = v[n][0];
+  }
+}
+template <int N>
+__device__ __forceinline__ void part_sum_n(const PartIn& p, int m, const int (&c)[N], float (&out)[N]) {
+  part_sum_r<N, 8>(p, m, c, out);
 }
 
 __device__ __forceinline__ float part_sum(const PartIn& p, int m, int c) {

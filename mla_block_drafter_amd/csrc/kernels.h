@@ -173,6 +173,15 @@ struct QbPost {
 };
 hipError_t launch_post_qb(const QbPost& a, hipStream_t st);
 
+// q_b post fused with the W_UK absorb GEMM (M <= 8, bf16 W_UK, qk_nope 128):
+// g is the absorb GEMM (query-buffer output), qb the post (fd_uk unused).
+struct QbAbsorbArgs {
+  GemvArgs g;
+  QbPost qb;
+};
+bool qb_absorb_supported(const GemvArgs& g, const QbPost& p);
+hipError_t launch_qb_absorb(const QbAbsorbArgs& a, hipStream_t st);
+
 struct SwigluPost {
   PartIn p; RowScale rs;
   int M, inter;
