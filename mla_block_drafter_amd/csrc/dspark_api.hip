@@ -850,7 +850,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   HIPCHK(run_gemv(m->lm, P.p_lm, P.f_lm, M, z, C.st, C.rs(P.ssq_b, c.hidden)));
   HIPCHK(mark(2 * DSPARK_STAGE_LM_HEAD + 1));
   HIPCHK(mark(2 * DSPARK_STAGE_MARKOV));
-  const bool rollout = m->w2.pm.fmt == DT_BF16 && markov_rollout_supported(m->w2.pm.KB, in->n_seq);
+  const bool rollout = m->w2.pm.fmt == DT_BF16 && markov_rollout_supported(m->w2.pm.KB, in->n_seq, c.vocab);
   if (rollout) {
     MarkovArgs a{};
     a.w2 = m->w2.pm.codes;

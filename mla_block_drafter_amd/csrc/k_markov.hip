@@ -43,14 +43,32 @@ constexpr unsigned MK_SPIN_LIMIT = 1u << 22;
 
 __device__ __forceinline__ u32x4 mk_ntload(const u32x4* p) { return __builtin_nontemporal_load(p); }
 
-__device__ __forceinline__ unsigned long long mk_shfl_xor(unsigned long long v, int o) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  lo = __shfl_xor(lo, o, 64);
-  hi = __shfl_xor(hi, o, 64);
+__device__ __forceinline__ unsigned long long mk_max(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+// Maximum of 64-bit keys over each 16-lane DPP row (every lane of the row
+// gets it): the DPP moves of common.h's row reductions, applied to both
+// halves of the key.  Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long mk_dpp_u64(unsigned long long v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ unsigned long long mk_row16_max(unsigned long long v) {
+  v = mk_max(v, mk_dpp_u64<DPP_XOR1>(v));
+  v = mk_max(v, mk_dpp_u64<DPP_XOR2>(v));
+  v = mk_max(v, mk_dpp_u64<DPP_HALF_MIRROR>(v));
+  return mk_max(v, mk_dpp_u64<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ unsigned long long mk_lane_u64(unsigned long long v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
   return ((unsigned long long)hi << 32) | lo;
 }
-
-__device__ __forceinline__ unsigned long long mk_max(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+__device__ __forceinline__ unsigned long long mk_wave_max(unsigned long long v) {
+  v = mk_row16_max(v);
+  return mk_max(mk_max(mk_lane_u64(v, 0), mk_lane_u64(v, 16)), mk_max(mk_lane_u64(v, 32), mk_lane_u64(v, 48)));
+}
 
 // Argmax keys of position `pos` for every sequence (into tok[m]), polling the
 // slots of all workgroups until each is written.  All threads take part; wave
@@ -68,8 +86,7 @@ __device__ void mk_poll(const MarkovArgs& a, int pos, int nwg, unsigned long lon
         missing |= x == 0;
         v = mk_max(v, x);
       }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) v = mk_max(v, mk_shfl_xor(v, o));
+      v = mk_wave_max(v);
       if (lane == 0) red[q] = v;
     }
     if (!__syncthreads_or(missing)) {
@@ -87,30 +104,30 @@ __device__ void mk_poll(const MarkovArgs& a, int pos, int nwg, unsigned long lon
   }
 }
 
-// This step's lm_head logits for the wave's outputs, straight to LDS (they
-// do not depend on the predecessor, so they arrive while it is resolved).
-__device__ __forceinline__ void mk_fetch_z(const MarkovArgs& a, int step, int t0, int T, int lane, float* dst) {
-#pragma unroll 1
-  for (int jr = 0; jr < MK_TPW * 4; ++jr) {
-    const int j = jr >> 2, r = jr & 3;
-    const int col = (t0 + j) * 16 + (lane & 15);
-    const int mm = (lane >> 4) * 4 + r;
-    if (t0 + j < T && col < a.vocab && mm < a.M)
-      __builtin_amdgcn_global_load_lds(a.z + ((long long)mm * a.block + step) * a.vocab + col, dst + jr * 64, 4, 0, 0);
-  }
+// This step's lm_head logits of the wave's MK_TPW * 16 columns, straight to
+// LDS as [sequence][column] (they do not depend on the predecessor, so they
+// arrive while it is resolved): one 16-byte copy per lane and sequence.
+constexpr int MK_ZCOLS = MK_TPW * 16;
+static_assert(MK_ZCOLS % 4 == 0 && MK_ZCOLS / 4 <= 64, "one copy per sequence");
+__device__ __forceinline__ void mk_fetch_z(const MarkovArgs& a, int step, int t0, int lane, float* dst) {
+  const int c = t0 * 16 + 4 * lane;  // first of this lane's four columns
+  const bool ok = 4 * lane < MK_ZCOLS && c + 4 <= a.vocab;
+  for (int mm = 0; mm < a.M; ++mm)
+    if (ok)
+      __builtin_amdgcn_global_load_lds(a.z + ((long long)mm * a.block + step) * a.vocab + c, dst + mm * MK_ZCOLS, 16, 0, 0);
 }
 
 template <int KB>
 __global__ __launch_bounds__(MK_THREADS, 1) void k_markov_rollout(MarkovArgs a) {
   __shared__ unsigned long long red[MK_WAVES * 16];
-  __shared__ float zl[MK_WAVES][MK_TPW * 4][64];  // lm_head logits of the wave's outputs, current step
+  __shared__ __attribute__((aligned(16))) float zl[MK_WAVES][16][MK_ZCOLS];  // lm_head logits [sequence][column], current step
   __shared__ int tok[16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.tiles;
   const int nwg = gridDim.x;
   const int t0 = (blockIdx.x * MK_WAVES + wave) * MK_TPW;
 
-  mk_fetch_z(a, 0, t0, T, lane, &zl[wave][0][0]);
+  mk_fetch_z(a, 0, t0, lane, &zl[wave][0][0]);
   // this wave's W2 tiles, resident for the whole block
   u32x4 w[MK_TPW][KB];
   {
@@ -143,38 +160,54 @@ __global__ __launch_bounds__(MK_THREADS, 1) void k_markov_rollout(MarkovArgs a) 
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) A[kb] = ok ? *(const bf16x8*)(src + 32 * kb) : bf16x8{};
     }
+    // tiles in pairs: two independent MFMA chains, and both tiles' logits
+    // requested before them; rows r >= M hold no sequence in any lane group
+    const int mg = (lane >> 4) * 4;  // first sequence of this lane's output rows
     unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+    static_assert(MK_TPW % 2 == 0, "tile pairs");
 #pragma unroll
-    for (int j = 0; j < MK_TPW; ++j) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MK_TPW; j += 2) {
+      float zv[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          zv[h][r] = r < a.M ? zl[wave][min(mg + r, 15)][(j + h) * 16 + (lane & 15)] : 0.f;
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kb], __builtin_bit_cast(bf16x8, w[j][kb]), acc, 0, 0, 0);
-      const int col = (t0 + j) * 16 + (lane & 15);
-      if (t0 + j < T && col < a.vocab) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kb], __builtin_bit_cast(bf16x8, w[j + h][kb]), acc[h], 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = (t0 + j + h) * 16 + (lane & 15);
+        const bool colok = t0 + j + h < T && col < a.vocab;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int mm = (lane >> 4) * 4 + r;  // sequence of output row r
-          if (mm >= a.M) continue;
-          const long long row = (long long)mm * a.block + step;
-          const float v = acc[r] + zl[wave][j * 4 + r][lane];
-          if (a.logits) a.logits[row * a.vocab + col] = v;
-          best[r] = mk_max(best[r], argmax_key(v, (uint32_t)col));
+          if (r >= a.M) break;
+          const int mm = mg + r;  // sequence of output row r
+          const float v = acc[h][r] + zv[h][r];
+          const bool ok = colok && mm < a.M;
+          if (a.logits && ok) a.logits[((long long)mm * a.block + step) * a.vocab + col] = v;
+          best[r] = ok ? mk_max(best[r], argmax_key(v, (uint32_t)col)) : best[r];
         }
       }
     }
     // argmax per sequence over the workgroup: the 16 columns of each lane
-    // group, then the waves; then this workgroup's slot
+    // group (rows r >= M hold no sequence in any group), then the waves;
+    // then this workgroup's slot
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) best[r] = mk_max(best[r], mk_shfl_xor(best[r], o));
+    for (int r = 0; r < 4; ++r) {
+      if (r >= a.M) break;
+      best[r] = mk_row16_max(best[r]);
+    }
     if ((lane & 15) == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave * 16 + (lane >> 4) * 4 + r] = best[r];
     }
     __syncthreads();  // also: every wave is done with zl of this step
-    if (step + 1 < a.block) mk_fetch_z(a, step + 1, t0, T, lane, &zl[wave][0][0]);
+    if (step + 1 < a.block) mk_fetch_z(a, step + 1, t0, lane, &zl[wave][0][0]);
     if (threadIdx.x < 16 && (int)threadIdx.x < a.M) {
       unsigned long long k = red[threadIdx.x];
 #pragma unroll
@@ -208,9 +241,12 @@ hipError_t launch_rollout(const MarkovArgs& a, hipStream_t st) {
 
 int markov_rollout_wgs(int tiles) { return ((tiles + MK_TPW - 1) / MK_TPW + MK_WAVES - 1) / MK_WAVES; }
 
-bool markov_rollout_supported(int KB, int M) { return (KB == 8 || KB == 2) && M >= 1 && M <= 16; }
+bool markov_rollout_supported(int KB, int M, int vocab) {
+  return (KB == 8 || KB == 2) && M >= 1 && M <= 16 && vocab % 4 == 0;  // logits copied four columns at a time
+}
 
 hipError_t launch_markov_rollout(const MarkovArgs& a, int KB, hipStream_t st) {
+  if (!markov_rollout_supported(KB, a.M, a.vocab)) return hipErrorInvalidValue;
   if (KB == 8) return launch_rollout<8>(a, st);
   if (KB == 2) return launch_rollout<2>(a, st);
   return hipErrorInvalidValue;

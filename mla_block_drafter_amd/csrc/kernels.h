@@ -204,7 +204,7 @@ struct MarkovArgs {
   unsigned* err;              // error flag, zeroed
 };
 int markov_rollout_wgs(int tiles);
-bool markov_rollout_supported(int KB, int M);
+bool markov_rollout_supported(int KB, int M, int vocab);
 hipError_t launch_markov_rollout(const MarkovArgs& a, int KB, hipStream_t st);
 
 struct MarkovFinalArgs {
