@@ -781,7 +781,8 @@ inline size_t gemv_lds_bytes(const GemvPlan& p) {
   return 0;
 }
 
-// int8 fragments staged in LDS when a workgroup's k range fits 32 KiB
+// int8 fragments staged in LDS when a workgroup's k range fits 32 KiB (the
+// fc GEMM's 64 KiB k range measured slower staged than read with the weights)
 inline bool gemv_lds_i8(const GemvPlan& p) { return p.ksteps_per_split * 520 <= 32768; }
 
 template <int FMT, int MT, int TPW, int MODE>

@@ -160,37 +160,23 @@ __global__ __launch_bounds__(MK_THREADS, 1) void k_markov_rollout(MarkovArgs a) 
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) A[kb] = ok ? *(const bf16x8*)(src + 32 * kb) : bf16x8{};
     }
-    // tiles in pairs: two independent MFMA chains, and both tiles' logits
-    // requested before them; rows r >= M hold no sequence in any lane group
-    const int mg = (lane >> 4) * 4;  // first sequence of this lane's output rows
     unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
-    static_assert(MK_TPW % 2 == 0, "tile pairs");
 #pragma unroll
-    for (int j = 0; j < MK_TPW; j += 2) {
-      float zv[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          zv[h][r] = r < a.M ? zl[wave][min(mg + r, 15)][(j + h) * 16 + (lane & 15)] : 0.f;
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int j = 0; j < MK_TPW; ++j) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kb], __builtin_bit_cast(bf16x8, w[j + h][kb]), acc[h], 0, 0, 0);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int col = (t0 + j + h) * 16 + (lane & 15);
-        const bool colok = t0 + j + h < T && col < a.vocab;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kb], __builtin_bit_cast(bf16x8, w[j][kb]), acc, 0, 0, 0);
+      const int col = (t0 + j) * 16 + (lane & 15);
+      if (t0 + j < T && col < a.vocab) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (r >= a.M) break;
-          const int mm = mg + r;  // sequence of output row r
-          const float v = acc[h][r] + zv[h][r];
-          const bool ok = colok && mm < a.M;
-          if (a.logits && ok) a.logits[((long long)mm * a.block + step) * a.vocab + col] = v;
-          best[r] = ok ? mk_max(best[r], argmax_key(v, (uint32_t)col)) : best[r];
+          const int mm = (lane >> 4) * 4 + r;  // sequence of output row r
+          if (mm >= a.M) continue;
+          const long long row = (long long)mm * a.block + step;
+          const float v = acc[r] + zl[wave][mm][j * 16 + (lane & 15)];
+          if (a.logits) a.logits[row * a.vocab + col] = v;
+          best[r] = mk_max(best[r], argmax_key(v, (uint32_t)col));
         }
       }
     }
