@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="latent caches as page pools of this many tokens (seeded page placement)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (byte-counter calibration) and exit")
     args = ap.parse_args()
@@ -175,8 +177,16 @@ def main():
     tokens = torch.empty((n, B), dtype=torch.int32, device=dev)
     conf = torch.empty((n, B), dtype=torch.float32, device=dev)
 
+    table = None
+    if args.page_size:
+        pc = gen.paged_layout(inp.caches, inp.kv_offsets, args.page_size, seed=wl.seed)
+        kv = [torch.from_numpy(p.view(np.int16)).to(dev).view(torch.bfloat16) for p in pc.pools]
+        table = torch.from_numpy(pc.table).to(dev)
+        del pc
+
     def run(evs=None):
-        model.draft_block(cap, kv, offs, prev, wl.total_ctx, tokens, conf, ws, stage_events=evs)
+        model.draft_block(cap, kv, offs, prev, wl.total_ctx, tokens, conf, ws, stage_events=evs,
+                          page_size=args.page_size, block_table=table)
 
     for _ in range(args.warmup):
         run()
@@ -265,7 +275,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "n_seq": n, "block": B, "ctx": int(wl.total_ctx // n),
                    "hidden": m.hidden, "layers": m.n_layers, "vocab": m.vocab, "weights": fmt,
-                   "algorithmic_bytes": total_bytes},
+                   "algorithmic_bytes": total_bytes, "kv_layout": f"paged{args.page_size}" if args.page_size else "packed"},
         "hbm_gbs": round(pass_gbs, 1),
         "hbm_frac_of_peak": round(pass_gbs / HBM_PEAK_GBS, 4),
         "hbm_frac_of_copy_probe": round(pass_gbs / copy_gbs, 4),

@@ -152,6 +152,18 @@ typedef struct dspark_block_in {
                                  position i >= 1 uses forced_prev[s][i-1] as its
                                  Markov predecessor instead of the drafted token
                                  (teacher-forced rollout); NULL = free running   */
+  /* Paged latent caches, the layout the draft shares with the target's cache
+     (huggingface.co "Kimi-K3-DSpark-NVFP4", original card, "Model Overview":
+     one 576-element latent per token, so the draft's pages unify with the
+     target's).  page_size == 0: kv[l] is packed as described above.  Else
+     kv[l] is a page pool [n_pages][page_size][kv_lora + qk_rope] (bf16 caches
+     only), the length of sequence s is still kv_offsets[s+1] - kv_offsets[s],
+     and its token j is row j % page_size of page block_table[s][j / page_size]
+     in every layer's pool.  Page indices are not range checked: each page a
+     sequence's length reaches must exist in every pool.                      */
+  int32_t page_size;          /* 0, or a power of two >= 32                     */
+  int32_t max_pages;          /* row stride of block_table (>= 1 when paged)    */
+  const int32_t* block_table; /* device int32 [n_seq][max_pages] when paged     */
 } dspark_block_in;
 
 typedef struct dspark_block_out {

@@ -456,6 +456,9 @@ struct Ctx {
   Plan P;
   unsigned char* ws;
   hipStream_t st;
+  // paged caches (page_log2 >= 0), see dspark_block_in
+  const int32_t* table = nullptr;
+  int page_log2 = -1, max_pages = 0;
   float* part() const { return (float*)(ws + P.part); }
   float* x() const { return (float*)(ws + P.x); }
   float* ssq(long long off) const { return (float*)(ws + off); }
@@ -562,6 +565,9 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
     a.C = P.C;
     a.slots = P.slots;
     a.len1 = P.n_seq == 1 ? (int)P.total_ctx : -1;  // the contract: kv_offsets = {0, total_ctx}
+    a.table = C.table;
+    a.page_log2 = C.page_log2;
+    a.max_pages = C.max_pages;
     a.tau = m.tau;
     a.fd_uv = P.f_uv.fd;
     GemvArgs g = gemv_base(L.uv, P.p_uv, P.f_uv, M);
@@ -766,6 +772,14 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   for (int l = 0; l < c.n_layers; ++l)
     if (!in->kv[l] && in->total_ctx > 0) return fail(DSPARK_EINVAL, "kv[%d] is NULL", l);
   const bool kv_f32 = in->kv_dtype == DSPARK_DT_F32;
+  int page_log2 = -1;
+  if (in->page_size != 0) {
+    const int ps = in->page_size;
+    if (ps < 32 || (ps & (ps - 1))) return fail(DSPARK_EINVAL, "page_size %d: not a power of two >= 32", ps);
+    if (!in->block_table || in->max_pages < 1) return fail(DSPARK_EINVAL, "paged caches need block_table and max_pages");
+    if (kv_f32) return fail(DSPARK_EUNSUPPORTED, "paged caches are bf16 only");
+    page_log2 = __builtin_ctz((unsigned)ps);
+  }
   Ctx C;
   C.m = m;
   make_plan(*m, in->n_seq, in->total_ctx, kv_f32, C.P);
@@ -777,6 +791,9 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   if (rc) return rc;
   C.ws = (unsigned char*)workspace;
   C.st = (hipStream_t)stream;
+  C.table = in->block_table;
+  C.page_log2 = page_log2;
+  C.max_pages = in->max_pages;
   Plan& P = C.P;
   for (Frag* f : {&P.f_fc, &P.f_qkva, &P.f_qb, &P.f_uk, &P.f_uv, &P.f_o, &P.f_gu, &P.f_down, &P.f_lm}) bind_frag(*f, C.ws);
   const int M = P.M;

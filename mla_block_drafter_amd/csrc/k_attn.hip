@@ -105,29 +105,41 @@ struct TileGeom {
 // This wave's share of one key tile: region-A keys wave, wave + 4, ... and
 // region-B load number wave.  Everything but the lane offsets is uniform, so
 // the address selection stays on the scalar unit.
-template <int CA, int CB>
+// trow: the cache row of key kt0 (a tile never crosses a page, so key kt0 + i
+// of the tile is row trow + i in both layouts; PAGED only keeps the two
+// kernels' specializations apart).
+//
+// Paged caches: the cache row of key kt0 (kt0 < len, wave-uniform) of a slot
+// whose first page is pfirst, lane i of pgv holding the slot's page i.
+__device__ __forceinline__ int paged_row(const AttnArgs& a, int kt0, int pfirst, int pgv) {
+  const int i = __builtin_amdgcn_readfirstlane((kt0 >> a.page_log2) - pfirst);  // 0 .. 7
+  const int page = __builtin_amdgcn_readlane(pgv, i);
+  return (page << a.page_log2) + (kt0 & ((1 << a.page_log2) - 1));
+}
+
+template <int CA, int CB, bool PAGED>
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, int lane, int wave, int kt0, int k_end, int s,
-                                           int len, int off, const uint16_t* cache, const uint16_t* bk,
+                                           int len, int trow, const uint16_t* cache, const uint16_t* bk,
                                            const uint16_t* dummy, uint16_t* dst) {
   using G = TileGeom<CA, CB>;
   static_assert(G::NB_A % 4 == 0 && G::NB_B <= 4, "load split over four waves");
   if (kt0 + KT <= min(len, k_end)) {
     // common case: the whole tile is valid cache rows (uniform row pointer)
     const long long ld = a.latent;
-    const uint16_t* src = cache + (off + kt0 + wave) * ld + 8 * lane;
+    const uint16_t* src = cache + (trow + wave) * ld + 8 * lane;
 #pragma unroll
     for (int i = 0; i < G::NB_A / 4; ++i, src += 4 * ld)
       if (CA == 64 || lane < CA) __builtin_amdgcn_global_load_lds(src, dst + (wave + 4 * i) * G::ROW_A, 16, 0, 0);
     if (wave < G::NB_B) {
       const int r = wave * G::KPB + lane / CB, c = CA + ((lane % CB) ^ bswz<CB>(r));
       // chunks past the stored row (query padding, zero) read the dummy row
-      const uint16_t* sb = 8 * c < a.latent ? cache + (off + kt0 + r) * ld + 8 * c : dummy;
+      const uint16_t* sb = 8 * c < a.latent ? cache + (trow + r) * ld + 8 * c : dummy;
       __builtin_amdgcn_global_load_lds(sb, dst + G::SIZE_A + wave * 512, 16, 0, 0);
     }
     return;
   }
   auto row_ptr = [&](int j) {
-    const uint16_t* c = cache + (long long)(off + j) * a.latent;
+    const uint16_t* c = cache + (long long)(trow + j - kt0) * a.latent;
     const uint16_t* k = bk + (long long)(s * a.block + (j - len)) * a.latent;
     const uint16_t* r = j < len ? c : k;
     return j < k_end ? r : dummy;
@@ -209,7 +221,7 @@ __device__ __forceinline__ void lds_wait_pair(u32x2& lo, u32x2& hi) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int NKB, int NDT>
+template <int NKB, int NDT, bool PAGED>
 __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   constexpr int DQ = NKB * 32;
   constexpr int R = NDT * 16;
@@ -238,6 +250,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   const uint16_t* cache = (const uint16_t*)a.cache;
   const uint16_t* bk = (const uint16_t*)a.bkeys;
   const uint16_t* dummy = bk + (long long)s * a.block * a.latent;
+  // paged caches: the page indices of this slot's keys (at most C / 32 = 8),
+  // one per lane of a VGPR, read once here: no memory load may enter the tile
+  // loop, whose LDS waits count on the shared counter (and eight scalar
+  // registers more would spill under this register pressure)
+  const int pfirst = PAGED ? k_begin >> a.page_log2 : 0;
+  int pgv = 0;
+  if (PAGED) {
+    const int32_t* tb = a.table + (long long)s * a.max_pages;
+    pgv = tb[min(pfirst + (lane & 7), a.max_pages - 1)];
+  }
 
   // Q fragments (B operand of S^T = K Q^T): row myrow, dims 32kb + 8 grp.
   bf16x8 qf[NKB];
@@ -280,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 #pragma unroll 1
   for (int i = 0; i < NBUF - 1; ++i)
     if (i < ntiles)
-      issue_tile<CA, CB>(a, lane, wave, k_begin + i * KT, k_end, s, len, off, cache, bk, dummy,
+      issue_tile<CA, CB, PAGED>(a, lane, wave, k_begin + i * KT, k_end, s, len, PAGED ? paged_row(a, k_begin + i * KT, pfirst, pgv) : off + k_begin + i * KT, cache, bk, dummy,
                          k_lds + i * G::BUF);
 
   // One barrier per tile.  Tile t is in LDS once at most the loads of the
@@ -301,7 +323,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (t + NBUF - 1 < ntiles)
-      issue_tile<CA, CB>(a, lane, wave, kt0 + (NBUF - 1) * KT, k_end, s, len, off, cache, bk, dummy,
+      issue_tile<CA, CB, PAGED>(a, lane, wave, kt0 + (NBUF - 1) * KT, k_end, s, len, PAGED ? paged_row(a, kt0 + (NBUF - 1) * KT, pfirst, pgv) : off + kt0 + (NBUF - 1) * KT, cache,
+                         bk, dummy,
                          k_lds + ((t + NBUF - 1) % NBUF) * G::BUF);
     const uint16_t* tb = k_lds + buf * G::BUF;
 
@@ -563,13 +586,21 @@ bool attn_bf16_supported(int DQ, int r) {
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (a.rows_pad % 64 || (long long)(a.rows_pad / 64) * a.slots > INT32_MAX) return hipErrorInvalidValue;
-  dim3 grid((a.rows_pad / 64) * a.slots), block(256);
-  if (a.DQ == 576 && a.r == 512)
-    hipLaunchKernelGGL((k_attn_bf16<18, 32>), grid, block, 0, st, a);
-  else if (a.DQ == 96 && a.r == 64)
-    hipLaunchKernelGGL((k_attn_bf16<3, 4>), grid, block, 0, st, a);
-  else
+  // pages of at least one key tile; a slot's keys span at most 8 pages
+  if (a.page_log2 >= 0 && (a.page_log2 < 5 || a.page_log2 > 24 || !a.table || a.max_pages < 1 ||
+                           a.C % KT || a.C / KT > 8))
     return hipErrorInvalidValue;
+  dim3 grid((a.rows_pad / 64) * a.slots), block(256);
+  const bool paged = a.page_log2 >= 0;
+  if (a.DQ == 576 && a.r == 512) {
+    if (paged) hipLaunchKernelGGL((k_attn_bf16<18, 32, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_bf16<18, 32, false>), grid, block, 0, st, a);
+  } else if (a.DQ == 96 && a.r == 64) {
+    if (paged) hipLaunchKernelGGL((k_attn_bf16<3, 4, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_bf16<3, 4, false>), grid, block, 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

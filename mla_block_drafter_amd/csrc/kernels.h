@@ -89,6 +89,11 @@ struct AttnArgs {
   int C;                  // keys per split (multiple of 32)
   int slots;              // slot bound (grid.y)
   int len1;               // n_seq == 1: the cache length (== offs[1]), so no lookup; else -1
+  // paged caches (page_log2 >= 0): cache = page pool [pages][1 << page_log2][latent];
+  // token j of sequence s in page table[s * max_pages + (j >> page_log2)]
+  const int32_t* table;
+  int page_log2;          // -1: packed rows, sequence s from offs[s]
+  int max_pages;
   float tau;
   uint16_t* o_part;       // [rows_pad][slots][r] fp16: each slot's O / l
   float* ml_part;         // [rows_pad][slots][2]: each slot's (m, l)

@@ -60,7 +60,8 @@ class Weight(C.Structure):
 class BlockIn(C.Structure):
     _fields_ = [("n_seq", C.c_int32), ("act_dtype", C.c_int32), ("kv_dtype", C.c_int32), ("pad_", C.c_int32),
                 ("total_ctx", C.c_int64), ("captured", C.c_void_p), ("kv", C.POINTER(C.c_void_p)),
-                ("kv_offsets", C.c_void_p), ("prev_token", C.c_void_p), ("forced_prev", C.c_void_p)]
+                ("kv_offsets", C.c_void_p), ("prev_token", C.c_void_p), ("forced_prev", C.c_void_p),
+                ("page_size", C.c_int32), ("max_pages", C.c_int32), ("block_table", C.c_void_p)]
 
 
 class BlockOut(C.Structure):
@@ -202,8 +203,10 @@ class Model:
 
     def draft_block(self, captured, kv: Sequence, kv_offsets, prev_token, total_ctx: int, tokens, conf,
                     workspace, logits=None, hidden=None, forced_prev=None, stream=None,
-                    stage_events=None) -> None:
-        """stage_events: optional list of 2*N_STAGES torch.cuda.Event (enable_timing)."""
+                    stage_events=None, page_size: int = 0, block_table=None) -> None:
+        """stage_events: optional list of 2*N_STAGES torch.cuda.Event (enable_timing).
+        page_size > 0: kv holds page pools and block_table (int32 [n_seq][max_pages])
+        maps each sequence's pages."""
         import torch
         n_seq = int(prev_token.shape[0])
         kv_arr = (C.c_void_p * len(kv))(*[t.data_ptr() if t is not None else None for t in kv])
@@ -217,6 +220,10 @@ class Model:
         bi.kv_offsets = kv_offsets.data_ptr()
         bi.prev_token = prev_token.data_ptr()
         bi.forced_prev = _ptr(forced_prev)
+        if page_size:
+            bi.page_size = int(page_size)
+            bi.max_pages = int(block_table.shape[1])
+            bi.block_table = block_table.data_ptr()
         bo = BlockOut(tokens.data_ptr(), conf.data_ptr(), _ptr(logits), _ptr(hidden), None)
         if stage_events is not None:
             evs = (C.c_void_p * (2 * N_STAGES))(*[e.cuda_event for e in stage_events])

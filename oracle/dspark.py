@@ -269,6 +269,22 @@ def layer(m, W: Weights, l: int, x: np.ndarray, caches, kv_off, attn_only=False,
     return x + mlp(m, W, l, x)
 
 
+# ---------------------------------------------------------- paged caches --
+def gather_pages(pool: np.ndarray, table: np.ndarray, lengths, page_size: int) -> np.ndarray:
+    """Packed rows [sum(lengths), latent] of a paged cache (huggingface.co
+    "Kimi-K3-DSpark-NVFP4", original card, "Model Overview": the draft's
+    latent pages share the target's page format).  Token j of sequence s is
+    row j mod page_size of page table[s, j div page_size]; sequences follow
+    each other in order, as in the packed layout."""
+    rows = []
+    for s, n in enumerate(lengths):
+        for j in range(int(n)):
+            rows.append(pool[table[s, j // page_size], j % page_size])
+    if not rows:
+        return pool.reshape(-1, pool.shape[-1])[:0].copy()
+    return np.stack(rows)
+
+
 # ----------------------------------------------------------- whole pass --
 def backbone(m, W: Weights, inputs, kv_fmt: str, cap_fmt: str, decompressed=False,
              keep_layers=False):

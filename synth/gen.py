@@ -268,3 +268,46 @@ def planted_verifier(draft: np.ndarray, plant_pos: np.ndarray, plant_delta: np.n
         if k < v.shape[1]:
             v[s, k] = (int(v[s, k]) + int(plant_delta[s])) % vocab
     return v
+
+
+@dataclass
+class PagedCaches:
+    pools: List[np.ndarray]   # per layer [n_pages, page_size, latent], storage format of the caches
+    table: np.ndarray         # int32 [n_seq, max_pages]: page of each sequence page (every entry valid)
+    page_size: int
+
+
+def paged_layout(caches: List[np.ndarray], kv_offsets: np.ndarray, page_size: int, seed: int,
+                 spare_pages: int = 3) -> PagedCaches:
+    """Scatter packed per-layer caches into page pools (a layout change only).
+
+    Sequence s needs ceil(len_s / page_size) pages; all pages (plus
+    `spare_pages` unused ones) get a seeded random placement in the pool.
+    Rows a sequence does not reach (the tail of its last page, unused pages)
+    hold random garbage, so a wrong page or row index shows up in results.
+    Unused block-table entries point at valid pages too.
+    """
+    n_seq = len(kv_offsets) - 1
+    lens = np.diff(np.asarray(kv_offsets, dtype=np.int64))
+    need = [int(-(-int(n) // page_size)) for n in lens]
+    max_pages = max(1, max(need))
+    n_pages = sum(need) + spare_pages
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(7001,)))
+    order = rng.permutation(n_pages).astype(np.int32)
+    table = rng.integers(0, n_pages, size=(n_seq, max_pages)).astype(np.int32)
+    k = 0
+    for s in range(n_seq):
+        table[s, :need[s]] = order[k:k + need[s]]
+        k += need[s]
+    pools = []
+    for l, c in enumerate(caches):
+        latent = c.shape[1]
+        garbage = normal((n_pages, page_size, latent), seed, 7002 + l, std=3.0)
+        pool = garbage if c.dtype == np.float32 else to_bf16_bits(garbage)
+        for s in range(n_seq):
+            off, n = int(kv_offsets[s]), int(lens[s])
+            for p in range(need[s]):
+                r0, r1 = p * page_size, min(n, (p + 1) * page_size)
+                pool[table[s, p], :r1 - r0] = c[off + r0:off + r1]
+        pools.append(pool)
+    return PagedCaches(pools, table, page_size)

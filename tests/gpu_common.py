@@ -49,6 +49,16 @@ class GpuWorkload:
         del tens
         self.cap, self.kv, self.offs, self.prev = device_inputs(wl, self.inputs)
         self.ws = self.model.workspace(wl.n_seq, wl.total_ctx)
+        self.page_size, self.table = 0, None
+
+    def use_pages(self, page_size: int, seed: int):
+        """Switch the caches to page pools holding the same rows (seeded page
+        placement, garbage elsewhere); returns the host layout."""
+        pc = gen.paged_layout(self.inputs.caches, self.inputs.kv_offsets, page_size, seed)
+        self.kv = [torch.from_numpy(p.view(np.int16)).to("cuda").view(torch.bfloat16) for p in pc.pools]
+        self.table = torch.from_numpy(pc.table).to("cuda")
+        self.page_size = page_size
+        return pc
 
     def draft(self, forced=None, want_logits=True, want_hidden=True):
         m = self.wl.model
@@ -60,7 +70,8 @@ class GpuWorkload:
         hidden = torch.empty((n * B, m.hidden), dtype=torch.float32, device=dev) if want_hidden else None
         fp = None if forced is None else torch.from_numpy(np.asarray(forced, np.int32)).to(dev)
         self.model.draft_block(self.cap, self.kv, self.offs, self.prev, self.wl.total_ctx, tokens, conf,
-                               self.ws, logits=logits, hidden=hidden, forced_prev=fp)
+                               self.ws, logits=logits, hidden=hidden, forced_prev=fp,
+                               page_size=self.page_size, block_table=self.table)
         torch.cuda.synchronize()
         out = dict(tokens=tokens.cpu().numpy(), conf=conf.cpu().numpy())
         if want_logits:
