@@ -211,6 +211,49 @@ int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_
                              int64_t total_ctx, void* workspace, size_t ws_bytes,
                              void* stream);
 
+/* Cache append: the latent cache rows of newly verified positions.  The
+ * draft's latent rows share the target's one-576-element-per-token page format
+ * (huggingface.co "Kimi-K3-DSpark-NVFP4", original card, "Model Overview"),
+ * and fc consumes the target states captured at a position
+ * (graysoft.dev "Lucebox Kimi-K3-DSpark Q8_0 GGUF", "Architecture metadata").
+ * Reading taken where the pages stop: the row of layer l at a new position is
+ * that layer's kv_a path applied to the position's fc output,
+ *   x   = RMSNorm(concat(captured) . W_fc^T; g_fc),
+ *   a   = RMSNorm(x; in_norm_l),  kv = a . W_kva_l^T,
+ *   row = [RMSNorm(kv[:kv_lora]; g_kva_l) | RoPE(kv[kv_lora:], position)],
+ * which for layer 0 is exactly the draft pass's own block key at that
+ * position. */
+typedef struct dspark_append_in {
+  int32_t n_new;               /* rows to append, 1 .. DSPARK_APPEND_MAX        */
+  int32_t act_dtype;           /* captured states: DSPARK_DT_F32 or _BF16       */
+  int32_t kv_dtype;            /* caches: DSPARK_DT_F32 or DSPARK_DT_BF16       */
+  int32_t pad_;
+  const void* captured;        /* device [n_new][n_captured][hidden], each row's
+                                  states in capture order                      */
+  const int32_t* positions;    /* device int32 [n_new]: each row's position in
+                                  its sequence (its RoPE angle)                */
+  const int64_t* slot_mapping; /* device int64 [n_new]: destination row of each
+                                  new row in every layer's cache, viewed as
+                                  [rows][kv_lora + qk_rope] (a page pool: page *
+                                  page_size + row in page); distinct, and not
+                                  range checked                                */
+  void* const* kv;             /* host array of n_layers device caches / pools  */
+} dspark_append_in;
+#define DSPARK_APPEND_MAX 128
+
+/* Bytes of device workspace dspark_cache_append needs for n_new rows
+ * (0 and the error text on bad arguments). */
+size_t dspark_append_workspace_bytes(const dspark_model* m, int32_t n_new);
+
+/* Computes and writes the rows described at dspark_append_in into every
+ * layer's cache; touches no other cache row.  Asynchronous on `stream`;
+ * `workspace` (256-byte aligned) is scratch for the call.  The model must
+ * hold the whole drafter (not layers_only) and n_captured * hidden inputs.
+ * Errors: EINVAL (nulls, n_new out of range, dtypes), EUNSUPPORTED (q_lora
+ * not a multiple of 16), EWORKSPACE, EHIP. */
+int32_t dspark_cache_append(const dspark_model* m, const dspark_append_in* in, void* workspace,
+                            size_t ws_bytes, void* stream);
+
 /* Acceptance length (huggingface.co card, "Why acceptance is so sensitive":
  * a block is accepted up to its first mismatch): out_len[s] = the largest
  * k <= block with draft[s][j] == verifier[s][j] for all j < k.  Device

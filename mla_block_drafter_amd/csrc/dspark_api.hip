@@ -997,6 +997,205 @@ int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_
   return DSPARK_OK;
 }
 
+// ---------------------------------------------------------- cache append --
+namespace {
+
+// Rows row0 .. row0 + nrows - 1 of a packed matrix as a matrix of its own
+// (16-row tiles are stored one after another, codes and scales alike).
+bool row_view(const Mat& mt, int row0, int nrows, PackedMat& out) {
+  const PackedMat& p = mt.pm;
+  if (!mt.present || p.ngroups != 1 || row0 % 16 || row0 + nrows > p.G) return false;
+  const long long t0 = row0 / 16;
+  const int esz = p.fmt == DT_F32 ? 4 : p.fmt == DT_BF16 ? 2 : 1;
+  out = p;
+  out.codes = p.codes + t0 * 16 * p.Kp * esz;
+  if (p.fmt == DT_Q8_0) out.scales = (const unsigned char*)p.scales + t0 * (p.KB / 2) * 16 * 4;
+  else if (p.fmt == DT_FP8) out.scales = (const float*)p.scales + t0 * 16;
+  out.G = nrows;
+  out.TG = (int)cdiv(nrows, 16);
+  return true;
+}
+
+struct AppendPlan {
+  int M = 0;
+  Frag f_fc, f_kv;
+  GemvPlan p_fc{}, p_kv{};
+  PackedMat kv{};  // geometry of the kv_a rows (layer 0's view)
+  long long x = 0, part = 0, ssq_a = 0, ssq_b = 0, rope = 0, zero_begin = 0, zero_end = 0, total = 0;
+};
+
+int32_t make_append_plan(const dspark_model& m, int n_new, AppendPlan& A) {
+  const dspark_config& c = m.c;
+  if (m.layers_only) return fail(DSPARK_EINVAL, "model holds decoder layers only");
+  if (n_new < 1 || n_new > DSPARK_APPEND_MAX) return fail(DSPARK_EINVAL, "n_new %d out of range", n_new);
+  const int latent = c.kv_lora + c.qk_rope;
+  if (!row_view(m.L[0].qkva, c.q_lora, latent, A.kv))
+    return fail(DSPARK_EUNSUPPORTED, "kv_a rows start at q_lora %d: not a multiple of 16", c.q_lora);
+  A.M = n_new;
+  long long off = 0;
+  auto take = [&](long long bytes) {
+    const long long o = off;
+    off = rup(off + bytes, 256);
+    return o;
+  };
+  A.p_fc = plan_gemv(m.fc.pm, n_new, true, false, true);
+  A.p_kv = plan_gemv(A.kv, n_new, true, false, true);
+  frag_geom(A.f_fc, m.fc.pm, n_new, A.p_fc);
+  frag_geom(A.f_kv, A.kv, n_new, A.p_kv);
+  A.f_fc.off = take(A.f_fc.bytes);  // written whole by k_init
+  A.zero_begin = off;
+  A.f_kv.off = take(A.f_kv.bytes);
+  A.zero_end = off;
+  A.x = take((long long)n_new * c.hidden * 4);
+  A.part = take(std::max((long long)A.p_fc.S * n_new * m.fc.pm.G, (long long)A.p_kv.S * n_new * A.kv.G) * 4);
+  A.ssq_a = take((long long)n_new * SSQ_LD * 4);
+  A.ssq_b = take((long long)n_new * SSQ_LD * 4);
+  A.rope = take((long long)n_new * (c.qk_rope / 2) * 8);
+  A.total = off;
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+size_t dspark_append_workspace_bytes(const dspark_model* m, int32_t n_new) {
+  g_err.clear();
+  if (!m) {
+    fail(DSPARK_EINVAL, "model is NULL");
+    return 0;
+  }
+  AppendPlan A;
+  if (make_append_plan(*m, n_new, A)) return 0;
+  return (size_t)A.total;
+}
+
+int32_t dspark_cache_append(const dspark_model* m, const dspark_append_in* in, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  g_err.clear();
+  if (!m || !in) return fail(DSPARK_EINVAL, "model / in is NULL");
+  const dspark_config& c = m->c;
+  AppendPlan A;
+  int32_t rc = make_append_plan(*m, in->n_new, A);
+  if (rc) return rc;
+  if (!in->captured || !in->positions || !in->slot_mapping || !in->kv) return fail(DSPARK_EINVAL, "a required pointer is NULL");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!in->kv[l]) return fail(DSPARK_EINVAL, "kv[%d] is NULL", l);
+  if (in->act_dtype != DSPARK_DT_F32 && in->act_dtype != DSPARK_DT_BF16) return fail(DSPARK_EINVAL, "bad act_dtype");
+  if (in->kv_dtype != DSPARK_DT_F32 && in->kv_dtype != DSPARK_DT_BF16) return fail(DSPARK_EINVAL, "bad kv_dtype");
+  if (!workspace || (uintptr_t)workspace % 256) return fail(DSPARK_EINVAL, "workspace NULL or not 256-byte aligned");
+  if ((long long)ws_bytes < A.total) return fail(DSPARK_EWORKSPACE, "workspace %zu bytes, need %lld", ws_bytes, A.total);
+  unsigned char* ws = (unsigned char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  bind_frag(A.f_fc, ws);
+  bind_frag(A.f_kv, ws);
+  const int M = A.M, H = c.hidden;
+  float* x = (float*)(ws + A.x);
+  float* part = (float*)(ws + A.part);
+  auto rs = [&](long long o, int n) {
+    RowScale r{};
+    r.ssq = (const float*)(ws + o);
+    r.nch = (n + 255) / 256;
+    r.invn = 1.f / (float)n;
+    r.eps = c.rms_eps;
+    return r;
+  };
+  {  // zeroed fragments, fc input fragments of each row, RoPE table at the given positions
+    InitArgs a{};
+    a.zero_ptr = ws + A.zero_begin;
+    a.zero_bytes = A.zero_end - A.zero_begin;
+    a.captured = in->captured;
+    a.cap_f32 = in->act_dtype == DSPARK_DT_F32;
+    a.n_seq = M;  // one row per "sequence": captured is [n_new][n_captured][1][hidden]
+    a.ncap = c.n_captured;
+    a.block = 1;
+    a.H = H;
+    a.fd_fc = A.f_fc.fd;
+    a.rope = (float*)(ws + A.rope);
+    a.positions = in->positions;
+    a.freqs = (const double*)(m->base + m->freqs);
+    a.npairs = c.qk_rope / 2;
+    HIPCHK(launch_init(a, st));
+  }
+  {  // fc
+    GemvArgs g{};
+    g.w = m->fc.pm;
+    g.act = A.f_fc.fd.ptr;
+    g.act_gstride = A.f_fc.fd.gstride;
+    g.act_ld = A.f_fc.fd.ld;
+    g.M = M;
+    g.hilo = A.p_fc.hilo;
+    g.ksteps_per_split = A.p_fc.ksteps_per_split;
+    g.out = part;
+    g.out_ld = m->fc.pm.G;
+    g.out_split_stride = (long long)M * g.out_ld;
+    HIPCHK(launch_gemv(g, A.p_fc, GEMV_STORE, st));
+  }
+  auto resid = [&]() {
+    ResidPost a{};
+    a.x_in = x;
+    a.x_out = x;
+    a.M = M;
+    a.H = H;
+    return a;
+  };
+  {  // y = fc output (chunk sums of y^2)
+    ResidPost a = resid();
+    a.mode = RP_SUM;
+    a.p = PartIn{part, A.p_fc.S, (long long)m->fc.pm.G, (long long)M * m->fc.pm.G};
+    a.ssq_out = (float*)(ws + A.ssq_a);
+    HIPCHK(launch_post_resid(a, st));
+  }
+  {  // x = RMSNorm(y; g_fc) (chunk sums of x^2), fragments of in_norm_0 * x
+    ResidPost a = resid();
+    a.mode = RP_NORM;
+    a.rs_in = rs(A.ssq_a, H);
+    a.g0 = (const float*)(m->base + m->fc_norm);
+    a.g1 = (const float*)(m->base + m->L[0].in_norm);
+    a.fd = A.f_kv.fd;
+    a.ssq_out = (float*)(ws + A.ssq_b);
+    HIPCHK(launch_post_resid(a, st));
+  }
+  const int latent = c.kv_lora + c.qk_rope;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const Layer& L = m->L[l];
+    if (l > 0) {  // fragments of in_norm_l * x
+      ResidPost a = resid();
+      a.mode = RP_COPY;
+      a.g1 = (const float*)(m->base + L.in_norm);
+      a.fd = A.f_kv.fd;
+      HIPCHK(launch_post_resid(a, st));
+    }
+    PackedMat kv{};
+    if (!row_view(L.qkva, c.q_lora, latent, kv)) return fail(DSPARK_EUNSUPPORTED, "kv_a view of layer %d", l);
+    GemvArgs g{};
+    g.w = kv;
+    g.act = A.f_kv.fd.ptr;
+    g.act_gstride = A.f_kv.fd.gstride;
+    g.act_ld = A.f_kv.fd.ld;
+    g.M = M;
+    g.hilo = A.p_kv.hilo;
+    g.ksteps_per_split = A.p_kv.ksteps_per_split;
+    g.out = part;
+    g.out_ld = kv.G;
+    g.out_split_stride = (long long)M * kv.G;
+    HIPCHK(launch_gemv(g, A.p_kv, GEMV_STORE, st));
+    KvRowPost a{};
+    a.p = PartIn{part, A.p_kv.S, (long long)kv.G, (long long)M * kv.G};
+    a.rs_in = rs(A.ssq_b, H);
+    a.M = M;
+    a.r = c.kv_lora;
+    a.dr = c.qk_rope;
+    a.latent = latent;
+    a.g_kva = (const float*)(m->base + L.kv_a_norm);
+    a.eps = c.rms_eps;
+    a.rope = (const float*)(ws + A.rope);
+    a.dst = in->kv[l];
+    a.dst_f32 = in->kv_dtype == DSPARK_DT_F32;
+    a.slot = in->slot_mapping;
+    HIPCHK(launch_post_kv_rows(a, st));
+  }
+  return DSPARK_OK;
+}
+
 int32_t dspark_accept_len_host(const int32_t* draft, const int32_t* verifier, int32_t n_seq, int32_t block,
                                int32_t* out_len) {
   g_err.clear();

@@ -21,7 +21,8 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
       const int m = (int)(e / a.npairs), p = (int)(e % a.npairs);
       const int s = m / a.block, i = m % a.block;
       double sn, cs;
-      sincos((double)(a.offs[s + 1] - a.offs[s] + i) * a.freqs[p], &sn, &cs);
+      const long long pos = a.positions ? (long long)a.positions[m] : (long long)(a.offs[s + 1] - a.offs[s] + i);
+      sincos((double)pos * a.freqs[p], &sn, &cs);
       a.rope[2 * e] = (float)cs;
       a.rope[2 * e + 1] = (float)sn;
     }

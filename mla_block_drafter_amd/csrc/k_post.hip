@@ -78,6 +78,45 @@ __device__ __forceinline__ void rope_pair(float x0, float x1, const float* cs, f
   y1 = x0 * s + x1 * c;
 }
 
+// Latent row of activation row m from the split-K partials of its columns
+// col0 .. col0 + latent - 1 (scaled by r): c = RMSNorm(first rr columns; g)
+// and the rotated rope pairs (cos, sin per pair in cs), written as one row
+// at element offset `at` of dst (fp32 or bf16).  All threads of the block.
+__device__ __forceinline__ void latent_row(const PartIn& p, int m, int col0, float r, int latent, int rr, int dr,
+                                           const float* g, float eps, const float* cs, void* dst, long long at,
+                                           int f32, float* red, float* lat) {
+  // latent columns k = tid + 256 u (latent <= 1024), all partial loads in flight together
+  float s2 = 0.f;
+  {
+    int cc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cc[u] = (int)threadIdx.x + 256 * u < latent ? col0 + (int)threadIdx.x + 256 * u : -1;
+    float v[4];
+    part_sum_n<4>(p, m, cc, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = threadIdx.x + 256 * u;
+      if (k >= latent) continue;
+      lat[k] = r * v[u];
+      if (k < rr) s2 += lat[k] * lat[k];
+    }
+  }
+  const float rc = rsqrtf(block_sum256(s2, red) / rr + eps);  // also orders lat[]
+  for (int k = threadIdx.x; k < latent; k += 256) {
+    float v;
+    if (k < rr) {
+      v = g[k] * (lat[k] * rc);
+    } else {
+      const int e = k - rr, pr = e >> 1;
+      float y0, y1;
+      rope_pair(lat[rr + 2 * pr], lat[rr + 2 * pr + 1], cs + 2 * pr, y0, y1);
+      v = (e & 1) ? y1 : y0;
+    }
+    if (f32) ((float*)dst)[at + k] = v;
+    else ((uint16_t*)dst)[at + k] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
 // ------------------------------------------------------------- residual --
 __global__ __launch_bounds__(256) void k_post_resid(ResidPost a) {
   __shared__ float red[4];
@@ -138,37 +177,20 @@ __global__ __launch_bounds__(256) void k_post_qkva(QkvaPost a) {
     if (threadIdx.x == 0) a.ssq_cq[m * SSQ_LD + blockIdx.x] = sq;
     return;
   }
-  // latent columns k = tid + 256 u (latent <= 1024), all partial loads in flight together
-  float s2 = 0.f;
-  {
-    int cc[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) cc[u] = (int)threadIdx.x + 256 * u < a.latent ? a.q_lora + (int)threadIdx.x + 256 * u : -1;
-    float v[4];
-    part_sum_n<4>(a.p, m, cc, v);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = threadIdx.x + 256 * u;
-      if (k >= a.latent) continue;
-      lat[k] = r * v[u];
-      if (k < a.r) s2 += lat[k] * lat[k];
-    }
-  }
-  const float rc = rsqrtf(block_sum256(s2, red) / a.r + a.eps);  // also orders lat[]
-  for (int k = threadIdx.x; k < a.latent; k += 256) {
-    float v;
-    if (k < a.r) {
-      v = a.g_kva[k] * (lat[k] * rc);
-    } else {
-      const int e = k - a.r, pr = e >> 1;
-      float y0, y1;
-      rope_pair(lat[a.r + 2 * pr], lat[a.r + 2 * pr + 1], a.rope + ((long long)m * (a.dr / 2) + pr) * 2, y0, y1);
-      v = (e & 1) ? y1 : y0;
-    }
-    const long long o = (long long)m * a.latent + k;
-    if (a.kv_f32) ((float*)a.bkeys)[o] = v;
-    else ((uint16_t*)a.bkeys)[o] = (uint16_t)f32_to_bf16_bits(v);
-  }
+  latent_row(a.p, m, a.q_lora, r, a.latent, a.r, a.dr, a.g_kva, a.eps, a.rope + (long long)m * (a.dr / 2) * 2,
+             a.bkeys, (long long)m * a.latent, a.kv_f32, red, lat);
+}
+
+// ---------------------------------------------------------- cache append --
+// One workgroup per new row: its latent row into the cache row slot[m].
+__global__ __launch_bounds__(256) void k_post_kv_rows(KvRowPost a) {
+  __shared__ float red[4];
+  __shared__ float rs;
+  __shared__ float lat[1024];
+  const int m = blockIdx.x;
+  const float r = shared_row_scale(a.rs_in, m, &rs);
+  latent_row(a.p, m, 0, r, a.latent, a.r, a.dr, a.g_kva, a.eps, a.rope + (long long)m * (a.dr / 2) * 2, a.dst,
+             a.slot[m] * a.latent, a.dst_f32, red, lat);
 }
 
 // ------------------------------------------------------------------ q_b --
@@ -237,6 +259,12 @@ hipError_t launch_post_qkva(const QkvaPost& a, hipStream_t st) {
   if (a.latent > 1024 || (a.q_lora + 255) / 256 > SSQ_LD) return hipErrorInvalidValue;
   dim3 grid((a.q_lora + 255) / 256 + 1, a.M);
   hipLaunchKernelGGL(k_post_qkva, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_post_kv_rows(const KvRowPost& a, hipStream_t st) {
+  if (a.latent > 1024 || a.M < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_post_kv_rows, dim3(a.M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -131,6 +131,7 @@ struct InitArgs {
   // pos(m) * freqs[p] for row m = s * block + i at position kv_len(s) + i
   float* rope;            // [n_seq * block][npairs][2]
   const int32_t* offs;    // [n_seq + 1] cache offsets
+  const int32_t* positions;  // optional [n_seq * block]: position of row m (instead of the offsets)
   const double* freqs;    // [npairs]
   int npairs;
 };
@@ -168,6 +169,18 @@ struct QkvaPost {
   const float* rope;          // [M][dr/2][2] (cos, sin), written by k_init
 };
 hipError_t launch_post_qkva(const QkvaPost& a, hipStream_t st);
+
+// Cache append: the latent row of each new row m (kv_a partials, columns
+// 0 .. latent - 1) written to cache row slot[m].
+struct KvRowPost {
+  PartIn p; RowScale rs_in;
+  int M, r, dr, latent;
+  const float* g_kva; float eps;
+  const float* rope;          // [M][dr/2][2] (cos, sin), written by k_init
+  void* dst; int dst_f32;     // cache [rows][latent]
+  const int64_t* slot;        // [M] destination rows
+};
+hipError_t launch_post_kv_rows(const KvRowPost& a, hipStream_t st);
 
 struct QbPost {
   PartIn p; RowScale rs;

@@ -29,6 +29,7 @@ TOP_IDS = {"fc": W_FC, "fc_norm": W_FC_NORM, "final_norm": W_FINAL_NORM, "lm_hea
 
 EXPORTS = ["dspark_packed_bytes", "dspark_model_create", "dspark_model_destroy",
            "dspark_workspace_bytes", "dspark_draft_block", "dspark_layer_forward",
+           "dspark_append_workspace_bytes", "dspark_cache_append",
            "dspark_accept_len", "dspark_accept_len_host", "dspark_dequant", "dspark_last_error"]
 
 
@@ -62,6 +63,15 @@ class BlockIn(C.Structure):
                 ("total_ctx", C.c_int64), ("captured", C.c_void_p), ("kv", C.POINTER(C.c_void_p)),
                 ("kv_offsets", C.c_void_p), ("prev_token", C.c_void_p), ("forced_prev", C.c_void_p),
                 ("page_size", C.c_int32), ("max_pages", C.c_int32), ("block_table", C.c_void_p)]
+
+
+class AppendIn(C.Structure):
+    _fields_ = [("n_new", C.c_int32), ("act_dtype", C.c_int32), ("kv_dtype", C.c_int32), ("pad_", C.c_int32),
+                ("captured", C.c_void_p), ("positions", C.c_void_p), ("slot_mapping", C.c_void_p),
+                ("kv", C.POINTER(C.c_void_p))]
+
+
+APPEND_MAX = 128
 
 
 class BlockOut(C.Structure):
@@ -107,6 +117,10 @@ def lib():
     L.dspark_layer_forward.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_size_t,
                                        C.c_void_p]
+    L.dspark_append_workspace_bytes.restype = C.c_size_t
+    L.dspark_append_workspace_bytes.argtypes = [C.c_void_p, C.c_int32]
+    L.dspark_cache_append.restype = C.c_int32
+    L.dspark_cache_append.argtypes = [C.c_void_p, C.POINTER(AppendIn), C.c_void_p, C.c_size_t, C.c_void_p]
     L.dspark_accept_len.restype = C.c_int32
     L.dspark_accept_len.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
     L.dspark_accept_len_host.restype = C.c_int32
@@ -240,6 +254,31 @@ class Model:
                                          x_out.data_ptr(), kv.data_ptr(), kdt, kv_offsets.data_ptr(),
                                          int(total_ctx), workspace.data_ptr(), workspace.numel(),
                                          _stream_ptr(stream)))
+
+    def append_workspace(self, n_new: int):
+        import torch
+        n = lib().dspark_append_workspace_bytes(self.handle, n_new)
+        if n == 0:
+            raise DsparkError(EINVAL, last_error())
+        return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def cache_append(self, captured, positions, slot_mapping, kv: Sequence, workspace, stream=None) -> None:
+        """Latent rows of n_new verified positions into every layer's cache.
+        captured: [n_new][n_captured][hidden] (bf16 or f32); positions: int32
+        [n_new]; slot_mapping: int64 [n_new] destination rows; kv: per-layer
+        caches or page pools viewed as rows of kv_lora + qk_rope."""
+        import torch
+        ai = AppendIn()
+        ai.n_new = int(positions.shape[0])
+        ai.act_dtype = DT_F32 if captured.dtype == torch.float32 else DT_BF16
+        ai.kv_dtype = DT_F32 if kv[0].dtype == torch.float32 else DT_BF16
+        ai.captured = captured.data_ptr()
+        ai.positions = positions.data_ptr()
+        ai.slot_mapping = slot_mapping.data_ptr()
+        kv_arr = (C.c_void_p * len(kv))(*[t.data_ptr() for t in kv])
+        ai.kv = kv_arr
+        check(lib().dspark_cache_append(self.handle, C.byref(ai), workspace.data_ptr(), workspace.numel(),
+                                        _stream_ptr(stream)))
 
     def dequant(self, name: str, out, stream=None) -> None:
         check(lib().dspark_dequant(self.handle, weight_id(name), out.data_ptr(), _stream_ptr(stream)))

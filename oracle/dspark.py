@@ -285,6 +285,34 @@ def gather_pages(pool: np.ndarray, table: np.ndarray, lengths, page_size: int) -
     return np.stack(rows)
 
 
+# ---------------------------------------------------------- cache append --
+def cache_rows(m, W: Weights, captured: np.ndarray, positions, cap_fmt: str) -> np.ndarray:
+    """Latent cache rows of newly verified positions, one per layer.
+
+    Pages: huggingface.co "Kimi-K3-DSpark-NVFP4", original card, "Model
+    Overview" (one 576-element latent per token, the target's page format);
+    graysoft.dev "Lucebox Kimi-K3-DSpark Q8_0 GGUF", "Architecture metadata"
+    (fc consumes the captured target states).  Reading where the pages stop:
+    layer l's row at a position is its kv_a path applied to that position's
+    fc output x = RMSNorm(concat(captured) W_fc^T; g_fc):
+    [RMSNorm((RMSNorm(x; in_norm_l) W_kva^T)[:r]; g_kva) | RoPE(...[r:], pos)].
+    captured: [n, n_captured, H] (storage format cap_fmt); returns [L, n, r + dr].
+    """
+    n = len(positions)
+    cap = _decode_input(captured, cap_fmt).reshape(n, m.n_captured * m.hidden)
+    x = rmsnorm(cap @ W("fc").T, W("fc_norm"), m.rms_eps)
+    pos = np.asarray(positions, dtype=np.int64)
+    freqs = rope_frequencies(m)
+    r = m.kv_lora
+    out = np.empty((m.n_layers, n, r + m.qk_rope))
+    for l in range(m.n_layers):
+        a = rmsnorm(x, W(f"L{l}.in_norm"), m.rms_eps)
+        kv = a @ W(f"L{l}.kv_a").T
+        out[l, :, :r] = rmsnorm(kv[:, :r], W(f"L{l}.kv_a_norm"), m.rms_eps)
+        out[l, :, r:] = rope(kv[:, r:], pos, freqs)
+    return out
+
+
 # ----------------------------------------------------------- whole pass --
 def backbone(m, W: Weights, inputs, kv_fmt: str, cap_fmt: str, decompressed=False,
              keep_layers=False):
