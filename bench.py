@@ -134,6 +134,7 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the cache-append timing")
     ap.add_argument("--page-size", type=int, default=0,
                     help="latent caches as page pools of this many tokens (seeded page placement)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -246,6 +247,33 @@ def main():
         except Exception as e:  # graph capture is an extra, never the headline
             log(f"[bench] graph capture skipped: {e!r}")
 
+    append = None
+    if not args.no_append:
+        # dspark_cache_append of one block's worth of verified positions (the
+        # rows go to a separate pool, so the pass inputs stay as they are)
+        n_new = B
+        cap_new = gen.normal((n_new, m.n_captured, m.hidden), wl.seed, 9000)
+        cap_new = (torch.from_numpy(cap_new).to(dev) if wl.formats.captured == "f32" else
+                   torch.from_numpy(gen.to_bf16_bits(cap_new).view(np.int16)).to(dev).view(torch.bfloat16))
+        pos_new = torch.arange(n_new, dtype=torch.int32, device=dev) + int(wl.total_ctx // n)
+        slot_new = torch.arange(n_new, dtype=torch.int64, device=dev)
+        pool_new = [torch.zeros((n_new, m.latent), dtype=kv[0].dtype, device=dev) for _ in range(m.n_layers)]
+        ws_app = model.append_workspace(n_new)
+        for _ in range(args.warmup):
+            model.cache_append(cap_new, pos_new, slot_new, pool_new, ws_app)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            model.cache_append(cap_new, pos_new, slot_new, pool_new, ws_app)
+        b.record()
+        torch.cuda.synchronize()
+        app_ms = a.elapsed_time(b) / K
+        app_bytes = A.append_bytes(wl, n_new)
+        append = {"rows": n_new, "us": round(app_ms * 1e3, 2), "algorithmic_bytes": app_bytes,
+                  "gbs": round(app_bytes / (app_ms * 1e-3) / 1e9, 1)}
+        log(f"[bench] cache append of {n_new} rows: {app_ms * 1e3:.1f} us")
+
     copy_gbs = copy_probe_gbs(torch)
     log(f"[bench] device copy probe: {copy_gbs:.0f} GB/s")
     total_bytes = A.total_bytes(wl)
@@ -288,6 +316,7 @@ def main():
                      "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
         "cpu_baseline": cpu,
+        "cache_append": append,
     }
     print(json.dumps(out), flush=True)
 

@@ -66,3 +66,15 @@ def attention_flops(wl: C.Workload) -> int:
     per_key = 2 * m.n_heads * m.block * (m.latent + m.kv_lora)
     keys = wl.total_ctx + wl.n_seq * m.block
     return m.n_layers * per_key * keys
+
+
+def append_bytes(wl: C.Workload, n_new: int) -> int:
+    """One cache append of n_new rows: the fc weights, the kv_a rows of every
+    layer's fused q_a / kv_a projection, the captured states read and the
+    latent rows written (every layer)."""
+    m, f = wl.model, wl.formats
+    w = storage_bytes(C.tensor_format(f, "fc"), m.hidden, m.n_captured * m.hidden)
+    w += m.n_layers * storage_bytes(C.tensor_format(f, "L0.kv_a"), m.latent, m.hidden)
+    cap_e = 4 if f.captured == C.F32 else 2
+    kv_e = 4 if f.kv_cache == C.F32 else 2
+    return w + n_new * m.n_captured * m.hidden * cap_e + m.n_layers * n_new * m.latent * kv_e
