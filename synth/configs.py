@@ -89,6 +89,7 @@ class Workload:
     markov_dominant: bool = False  # W1, W2 ~ N(0, R^-1/2); lm_head = 0
     weight_std: float = 0.02
     spike: tuple = ()        # (cache row, factor): that row of every cache scaled (a far-away dominant key)
+    captured_dist: str = "gauss"  # captured states: "gauss" N(0,1) or "heavy" (Student-t, 3 dof, unit variance)
 
     @property
     def n_seq(self) -> int:

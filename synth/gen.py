@@ -61,6 +61,14 @@ def normal(shape, seed: int, idx: int, std: float = 1.0) -> np.ndarray:
     return out.reshape(shape)
 
 
+def student_t(shape, seed: int, idx: int, df: float) -> np.ndarray:
+    """Student-t draws with `df` degrees of freedom scaled to unit variance."""
+    n = int(np.prod(shape))
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(idx, 0)))
+    v = rng.standard_t(df, size=n) * np.sqrt((df - 2.0) / df)
+    return v.astype(np.float32).reshape(shape)
+
+
 def uniform(shape, seed: int, idx: int, lo: float, hi: float) -> np.ndarray:
     out = np.empty(int(np.prod(shape)), dtype=np.float32)
     _fill(out, seed, idx, "uniform", lo, hi)
@@ -243,7 +251,9 @@ def make_inputs(wl: C.Workload) -> Inputs:
         x = normal((n_seq * blk, m.hidden), wl.seed, base + 0)
         x_in = bf16_bits_to_f32(to_bf16_bits(x))
     else:
-        cap = normal((n_seq, m.n_captured, blk, m.hidden), wl.seed, base + 0)
+        shape = (n_seq, m.n_captured, blk, m.hidden)
+        cap = (student_t(shape, wl.seed, base + 0, 3.0) if wl.captured_dist == "heavy"
+               else normal(shape, wl.seed, base + 0))
         captured = as_fmt(cap, wl.formats.captured)
     caches = []
     for l in range(m.n_layers):
