@@ -164,6 +164,15 @@ typedef struct dspark_block_in {
   int32_t page_size;          /* 0, or a power of two >= 32                     */
   int32_t max_pages;          /* row stride of block_table (>= 1 when paged)    */
   const int32_t* block_table; /* device int32 [n_seq][max_pages] when paged     */
+  /* Probabilistic drafting (huggingface.co "Kimi-K3-DSpark-NVFP4", "Sampling
+     options": the draft sampled from its own distribution).  sample_u == NULL:
+     greedy (argmax).  Else token i is the draw from softmax(l_i / temperature)
+     given by the Gumbel-max rule, argmax_v (l_i[v] / temperature
+     - ln(-ln sample_u[s][i][v])); the returned logits stay l_i.  Needs bf16
+     Markov weights and n_seq <= 16 (EUNSUPPORTED otherwise).               */
+  const float* sample_u;      /* device float [n_seq][block][vocab], in (0, 1)  */
+  float temperature;          /* > 0 when sample_u is set                       */
+  int32_t pad2_;
 } dspark_block_in;
 
 typedef struct dspark_block_out {
@@ -253,6 +262,41 @@ size_t dspark_append_workspace_bytes(const dspark_model* m, int32_t n_new);
  * not a multiple of 16), EWORKSPACE, EHIP. */
 int32_t dspark_cache_append(const dspark_model* m, const dspark_append_in* in, void* workspace,
                             size_t ws_bytes, void* stream);
+
+/* Verification of a sampled draft block (huggingface.co "Kimi-K3-DSpark-
+ * NVFP4", "Sampling options": rejection_sample_method verifies the block token
+ * by token or "as a unit").  With q_i = softmax(draft_logits[s][i] / T) and
+ * p_i = softmax(target_logits[s][i] / T) (i = block: after the whole block):
+ *   DSPARK_VERIFY_TOKEN: accept x_i while u[s][i] < min(1, p_i(x_i) / q_i(x_i));
+ *     at the first rejection draw the next token from max(p_i - q_i, 0), after
+ *     a fully accepted block from p_block;
+ *   DSPARK_VERIFY_BLOCK: w_0 = 1, w_k = min(w_{k-1} p_{k-1}(x_{k-1}) /
+ *     q_{k-1}(x_{k-1}), 1); length k is accepted when u[s][k-1] < h_k with
+ *     h_k = S_k / (S_k + 1 - w_k), S_k the mass of max(w_k p_k - q_k, 0)
+ *     (h_block = w_block); the result is the largest accepted k, and the next
+ *     token is drawn from max(w_k p_k - q_k, 0) (from p_block when k = block).
+ * Draws: the lowest index whose cumulative mass exceeds u[s][block] times the
+ * total.  Outputs: out_len[s] in [0, block] accepted draft tokens and
+ * out_token[s] the next token.  All pointers are device pointers;
+ * asynchronous on `stream`; a draft token outside [0, vocab) is rejected. */
+#define DSPARK_VERIFY_TOKEN 0
+#define DSPARK_VERIFY_BLOCK 1
+typedef struct dspark_verify_in {
+  int32_t n_seq, block, vocab, method;
+  float temperature;            /* > 0                                           */
+  int32_t pad_;
+  const int32_t* draft;         /* [n_seq][block]                                */
+  const float* draft_logits;    /* [n_seq][block][vocab]                          */
+  const float* target_logits;   /* [n_seq][block + 1][vocab]                      */
+  const float* u;               /* [n_seq][block + 1] uniforms in [0, 1)          */
+} dspark_verify_in;
+
+/* Workspace bytes dspark_verify needs (0 and the error text on bad sizes). */
+size_t dspark_verify_workspace_bytes(int32_t n_seq, int32_t block);
+
+/* Errors: EINVAL (nulls, sizes, method, temperature), EWORKSPACE, EHIP. */
+int32_t dspark_verify(const dspark_verify_in* in, int32_t* out_len, int32_t* out_token, void* workspace,
+                      size_t ws_bytes, void* stream);
 
 /* Acceptance length (huggingface.co card, "Why acceptance is so sensitive":
  * a block is accepted up to its first mismatch): out_len[s] = the largest

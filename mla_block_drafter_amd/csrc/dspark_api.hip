@@ -780,6 +780,11 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     if (kv_f32) return fail(DSPARK_EUNSUPPORTED, "paged caches are bf16 only");
     page_log2 = __builtin_ctz((unsigned)ps);
   }
+  if (in->sample_u) {
+    if (!(in->temperature > 0.f)) return fail(DSPARK_EINVAL, "temperature must be > 0 when sample_u is set");
+    if (!(m->w2.pm.fmt == DT_BF16 && markov_rollout_supported(m->w2.pm.KB, in->n_seq, c.vocab)))
+      return fail(DSPARK_EUNSUPPORTED, "probabilistic drafting needs the bf16 Markov rollout");
+  }
   Ctx C;
   C.m = m;
   make_plan(*m, in->n_seq, in->total_ctx, kv_f32, C.P);
@@ -884,6 +889,8 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.slots = (unsigned long long*)(C.ws + P.mslots);
     a.max_wgs = P.mwgs;
     a.err = (unsigned*)(C.ws + P.merr);
+    a.sample_u = in->sample_u;
+    a.inv_temp = in->sample_u ? 1.f / in->temperature : 1.f;
     HIPCHK(launch_markov_rollout(a, m->w2.pm.KB, C.st));
   }
   for (int i = 0; !rollout && i < c.block; ++i) {
@@ -1193,6 +1200,47 @@ int32_t dspark_cache_append(const dspark_model* m, const dspark_append_in* in, v
     a.slot = in->slot_mapping;
     HIPCHK(launch_post_kv_rows(a, st));
   }
+  return DSPARK_OK;
+}
+
+// ------------------------------------------------------------ verification --
+size_t dspark_verify_workspace_bytes(int32_t n_seq, int32_t block) {
+  g_err.clear();
+  if (n_seq < 1 || block < 1 || block > 64) {
+    fail(DSPARK_EINVAL, "verify workspace: bad n_seq / block");
+    return 0;
+  }
+  const long long nch = verify_nch();
+  return (size_t)(rup((long long)n_seq * (block + 1) * nch * 4 * 4, 256) + (long long)n_seq * block * nch * 2 * 4);
+}
+
+int32_t dspark_verify(const dspark_verify_in* in, int32_t* out_len, int32_t* out_token, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!in || !out_len || !out_token) return fail(DSPARK_EINVAL, "in / out_len / out_token is NULL");
+  if (in->n_seq < 1 || in->block < 1 || in->block > 64 || in->vocab < 1)
+    return fail(DSPARK_EINVAL, "bad n_seq / block / vocab");
+  if (in->method != DSPARK_VERIFY_TOKEN && in->method != DSPARK_VERIFY_BLOCK) return fail(DSPARK_EINVAL, "bad method");
+  if (!(in->temperature > 0.f)) return fail(DSPARK_EINVAL, "temperature must be > 0");
+  if (!in->draft || !in->draft_logits || !in->target_logits || !in->u) return fail(DSPARK_EINVAL, "a required pointer is NULL");
+  const size_t need = dspark_verify_workspace_bytes(in->n_seq, in->block);
+  if (!workspace || (uintptr_t)workspace % 256) return fail(DSPARK_EINVAL, "workspace NULL or not 256-byte aligned");
+  if (ws_bytes < need) return fail(DSPARK_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  VerifyArgs a{};
+  a.n_seq = in->n_seq;
+  a.block = in->block;
+  a.vocab = in->vocab;
+  a.method = in->method == DSPARK_VERIFY_TOKEN ? DSPARK_VERIFY_TOKEN_C : DSPARK_VERIFY_BLOCK_C;
+  a.inv_temp = 1.f / in->temperature;
+  a.draft = in->draft;
+  a.dlog = in->draft_logits;
+  a.tlog = in->target_logits;
+  a.u = in->u;
+  a.stats = (float*)workspace;
+  a.resid = (float*)((unsigned char*)workspace + rup((long long)in->n_seq * (in->block + 1) * verify_nch() * 4 * 4, 256));
+  a.out_len = out_len;
+  a.out_token = out_token;
+  HIPCHK(launch_verify(a, (hipStream_t)stream));
   return DSPARK_OK;
 }
 

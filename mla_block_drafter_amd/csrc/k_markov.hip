@@ -176,7 +176,9 @@ __global__ __launch_bounds__(MK_THREADS, 1) void k_markov_rollout(MarkovArgs a) 
           const long long row = (long long)mm * a.block + step;
           const float v = acc[r] + zl[wave][mm][j * 16 + (lane & 15)];
           if (a.logits) a.logits[row * a.vocab + col] = v;
-          best[r] = mk_max(best[r], argmax_key(v, (uint32_t)col));
+          // probabilistic drafting: argmax of v / T plus a Gumbel variate
+          const float sel = a.sample_u ? v * a.inv_temp - logf(-logf(a.sample_u[row * a.vocab + col])) : v;
+          best[r] = mk_max(best[r], argmax_key(sel, (uint32_t)col));
         }
       }
     }

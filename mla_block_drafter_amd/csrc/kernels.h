@@ -220,10 +220,28 @@ struct MarkovArgs {
   unsigned long long* slots;  // [block][M][workgroups] argmax keys, zeroed
   int max_wgs;                // workgroups the slot array was sized for
   unsigned* err;              // error flag, zeroed
+  const float* sample_u;      // optional [n_seq][block][vocab] uniforms: Gumbel-max draws
+  float inv_temp;             // 1 / temperature (with sample_u)
 };
 int markov_rollout_wgs(int tiles);
 bool markov_rollout_supported(int KB, int M, int vocab);
 hipError_t launch_markov_rollout(const MarkovArgs& a, int KB, hipStream_t st);
+
+// Verification of a sampled draft block (token rule or block rule).
+constexpr int DSPARK_VERIFY_TOKEN_C = 0, DSPARK_VERIFY_BLOCK_C = 1;
+struct VerifyArgs {
+  int n_seq, block, vocab, method;
+  float inv_temp;
+  const int32_t* draft;       // [n_seq][block]
+  const float* dlog;          // [n_seq][block][vocab] draft logits
+  const float* tlog;          // [n_seq][block + 1][vocab] target logits
+  const float* u;             // [n_seq][block + 1] uniforms: acceptance, then the draw
+  float* stats;               // [n_seq][block + 1][verify_nch()][4]
+  float* resid;               // [n_seq][block][verify_nch()][2]
+  int32_t* out_len; int32_t* out_token;
+};
+int verify_nch();
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 
 struct MarkovFinalArgs {
   const unsigned long long* keys;

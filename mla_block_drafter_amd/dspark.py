@@ -30,6 +30,7 @@ TOP_IDS = {"fc": W_FC, "fc_norm": W_FC_NORM, "final_norm": W_FINAL_NORM, "lm_hea
 EXPORTS = ["dspark_packed_bytes", "dspark_model_create", "dspark_model_destroy",
            "dspark_workspace_bytes", "dspark_draft_block", "dspark_layer_forward",
            "dspark_append_workspace_bytes", "dspark_cache_append",
+           "dspark_verify_workspace_bytes", "dspark_verify",
            "dspark_accept_len", "dspark_accept_len_host", "dspark_dequant", "dspark_last_error"]
 
 
@@ -62,7 +63,17 @@ class BlockIn(C.Structure):
     _fields_ = [("n_seq", C.c_int32), ("act_dtype", C.c_int32), ("kv_dtype", C.c_int32), ("pad_", C.c_int32),
                 ("total_ctx", C.c_int64), ("captured", C.c_void_p), ("kv", C.POINTER(C.c_void_p)),
                 ("kv_offsets", C.c_void_p), ("prev_token", C.c_void_p), ("forced_prev", C.c_void_p),
-                ("page_size", C.c_int32), ("max_pages", C.c_int32), ("block_table", C.c_void_p)]
+                ("page_size", C.c_int32), ("max_pages", C.c_int32), ("block_table", C.c_void_p),
+                ("sample_u", C.c_void_p), ("temperature", C.c_float), ("pad2_", C.c_int32)]
+
+
+class VerifyIn(C.Structure):
+    _fields_ = [("n_seq", C.c_int32), ("block", C.c_int32), ("vocab", C.c_int32), ("method", C.c_int32),
+                ("temperature", C.c_float), ("pad_", C.c_int32), ("draft", C.c_void_p),
+                ("draft_logits", C.c_void_p), ("target_logits", C.c_void_p), ("u", C.c_void_p)]
+
+
+VERIFY_TOKEN, VERIFY_BLOCK = 0, 1
 
 
 class AppendIn(C.Structure):
@@ -121,6 +132,10 @@ def lib():
     L.dspark_append_workspace_bytes.argtypes = [C.c_void_p, C.c_int32]
     L.dspark_cache_append.restype = C.c_int32
     L.dspark_cache_append.argtypes = [C.c_void_p, C.POINTER(AppendIn), C.c_void_p, C.c_size_t, C.c_void_p]
+    L.dspark_verify_workspace_bytes.restype = C.c_size_t
+    L.dspark_verify_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
+    L.dspark_verify.restype = C.c_int32
+    L.dspark_verify.argtypes = [C.POINTER(VerifyIn), C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     L.dspark_accept_len.restype = C.c_int32
     L.dspark_accept_len.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
     L.dspark_accept_len_host.restype = C.c_int32
@@ -217,7 +232,8 @@ class Model:
 
     def draft_block(self, captured, kv: Sequence, kv_offsets, prev_token, total_ctx: int, tokens, conf,
                     workspace, logits=None, hidden=None, forced_prev=None, stream=None,
-                    stage_events=None, page_size: int = 0, block_table=None) -> None:
+                    stage_events=None, page_size: int = 0, block_table=None, sample_u=None,
+                    temperature: float = 1.0) -> None:
         """stage_events: optional list of 2*N_STAGES torch.cuda.Event (enable_timing).
         page_size > 0: kv holds page pools and block_table (int32 [n_seq][max_pages])
         maps each sequence's pages."""
@@ -234,6 +250,9 @@ class Model:
         bi.kv_offsets = kv_offsets.data_ptr()
         bi.prev_token = prev_token.data_ptr()
         bi.forced_prev = _ptr(forced_prev)
+        if sample_u is not None:
+            bi.sample_u = sample_u.data_ptr()
+            bi.temperature = float(temperature)
         if page_size:
             bi.page_size = int(page_size)
             bi.max_pages = int(block_table.shape[1])
@@ -282,6 +301,27 @@ class Model:
 
     def dequant(self, name: str, out, stream=None) -> None:
         check(lib().dspark_dequant(self.handle, weight_id(name), out.data_ptr(), _stream_ptr(stream)))
+
+
+def verify(draft, draft_logits, target_logits, u, temperature: float, method: int, out_len, out_token,
+           stream=None) -> None:
+    """Verification of sampled draft blocks (include/dspark.h, dspark_verify).
+    draft int32 [n_seq][block]; draft_logits [n_seq][block][vocab];
+    target_logits [n_seq][block + 1][vocab]; u [n_seq][block + 1]."""
+    import torch
+    n_seq, block = draft.shape
+    vi = VerifyIn()
+    vi.n_seq, vi.block, vi.vocab, vi.method = int(n_seq), int(block), int(draft_logits.shape[-1]), int(method)
+    vi.temperature = float(temperature)
+    vi.draft, vi.draft_logits = draft.data_ptr(), draft_logits.data_ptr()
+    vi.target_logits, vi.u = target_logits.data_ptr(), u.data_ptr()
+    L = lib()
+    nb = L.dspark_verify_workspace_bytes(int(n_seq), int(block))
+    if nb == 0:
+        raise DsparkError(EINVAL, last_error())
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    check(L.dspark_verify(C.byref(vi), out_len.data_ptr(), out_token.data_ptr(), ws.data_ptr(), nb,
+                          _stream_ptr(stream)))
 
 
 def accept_len(draft, verifier, out, stream=None) -> None:

@@ -334,14 +334,26 @@ def backbone(m, W: Weights, inputs, kv_fmt: str, cap_fmt: str, decompressed=Fals
     return hf, z, per_layer
 
 
+def gumbel(u: np.ndarray) -> np.ndarray:
+    """Standard Gumbel variates -ln(-ln u) of uniforms u in (0, 1)."""
+    return -np.log(-np.log(np.asarray(u, dtype=np.float64)))
+
+
 def markov_rollout(m, W: Weights, hf: np.ndarray, z: np.ndarray, prev_token,
-                   forced: Optional[np.ndarray] = None):
+                   forced: Optional[np.ndarray] = None, sample_u: Optional[np.ndarray] = None,
+                   temperature: float = 1.0):
     """Sequential Markov head and confidence over each sequence's block.
 
     For i = 0..B-1: u = W1[t_{i-1}] (zero when t_{i-1} = -1), l_i = z_i + W2 u,
     t_i = argmax l_i (lowest index on ties), conf_i = sigmoid(w_h . hf_i +
     w_m . u + b).  t_{-1} = prev_token; with `forced`, t_{i-1} for i >= 1 is
     forced[s, i-1] instead of the drafted token (teacher-forced rollout).
+
+    Probabilistic drafting (huggingface.co "Kimi-K3-DSpark-NVFP4", "Sampling
+    options": the draft sampled from its own distribution): with `sample_u`
+    ([n_seq, B, V] uniforms in (0, 1), an input), t_i is a draw from
+    softmax(l_i / temperature) by the Gumbel-max rule, t_i = argmax_v
+    (l_i[v] / temperature - ln(-ln u[s, i, v])).  The logits returned stay l_i.
     """
     B, H, V = m.block, m.hidden, m.vocab
     n_seq = len(prev_token)
@@ -358,20 +370,24 @@ def markov_rollout(m, W: Weights, hf: np.ndarray, z: np.ndarray, prev_token,
                 t_prev = int(forced[s, i - 1]) if forced is not None else int(tokens[s, i - 1])
             u = w1[t_prev] if t_prev >= 0 else np.zeros(m.markov_rank)
             li = z[s * B + i] + w2 @ u
-            tokens[s, i] = argmax_lowest(li)
+            if sample_u is None:
+                tokens[s, i] = argmax_lowest(li)
+            else:
+                tokens[s, i] = argmax_lowest(li / temperature + gumbel(sample_u[s, i]))
             logits[s, i] = li
             conf[s, i] = sigmoid(w_h @ hf[s * B + i] + w_m @ u + cb[0])
     return tokens, conf, logits
 
 
 def draft_block(wl, stored, inputs, forced: Optional[np.ndarray] = None,
-                decompressed: bool = False, keep_layers: bool = False) -> dict:
+                decompressed: bool = False, keep_layers: bool = False,
+                sample_u: Optional[np.ndarray] = None, temperature: float = 1.0) -> dict:
     """The whole draft pass for every sequence of the workload."""
     m = wl.model
     W = Weights(stored)
     hf, z, per_layer = backbone(m, W, inputs, wl.formats.kv_cache, wl.formats.captured,
                                 decompressed=decompressed, keep_layers=keep_layers)
-    tokens, conf, logits = markov_rollout(m, W, hf, z, inputs.prev_token, forced)
+    tokens, conf, logits = markov_rollout(m, W, hf, z, inputs.prev_token, forced, sample_u, temperature)
     out = dict(tokens=tokens, conf=conf, logits=logits, z=z, hidden=hf)
     if keep_layers:
         out["layers"] = per_layer
