@@ -10,6 +10,15 @@ Test infrastructure only (see oracle/__init__.py).
 * FP8 E4M3FN, per output channel (huggingface.co "Kimi-K3-DSpark-NVFP4",
   "Limitations": the per-channel weight-only FP8 path): OCP 8-bit E4M3 with
   bias 7, no infinities, 0x7F/0xFF = NaN, largest finite 448; weight = s_n * v.
+* MXFP4 (huggingface.co "Kimi-K3-DSpark-NVFP4", "Drift-limited acceptance
+  ceiling" and "Detail": the 4-bit MX variant measured beside NVFP4), as the
+  OCP Microscaling (MX) format defines it: blocks of 32 consecutive weights
+  along a row share one E8M0 scale X = 2^(e - 127) (code 255 = NaN); each
+  weight is an FP4 E2M1 element (sign, 2 exponent bits with bias 1, 1 mantissa
+  bit: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}); weight = X * element.  The pages fix
+  no byte layout; the stored one here is 17 bytes per block: the scale code,
+  then 16 bytes with element 2i in the low nibble of byte i and element
+  2i + 1 in the high nibble.
 
 Encoders are here only so that tests can state round-trip properties; the
 draft pass itself only ever decodes.
@@ -116,6 +125,77 @@ def e4m3fn_encode(x: np.ndarray) -> np.ndarray:
     return (c | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
+# --------------------------------------------------------------- MXFP4 ----
+MX_BLOCK = 32
+MX_BYTES = 17
+
+
+def e2m1_value(code: int) -> float:
+    """One FP4 E2M1 code (4 bits) -> its real value."""
+    s = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return s * (m / 2.0)                      # subnormal: m * 2^(1 - bias) / 2
+    return s * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+def e8m0_value(code: int) -> float:
+    """One E8M0 scale code -> 2^(code - 127); 255 is NaN."""
+    return float("nan") if code == 255 else 2.0 ** (int(code) - 127)
+
+
+_E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+_E8M0_TABLE = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
+
+
+def mxfp4_decode(blocks: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """[rows, cols/32*17] uint8 -> float64 [rows, cols]; weight = X * element."""
+    nb = cols // MX_BLOCK
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(rows, nb, MX_BYTES)
+    x = _E8M0_TABLE[b[:, :, 0]][..., None]             # [rows, nb, 1]
+    packed = b[:, :, 1:]
+    codes = np.empty((rows, nb, MX_BLOCK), dtype=np.uint8)
+    codes[:, :, 0::2] = packed & 0x0F
+    codes[:, :, 1::2] = packed >> 4
+    return (x * _E2M1_TABLE[codes]).reshape(rows, cols)
+
+
+def e2m1_encode(r: np.ndarray) -> np.ndarray:
+    """float -> E2M1 code: nearest element, ties to the even code (mantissa
+    bit 0), magnitudes above 6 saturate to +-6."""
+    r = np.asarray(r, dtype=np.float64)
+    pos = _E2M1_TABLE[:8]                                # 0 .. 6, increasing
+    a = np.minimum(np.abs(r), 6.0)
+    i = np.clip(np.searchsorted(pos, a, side="left"), 1, 7)
+    lo_v, hi_v = pos[i - 1], pos[i]
+    pick_hi = (hi_v - a < a - lo_v) | ((hi_v - a == a - lo_v) & (i % 2 == 0))
+    c = np.where(pick_hi, i, i - 1)
+    c = np.where(a == 0, 0, c)
+    return (c | np.where(np.signbit(r) & (c != 0), 0x8, 0)).astype(np.uint8)
+
+
+def mxfp4_encode(w: np.ndarray) -> np.ndarray:
+    """float32 [rows, K] -> 17-byte blocks, by the MX conversion rule: the
+    shared exponent is floor(log2(amax)) - 2 (2 = exponent of the largest
+    power of two in E2M1), clamped to the E8M0 range [-127, 127]; elements are
+    x / X rounded to E2M1 (nearest, ties to even, saturating).  An all-zero
+    block stores exponent -127 and zero elements."""
+    x = np.ascontiguousarray(w, dtype=np.float32).astype(np.float64)
+    rows, K = x.shape
+    nb = K // MX_BLOCK
+    xb = x.reshape(rows, nb, MX_BLOCK)
+    amax = np.max(np.abs(xb), axis=2)
+    _, e = np.frexp(amax)                                # amax = f 2^e, f in [0.5, 1)
+    shared = np.where(amax > 0, e - 1 - 2, -127)
+    shared = np.clip(shared, -127, 127)
+    codes = e2m1_encode(xb / np.ldexp(1.0, shared)[..., None])
+    out = np.empty((rows, nb, MX_BYTES), dtype=np.uint8)
+    out[:, :, 0] = (shared + 127).astype(np.uint8)
+    out[:, :, 1:] = codes[:, :, 0::2] | (codes[:, :, 1::2] << 4)
+    return out.reshape(rows, nb * MX_BYTES)
+
+
 # ------------------------------------------------------------ dispatch ----
 def decode(stored) -> np.ndarray:
     """A stored tensor (attributes fmt, shape, data, scales) -> float64."""
@@ -128,6 +208,8 @@ def decode(stored) -> np.ndarray:
         return q8_0_decode(stored.data, shape[0], shape[1])
     if fmt == "fp8_e4m3":
         return fp8_decode(stored.data, stored.scales)
+    if fmt == "mxfp4":
+        return mxfp4_decode(stored.data, shape[0], shape[1])
     raise ValueError(fmt)
 
 
@@ -142,4 +224,6 @@ def decode_rows(stored, r0: int, r1: int) -> np.ndarray:
         return q8_0_decode(stored.data[r0:r1], r1 - r0, cols)
     if fmt == "fp8_e4m3":
         return fp8_decode(stored.data[r0:r1], stored.scales[r0:r1])
+    if fmt == "mxfp4":
+        return mxfp4_decode(stored.data[r0:r1], r1 - r0, cols)
     raise ValueError(fmt)

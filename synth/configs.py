@@ -27,6 +27,7 @@ F32 = "f32"
 BF16 = "bf16"
 Q8_0 = "q8_0"
 FP8 = "fp8_e4m3"
+MXFP4 = "mxfp4"
 
 
 @dataclass(frozen=True)
@@ -114,6 +115,7 @@ ALL_BF16 = Formats(fc=BF16, q_a=BF16, q_b=BF16, kv_b=BF16, o=BF16, mlp=BF16,
                    lm_head=BF16, markov=BF16)
 Q8 = Formats()
 FP8_PC = Formats(fc=FP8, q_b=FP8, o=FP8, mlp=FP8)
+MX4 = Formats(fc=MXFP4, q_b=MXFP4, o=MXFP4, mlp=MXFP4)  # same tensor selection as FP8
 
 SEED_BASE = 20261200
 

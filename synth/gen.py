@@ -154,6 +154,43 @@ def to_fp8_e4m3_per_channel(w: np.ndarray):
     return codes, s
 
 
+_E2M1_POS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def to_mxfp4(w: np.ndarray) -> np.ndarray:
+    """[rows, K] float32 -> [rows, K/32*17] uint8 MX blocks (E8M0 scale code,
+    then 16 bytes of E2M1 pairs, element 2i in the low nibble).
+
+    X = 2^(floor(log2 amax) - 2) (2^-127 for an all-zero block); each x / X is
+    rounded on its own grid: steps of 0.5 below 2, of 1 in [2, 4), of 2 from 4,
+    ties to even, capped at 6."""
+    rows, K = w.shape
+    if K % 32:
+        raise ValueError("MXFP4 needs K % 32 == 0")
+    nb = K // 32
+    out = np.empty((rows, nb, 17), dtype=np.uint8)
+
+    def work(r0):
+        r1 = min(rows, r0 + 2048)
+        x = w[r0:r1].reshape(r1 - r0, nb, 32).astype(np.float32, copy=False)
+        amax = np.abs(x).max(axis=2)
+        bits = amax.view(np.int32)
+        e = ((bits >> 23) & 0xFF) - 127                   # floor(log2 amax) for normal amax
+        e = np.where(amax > 0, e, -125)
+        sexp = np.clip(e - 2, -127, 127)
+        a = np.abs(x) / np.ldexp(np.float32(1.0), sexp)[..., None].astype(np.float32)
+        q = np.where(a < 2, np.rint(a * 2) / 2, np.where(a < 4, np.rint(a), 2 * np.rint(a / 2)))
+        q = np.minimum(q, 6.0).astype(np.float32)
+        c = np.searchsorted(_E2M1_POS, q).astype(np.uint8)
+        c = c | np.where((x < 0) & (c > 0), 8, 0).astype(np.uint8)
+        out[r0:r1, :, 0] = (sexp + 127).astype(np.uint8)
+        out[r0:r1, :, 1:] = c[:, :, 0::2] | (c[:, :, 1::2] << 4)
+
+    with _pool() as ex:
+        list(ex.map(work, range(0, rows, 2048)))
+    return out.reshape(rows, nb * 17)
+
+
 @dataclass
 class Stored:
     """One weight tensor in its storage format.
@@ -162,6 +199,7 @@ class Stored:
     bf16: data uint16 [rows, cols] (bf16 bit patterns)
     q8_0: data uint8 [rows, cols/32*34] (canonical 34-byte blocks)
     fp8_e4m3: data uint8 [rows, cols], scales float32 [rows]
+    mxfp4: data uint8 [rows, cols/32*17] (MX blocks of 32: E8M0 scale, 16 B of E2M1)
     """
     fmt: str
     shape: tuple
@@ -183,6 +221,8 @@ def store(w: np.ndarray, fmt: str) -> Stored:
     if fmt == C.FP8:
         codes, s = to_fp8_e4m3_per_channel(w)
         return Stored(fmt, w.shape, codes, s)
+    if fmt == C.MXFP4:
+        return Stored(fmt, w.shape, to_mxfp4(w))
     raise ValueError(fmt)
 
 
