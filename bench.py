@@ -287,7 +287,7 @@ def main():
         t = time.time()
         cpu = cpu_baseline(wl, stored, inp)
         log(f"[bench] cpu baseline in {time.time() - t:.1f}s: {cpu}")
-    fmt = {C.Q8_0: "q8_0", C.FP8: "fp8_e4m3", C.BF16: "bf16", C.F32: "f32"}[wl.formats.mlp]
+    fmt = {C.Q8_0: "q8_0", C.FP8: "fp8_e4m3", C.MXFP4: "mxfp4", C.BF16: "bf16", C.F32: "f32"}[wl.formats.mlp]
     out = {
         "metric": METRIC,
         "value": round(ms_step * 1e3 / blocks, 2),

@@ -54,6 +54,15 @@ extern "C" {
  * scale per output row; weight = scale[row] * e4m3(code) (huggingface.co card,
  * "Limitations": per-channel weight-only FP8). */
 #define DSPARK_DT_FP8_E4M3 3
+/* MXFP4 (OCP Microscaling): blocks of 32 consecutive weights along a row, 17
+ * bytes each: one E8M0 scale code e (X = 2^(e - 127)) then 16 bytes of FP4
+ * E2M1 codes, element 2i in the low nibble of byte i and 2i + 1 in the high
+ * nibble; weight = X * e2m1(code) (huggingface.co card, "Drift-limited
+ * acceptance ceiling" and "Detail": the MXFP4 variant).  cols % 32 == 0 and
+ * round_up(cols, 64) % 128 == 0 (the device layout holds four blocks per
+ * 1 KiB chunk).  On the device a scale code of 0 decodes as 0 (not 2^-127)
+ * and 255 as +inf (not NaN): only the exponent field is formed. */
+#define DSPARK_DT_MXFP4 4
 
 /* ---- weight table ids ---- */
 #define DSPARK_W_FC 0          /* [hidden][n_captured*hidden] fc ("context_proj")  */
@@ -102,7 +111,8 @@ typedef struct dspark_weight {
   int32_t id;          /* DSPARK_W_* or DSPARK_LAYER_W(l, k)                    */
   int32_t dtype;       /* DSPARK_DT_*; norms and the confidence head are F32    */
   const void* data;    /* device; F32 float[rows][cols]; BF16 uint16[rows][cols];
-                          Q8_0 uint8[rows][cols/32*34]; FP8 uint8[rows][cols]   */
+                          Q8_0 uint8[rows][cols/32*34]; FP8 uint8[rows][cols];
+                          MXFP4 uint8[rows][cols/32*17]                         */
   const void* scales;  /* device float[rows] for FP8, else NULL                 */
   int64_t rows, cols;  /* vectors: rows = length, cols = 1                      */
 } dspark_weight;
@@ -111,7 +121,7 @@ typedef struct dspark_model dspark_model; /* opaque, host memory */
 
 /* Bytes of device memory the caller must provide to dspark_model_create for
  * the repacked weights (device layouts: 16-row tiles in MFMA fragment order,
- * Q8_0 codes and fp16 scales in separate planes).  0 on invalid input (see
+ * Q8_0 / MXFP4 codes and block scales in separate planes).  0 on invalid input (see
  * dspark_last_error). */
 size_t dspark_packed_bytes(const dspark_config* cfg, const dspark_weight* w, int32_t n);
 

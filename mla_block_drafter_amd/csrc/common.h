@@ -16,6 +16,12 @@
 //             holding the fp16 scales of blocks 2p (low half) and 2p+1, so a
 //             wave reads 64 contiguous bytes of scales per 1 KiB of codes.
 //             FP8 scales: fp32 [tiles*16].
+//   * MXFP4:  one 1 KiB chunk per (tile, quad of k blocks), index
+//             t*(KB/4) + p; lane l owns 16 bytes: dword j holds the 8 E2M1
+//             codes (element i in nibble i) of block 4p + j, same row /
+//             column rule as BF16.  Scales: one dword per (tile, quad, row):
+//             [tiles][KB/4][16], byte j = E8M0 code of block 4p + j.
+//             Needs KB % 4 == 0.
 //   * F32:    one 1 KiB chunk per (tile, 16-wide k group g); lane l owns 4
 //             floats of row 16t + (l & 15), columns 16g + 4(l >> 4) .. +3,
 //             fed to four v_mfma_f32_16x16x4_f32 in turn.
@@ -47,7 +53,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_Q8_0 = 2, DT_FP8 = 3 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_Q8_0 = 2, DT_FP8 = 3, DT_MXFP4 = 4 };
 
 // ------------------------------------------------------------------ scalars --
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -107,11 +113,30 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// E8M0 scale code j (byte j of w) -> fp32 2^(code - 127), formed as the
+// exponent field alone (code 0 gives 0, code 255 gives +inf).
+template <int J>
+__device__ __forceinline__ float e8m0_f32(uint32_t w) {
+  return __uint_as_float((J < 3 ? w << (23 - 8 * J) : w >> 1) & 0x7F800000u);
+}
+
+// Eight E2M1 codes (nibble i = element i) times a power-of-two scale -> eight
+// bf16, exact (two significant bits), by the gfx950 scaled conversion.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // ---------------------------------------------------------------- matrices --
 // Device view of one packed weight matrix (see the layout notes above).
 struct PackedMat {
   const unsigned char* codes;  // code plane
-  const void* scales;          // Q8_0: u32 [tiles][KB/2][16]; FP8: f32 [tiles*16]; else null
+  const void* scales;          // Q8_0: u32 [tiles][KB/2][16]; FP8: f32 [tiles*16];
+                               // MXFP4: u32 [tiles][KB/4][16]; else null
   int fmt;                     // DT_*
   int ngroups;                 // >= 1
   int G;                       // logical rows per group

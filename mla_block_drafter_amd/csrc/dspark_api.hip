@@ -43,6 +43,16 @@ struct Mat {
   bool present = false;
 };
 
+// Bytes of one packed row of n reduction elements.
+long long code_bytes(int fmt, long long n) {
+  return fmt == DT_F32 ? 4 * n : fmt == DT_BF16 ? 2 * n : fmt == DT_MXFP4 ? n / 2 : n;
+}
+
+// Bytes of the scale plane per 16-row tile.
+long long scale_tile_bytes(const PackedMat& p) {
+  return p.fmt == DT_Q8_0 ? (p.KB / 2) * 16 * 4 : p.fmt == DT_FP8 ? 16 * 4 : p.fmt == DT_MXFP4 ? (p.KB / 4) * 16 * 4 : 0;
+}
+
 void mat_geom(Mat& m, int fmt, int ngroups, int G, int K) {
   PackedMat& p = m.pm;
   p.fmt = fmt;
@@ -53,9 +63,10 @@ void mat_geom(Mat& m, int fmt, int ngroups, int G, int K) {
   p.Kp = (int)rup(K, 64);
   p.KB = p.Kp / 32;
   const long long T = (long long)ngroups * p.TG;
-  const int esz = fmt == DT_F32 ? 4 : fmt == DT_BF16 ? 2 : 1;
-  m.codes_bytes = T * 16 * p.Kp * esz;
-  m.scales_bytes = fmt == DT_Q8_0 ? T * (p.KB / 2) * 16 * 4 : fmt == DT_FP8 ? T * 16 * 4 : 0;
+  m.codes_bytes = T * 16 * code_bytes(fmt, p.Kp);
+  m.scales_bytes = fmt == DT_Q8_0 ? T * (p.KB / 2) * 16 * 4
+                   : fmt == DT_FP8 ? T * 16 * 4
+                   : fmt == DT_MXFP4 ? T * (p.KB / 4) * 16 * 4 : 0;
   m.present = true;
 }
 
@@ -113,11 +124,13 @@ int32_t get_mat(const dspark_weight* w, int n, int id, long long rows, long long
   if (x->rows != rows || x->cols != cols)
     return fail(DSPARK_EINVAL, "weight id %d: shape [%lld][%lld], expected [%lld][%lld]", id, (long long)x->rows,
                 (long long)x->cols, rows, cols);
-  if (x->dtype < DSPARK_DT_F32 || x->dtype > DSPARK_DT_FP8_E4M3)
+  if (x->dtype < DSPARK_DT_F32 || x->dtype > DSPARK_DT_MXFP4)
     return fail(DSPARK_EUNSUPPORTED, "weight id %d: unknown dtype %d", id, x->dtype);
   if (!x->data) return fail(DSPARK_EINVAL, "weight id %d: data is NULL", id);
   if (x->dtype == DSPARK_DT_Q8_0 && cols % 32) return fail(DSPARK_EUNSUPPORTED, "weight id %d: Q8_0 needs cols %% 32 == 0", id);
   if (x->dtype == DSPARK_DT_FP8_E4M3 && !x->scales) return fail(DSPARK_EINVAL, "weight id %d: FP8 scales NULL", id);
+  if (x->dtype == DSPARK_DT_MXFP4 && (cols % 32 || rup(cols, 64) % 128))
+    return fail(DSPARK_EUNSUPPORTED, "weight id %d: MXFP4 needs cols %% 32 == 0 and round_up(cols, 64) %% 128 == 0", id);
   return DSPARK_OK;
 }
 
@@ -1013,11 +1026,9 @@ bool row_view(const Mat& mt, int row0, int nrows, PackedMat& out) {
   const PackedMat& p = mt.pm;
   if (!mt.present || p.ngroups != 1 || row0 % 16 || row0 + nrows > p.G) return false;
   const long long t0 = row0 / 16;
-  const int esz = p.fmt == DT_F32 ? 4 : p.fmt == DT_BF16 ? 2 : 1;
   out = p;
-  out.codes = p.codes + t0 * 16 * p.Kp * esz;
-  if (p.fmt == DT_Q8_0) out.scales = (const unsigned char*)p.scales + t0 * (p.KB / 2) * 16 * 4;
-  else if (p.fmt == DT_FP8) out.scales = (const float*)p.scales + t0 * 16;
+  out.codes = p.codes + t0 * 16 * code_bytes(p.fmt, p.Kp);
+  if (p.scales) out.scales = (const unsigned char*)p.scales + t0 * scale_tile_bytes(p);
   out.G = nrows;
   out.TG = (int)cdiv(nrows, 16);
   return true;

@@ -1,5 +1,5 @@
 // Skinny GEMM for the draft pass: M = 7 activation rows per sequence against a
-// weight matrix streamed once from HBM (weight-only BF16 / Q8_0 / FP8 / F32).
+// weight matrix streamed once from HBM (weight-only BF16 / Q8_0 / FP8 / MXFP4 / F32).
 //
 // Why MFMA for a 7-row product: with packed-fp32 VALU ops unavailable, a VALU
 // dot product costs 7 FMAs plus a decode per weight element, about 700 us of
@@ -260,7 +260,7 @@ __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, 
   }
 }
 
-// bf16-family weights (BF16 / Q8_0 / FP8).
+// bf16-family weights (BF16 / Q8_0 / FP8 / MXFP4).
 //
 // AMODE selects the activation operand:
 //  A_GLOBAL:  prepared bf16 fragments read from global memory (L2 resident);
@@ -521,7 +521,110 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
 
     // Weight stream, software pipelined: the loads of stage s+1 are issued
     // before stage s is consumed, so a wave always has loads in flight.
-    if constexpr (FMT == DT_BF16 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
+    if constexpr (FMT == DT_MXFP4) {
+      // E2M1 codes decoded to bf16 with the block's E8M0 scale folded into
+      // the conversion (exact), then the bf16 MFMA.  One 1 KiB chunk per
+      // (tile, quad of k blocks) and one scale dword per (tile, quad, row).
+      // Split-K ranges are whole quads (KB % 4 == 0, unit 4).
+      const int KQ = KB >> 2, q1 = kb1 >> 2;
+      const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)t0 * KQ * 1024,
+                                                 (uint32_t)(TPW * KQ * 1024));
+      const __amdgpu_buffer_rsrc_t sr = buf_rsrc((const unsigned char*)a.w.scales + (long long)t0 * KQ * 64,
+                                                 (uint32_t)(TPW * KQ * 64));
+      const uint32_t l16 = lane * 16, ls = (lane & 15) * 4;
+      auto scale = [](uint32_t w, int i) {
+        return i == 0 ? e8m0_f32<0>(w) : i == 1 ? e8m0_f32<1>(w) : i == 2 ? e8m0_f32<2>(w) : e8m0_f32<3>(w);
+      };
+      if constexpr (MT == 1 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
+        // prepared fragments: a quad's four activation fragments are loaded
+        // with its weights, stage by stage (U quads x TPW tiles)
+        constexpr int U = 2;
+        const __amdgpu_buffer_rsrc_t ar = buf_rsrc(afrag, (uint32_t)(KB * 1024));
+        struct Stage {
+          u32x4 w[U][TPW];
+          uint32_t s[U][TPW];
+          u32x4 x[U][4];
+        };
+        auto load_stage = [&](Stage& st, int p0) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int p = p0 + u;
+            const bool ok = p < q1;
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+              st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                  wr, ok ? (uint32_t)((j * KQ + p) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
+              st.s[u][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, ok ? (uint32_t)((j * KQ + p) * 64) + ls : BUF_OOB,
+                                                                0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              st.x[u][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                  ar, ok ? (uint32_t)((4 * p + i) * 1024) + l16 : BUF_OOB, 0, 0));
+          }
+        };
+        auto compute_stage = [&](const Stage& st, int p0) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (p0 + u >= q1) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bf16x8 A = __builtin_bit_cast(bf16x8, st.x[u][i]);
+#pragma unroll
+              for (int j = 0; j < TPW; ++j)
+                acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    A, fp4x8_to_bf16x8(st.w[u][j][i], scale(st.s[u][j], i)), acc[0][j], 0, 0, 0);
+            }
+          }
+        };
+        Stage sa, sb;
+        const int p0 = kb0 >> 2;
+        const int nst = (q1 - p0 + U - 1) / U;
+        load_stage(sa, p0);
+        int p = p0, st = 0;
+        for (; st + 2 < nst; st += 2, p += 2 * U) {
+          load_stage(sb, p + U);
+          compute_stage(sa, p);
+          load_stage(sa, p + 2 * U);
+          compute_stage(sb, p + U);
+        }
+        if (st + 1 < nst) {
+          load_stage(sb, p + U);
+          compute_stage(sa, p);
+          compute_stage(sb, p + U);
+        } else if (nst > 0) {
+          compute_stage(sa, p);
+        }
+      } else {
+        // several m-tiles, or activations staged in LDS: weights by quad,
+        // activations read as consumed
+        stage_activations();
+        staged = true;
+        for (int p = kb0 >> 2; p < q1; ++p) {
+          u32x4 w[TPW];
+          uint32_t sc[TPW];
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                wr, (uint32_t)((j * KQ + p) * 1024) + l16, 0, BUF_NT));
+            sc[j] = __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)((j * KQ + p) * 64) + ls, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bf16x8 A[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) A[mt] = load_a(mt, 4 * p + i);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+              const bf16x8 B = fp4x8_to_bf16x8(w[j][i], scale(sc[j], i));
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt], B, acc[mt][j], 0, 0, 0);
+            }
+          }
+        }
+      }
+    } else if constexpr (FMT == DT_BF16 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
       // bf16 weights, prepared bf16 activation fragments: both loaded per
       // stage of U k blocks (tile j, k block kb: 1 KiB of weights; m-tile mt:
       // 1 KiB of activations).

@@ -27,14 +27,19 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   // matrices of at least 1792 tiles (the fused 28,672-row gate/up).  One
   // when the matrix has too few tiles.
   p.TPW = 1;
-  if (p.MT == 1) {
+  if (p.MT == 1 && w.fmt == DT_MXFP4) {
+    // four tiles share each quad's four activation fragments (a 16-row
+    // tile's quad of E2M1 codes is only 1 KiB)
+    if (w.TG % 4 == 0 && T / 4 >= (allow_split ? 64 : 256)) p.TPW = 4;
+    else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 64 : 256)) p.TPW = 2;
+  } else if (p.MT == 1) {
     if (w.TG % 4 == 0 && ((gather && T / 4 >= 256) || (allow_split && T / 4 >= 448))) p.TPW = 4;
     else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 128 : 256)) p.TPW = 2;
   }
   const int waves = T / p.TPW;
   p.grid_x = (waves + 3) / 4;
   const int ksteps = f32 ? (w.Kp >> 4) : w.KB;
-  const int unit = (w.fmt == DT_Q8_0 || w.fmt == DT_FP8) ? 2 : 1;
+  const int unit = w.fmt == DT_MXFP4 ? 4 : (w.fmt == DT_Q8_0 || w.fmt == DT_FP8) ? 2 : 1;
   int S = 1;
   if (allow_split)
     S = std::max(1, std::min(kMaxWaves / std::max(waves, 1), ksteps / 8));
@@ -66,6 +71,7 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
 hipError_t launch_gemv_bf16(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 hipError_t launch_gemv_q8_0(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 hipError_t launch_gemv_fp8(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
+hipError_t launch_gemv_mxfp4(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 hipError_t launch_gemv_f32(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 
 hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st) {
@@ -74,6 +80,7 @@ hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& p, int mode, hipStream
     case DT_BF16: return launch_gemv_bf16(a, p, mode, st);
     case DT_Q8_0: return launch_gemv_q8_0(a, p, mode, st);
     case DT_FP8: return launch_gemv_fp8(a, p, mode, st);
+    case DT_MXFP4: return launch_gemv_mxfp4(a, p, mode, st);
     case DT_F32: return launch_gemv_f32(a, p, mode, st);
   }
   return hipErrorInvalidValue;

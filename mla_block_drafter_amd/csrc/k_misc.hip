@@ -127,7 +127,14 @@ __device__ __forceinline__ long long code_offset(const PackedMat& w, int n, int 
   }
   const int kb = k >> 5, q = (k >> 3) & 3, i = k & 7;
   if (w.fmt == DT_BF16) return (((long long)tile * w.KB + kb) * 64 + q * 16 + r16) * 16 + i * 2;
+  if (w.fmt == DT_MXFP4)  // byte holding element k (low nibble when k is even)
+    return (((long long)tile * (w.KB >> 2) + (kb >> 2)) * 64 + q * 16 + r16) * 16 + (kb & 3) * 4 + (i >> 1);
   return (((long long)tile * (w.KB >> 1) + (kb >> 1)) * 64 + q * 16 + r16) * 16 + (kb & 1) * 8 + i;
+}
+
+// Byte offset of the E8M0 scale code of (tile, row r16, k block kb).
+__device__ __forceinline__ long long mx_scale_offset(const PackedMat& w, int tile, int r16, int kb) {
+  return (((long long)tile * (w.KB >> 2) + (kb >> 2)) * 16 + r16) * 4 + (kb & 3);
 }
 
 // One thread per (destination row, 32-wide k block).
@@ -140,6 +147,17 @@ __global__ __launch_bounds__(256) void k_repack(RepackArgs a) {
   int n;  // destination logical row
   if (a.xf == XF_NORMAL) n = a.row0 + lr;
   else n = lr;
+  if (a.src_fmt == DT_MXFP4) {  // whole bytes (element pairs) and the block's scale code
+    const unsigned char* blk = (const unsigned char*)a.src + (long long)lr * (a.src_cols / 32 * 17) + kb * 17;
+    int tile, r16;
+    for (int kk = 0; kk < 32; kk += 2) {
+      const long long off = code_offset(a.dst, n, kb * 32 + kk, tile, r16);
+      a.codes[off] = blk[1 + kk / 2];
+    }
+    code_offset(a.dst, n, kb * 32, tile, r16);
+    ((unsigned char*)a.scales)[mx_scale_offset(a.dst, tile, r16, kb)] = blk[0];
+    return;
+  }
   for (int kk = 0; kk < 32; ++kk) {
     const int k = kb * 32 + kk;
     if (k >= K) break;
@@ -206,6 +224,12 @@ __global__ __launch_bounds__(256) void k_dequant(PackedMat w, float* out) {
       float sc = 1.f;
       if (w.fmt == DT_BF16) {
         b = *(const bf16x8*)(w.codes + off);
+      } else if (w.fmt == DT_MXFP4) {
+        const uint32_t c = *(const uint32_t*)(w.codes + off);
+        const uint32_t sw = ((const uint32_t*)w.scales)[((long long)tile * (w.KB >> 2) + (kb >> 2)) * 16 + r16];
+        const int j = kb & 3;
+        b = fp4x8_to_bf16x8(c, j == 0 ? e8m0_f32<0>(sw) : j == 1 ? e8m0_f32<1>(sw) : j == 2 ? e8m0_f32<2>(sw)
+                                                                                            : e8m0_f32<3>(sw));
       } else {
         const u32x2 c = *(const u32x2*)(w.codes + off);
         if (w.fmt == DT_Q8_0) {

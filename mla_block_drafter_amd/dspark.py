@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 # ---- constants mirrored from include/dspark.h ----
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENODEVICE = 0, -1, -2, -3, -4, -5
-DT_F32, DT_BF16, DT_Q8_0, DT_FP8_E4M3 = 0, 1, 2, 3
+DT_F32, DT_BF16, DT_Q8_0, DT_FP8_E4M3, DT_MXFP4 = 0, 1, 2, 3, 4
 W_FC, W_FC_NORM, W_FINAL_NORM, W_LM_HEAD = 0, 1, 2, 3
 W_MARKOV_W1, W_MARKOV_W2, W_CONF_W, W_CONF_B = 4, 5, 6, 7
 W_LAYER_BASE, W_LAYER_STRIDE = 16, 16
@@ -23,7 +23,7 @@ L_KEYS = ["in_norm", "q_a", "q_a_norm", "kv_a", "kv_a_norm", "q_b", "kv_b", "o",
           "post_norm", "gate", "up", "down"]
 CFG_LAYERS_ONLY = 1
 
-FMT_CODE = {"f32": DT_F32, "bf16": DT_BF16, "q8_0": DT_Q8_0, "fp8_e4m3": DT_FP8_E4M3}
+FMT_CODE = {"f32": DT_F32, "bf16": DT_BF16, "q8_0": DT_Q8_0, "fp8_e4m3": DT_FP8_E4M3, "mxfp4": DT_MXFP4}
 TOP_IDS = {"fc": W_FC, "fc_norm": W_FC_NORM, "final_norm": W_FINAL_NORM, "lm_head": W_LM_HEAD,
            "markov_w1": W_MARKOV_W1, "markov_w2": W_MARKOV_W2, "conf_w": W_CONF_W, "conf_b": W_CONF_B}
 

@@ -3,7 +3,7 @@
 Every weight and every latent-cache row is counted once per pass; re-reads
 (W2 once per Markov step, key tiles per query-row group, split-K partials) are
 not counted.  Q8_0 = 34 bytes per 32 weights, FP8 = 1 byte per weight + one
-fp32 scale per row, bf16 = 2, f32 = 4.  W1 contributes only the gathered
+fp32 scale per row, MXFP4 = 17 bytes per 32 weights, bf16 = 2, f32 = 4.  W1 contributes only the gathered
 rows (n_seq * block rows).  Outputs and intermediate activations are not
 counted.
 """
@@ -19,6 +19,8 @@ def storage_bytes(fmt: str, rows: int, cols: int) -> int:
         return rows * (cols // 32) * 34
     if fmt == C.FP8:
         return rows * cols + 4 * rows
+    if fmt == C.MXFP4:
+        return rows * (cols // 32) * 17
     if fmt == C.BF16:
         return 2 * rows * cols
     return 4 * rows * cols

@@ -91,6 +91,18 @@ def test_full_size_q8_0_layer_with_mlp_ctx8192():
     _layer_case_with_inputs(one, stored, np.ascontiguousarray(x_in), inp, with_mlp=True)
 
 
+def test_full_size_mxfp4_layer_with_mlp_ctx8192():
+    """Layer 0 of the full geometry with MXFP4 q_b, o_proj and MLP (the
+    tensor selection of the 4-bit builds), ctx 8192, MLP included."""
+    full = C.CFG3.replace(name="full_mxfp4_bs1_ctx8192", formats=C.MX4)
+    one = full.replace(model=C.ModelConfig(n_layers=1), attn_only=False)
+    names = [n for n in C.tensor_names(full.model) if n.startswith("L0.")]
+    stored = gen.make_weights(full, names=names)
+    inp = gen.make_inputs(full.replace(model=C.ModelConfig(n_layers=1)))
+    x_in = gen.normal((7, full.model.hidden), full.seed, 4243)
+    _layer_case_with_inputs(one, stored, np.ascontiguousarray(x_in), inp, with_mlp=True)
+
+
 def _golden(k):
     path = os.path.join(GOLDEN, f"pass_cfg{k}.npz")
     if not os.path.exists(path):
@@ -98,7 +110,7 @@ def _golden(k):
     return np.load(path)
 
 
-@pytest.mark.parametrize("k", [3, 4, 5])
+@pytest.mark.parametrize("k", [3, 4, 5, 6])
 def test_full_pass_vs_oracle_golden(k):
     from tests.gpu_common import GpuWorkload
     gold = _golden(k)

@@ -33,6 +33,7 @@ FORMATS = {
     "bf16": C.ALL_BF16,
     "q8_0": C.Q8,
     "fp8": C.FP8_PC,
+    "mxfp4": C.MX4,
     "f32w_bf16kv": C.Formats(fc="f32", q_a="f32", q_b="f32", kv_b="f32", o="f32", mlp="f32",
                               lm_head="f32", markov="f32"),
 }
@@ -70,7 +71,7 @@ def test_small_ragged_all_formats(fmt):
     print(fmt, "near-ties", ties, flush=True)
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["q8_0", "bf16", "fp8", "mxfp4"])
 def test_small_bs1_formats(fmt):
     """One sequence (7 activation rows): the hi/lo activation paths, including
     the int8 MFMA path of Q8_0 weights."""
@@ -104,9 +105,11 @@ def test_small_far_dominant_key_bf16():
 
 def test_dequant_bit_exact():
     """Decoding the repacked planes gives exactly the oracle's decoded values
-    (Q8_0 d*q and bf16 exact in fp32; FP8 s*e4m3(q) correctly rounded)."""
+    (Q8_0 d*q, MXFP4 X*e2m1(q) and bf16 exact in fp32; FP8 s*e4m3(q)
+    correctly rounded)."""
     from mla_block_drafter_amd import dspark as D
     for fmt, names in [("q8_0", ["L0.q_b", "L1.o", "L0.down", "fc"]), ("fp8", ["L0.q_b", "L1.down", "fc"]),
+                       ("mxfp4", ["L0.q_b", "L1.o", "L1.down", "fc"]),
                        ("bf16", ["lm_head", "L0.o", "markov_w2"]), ("f32w_bf16kv", ["L0.o", "lm_head"])]:
         wl = C.Workload("deq", SMALL, FORMATS[fmt], seed=31, kv_lens=(5,))
         g = _gw(wl)
