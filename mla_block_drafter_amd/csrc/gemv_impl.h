@@ -537,8 +537,9 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
       };
       if constexpr (MT == 1 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
         // prepared fragments: a quad's four activation fragments are loaded
-        // with its weights, stage by stage (U quads x TPW tiles)
-        constexpr int U = 2;
+        // with its weights, stage by stage (U quads x TPW tiles; one quad per
+        // stage measured as fast as two or four, with fewer registers)
+        constexpr int U = 1;
         const __amdgpu_buffer_rsrc_t ar = buf_rsrc(afrag, (uint32_t)(KB * 1024));
         struct Stage {
           u32x4 w[U][TPW];

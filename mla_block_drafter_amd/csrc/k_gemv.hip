@@ -29,8 +29,9 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   p.TPW = 1;
   if (p.MT == 1 && w.fmt == DT_MXFP4) {
     // four tiles share each quad's four activation fragments (a 16-row
-    // tile's quad of E2M1 codes is only 1 KiB)
-    if (w.TG % 4 == 0 && T / 4 >= (allow_split ? 64 : 256)) p.TPW = 4;
+    // tile's quad of E2M1 codes is only 1 KiB); with a short k range
+    // (q_b's 1536) two tiles per wave measured faster
+    if (w.TG % 4 == 0 && w.KB >= 128 && T / 4 >= (allow_split ? 64 : 256)) p.TPW = 4;
     else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 64 : 256)) p.TPW = 2;
   } else if (p.MT == 1) {
     if (w.TG % 4 == 0 && ((gather && T / 4 >= 256) || (allow_split && T / 4 >= 448))) p.TPW = 4;

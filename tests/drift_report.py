@@ -1,6 +1,6 @@
 """Drift report at the full geometry (run on a GPU machine, not collected by pytest):
 
-    python -m tests.drift_report [--dist gauss|heavy] [--n-seq 16] [--formats q8_0,fp8,bf16]
+    python -m tests.drift_report [--dist gauss|heavy] [--n-seq 16] [--formats q8_0,fp8,mxfp4,bf16]
 
 Reference: the oracle with the fp32 master weights; variants: the GPU draft
 pass with the weights stored as each format (same master values), on the
@@ -20,13 +20,13 @@ def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--dist", default="gauss")
     ap.add_argument("--n-seq", type=int, default=16)
-    ap.add_argument("--formats", default="q8_0,fp8,bf16")
+    ap.add_argument("--formats", default="q8_0,fp8,mxfp4,bf16")
     args = ap.parse_args()
     import torch
     from synth import configs as C, gen
     from tests import drift as DR
     from tests.gpu_common import GpuWorkload
-    fmts = {"bf16": C.ALL_BF16, "q8_0": C.Q8, "fp8": C.FP8_PC}
+    fmts = {"bf16": C.ALL_BF16, "q8_0": C.Q8, "fp8": C.FP8_PC, "mxfp4": C.MX4}
     lens = tuple(int(v) for v in np.random.default_rng(11).integers(256, 2048, size=args.n_seq))
     base = C.Workload(f"drift_full_{args.dist}", C.FULL, dataclasses.replace(C.ALL_F32, kv_cache=C.BF16,
                                                                             captured=C.BF16),

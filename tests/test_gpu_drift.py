@@ -23,7 +23,7 @@ def _need_gpu():
     D.lib()
 
 
-FORMATS = {"bf16": C.ALL_BF16, "q8_0": C.Q8, "fp8": C.FP8_PC}
+FORMATS = {"bf16": C.ALL_BF16, "q8_0": C.Q8, "fp8": C.FP8_PC, "mxfp4": C.MX4}
 F32_WEIGHTS = dataclasses.replace(C.ALL_F32, kv_cache=C.BF16, captured=C.BF16)
 
 
