@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append timing")
+    ap.add_argument("--no-sampling", action="store_true",
+                    help="skip the sampled-pass and block-verification timings")
     ap.add_argument("--page-size", type=int, default=0,
                     help="latent caches as page pools of this many tokens (seeded page placement)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -274,6 +276,66 @@ def main():
                   "gbs": round(app_bytes / (app_ms * 1e-3) / 1e9, 1)}
         log(f"[bench] cache append of {n_new} rows: {app_ms * 1e3:.1f} us")
 
+    sampling = None
+    if not args.no_sampling:
+        # probabilistic drafting (Gumbel-max draws from resident uniforms at
+        # temperature 1) and block verification of the sampled block against
+        # synthetic target logits (the draft's logits plus noise)
+        V = m.vocab
+        u = torch.rand((n, B, V), generator=torch.Generator(device=dev).manual_seed(wl.seed), device=dev)
+        u.clamp_(1e-7, 1 - 1e-7)
+        for _ in range(args.warmup):
+            model.draft_block(cap, kv, offs, prev, wl.total_ctx, tokens, conf, ws, sample_u=u, temperature=1.0,
+                              page_size=args.page_size, block_table=table)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            model.draft_block(cap, kv, offs, prev, wl.total_ctx, tokens, conf, ws, sample_u=u, temperature=1.0,
+                              page_size=args.page_size, block_table=table)
+        b.record()
+        torch.cuda.synchronize()
+        samp_ms = a.elapsed_time(b) / K
+        dlog = torch.empty((n, B, V), dtype=torch.float32, device=dev)
+        model.draft_block(cap, kv, offs, prev, wl.total_ctx, tokens, conf, ws, logits=dlog, sample_u=u,
+                          temperature=1.0, page_size=args.page_size, block_table=table)
+        g = torch.Generator(device=dev).manual_seed(wl.seed + 1)
+        tlog = torch.cat([dlog, dlog[:, -1:]], dim=1) + torch.randn((n, B + 1, V), generator=g, device=dev)
+        r = torch.rand((n, B + 1), generator=g, device=dev)
+        out_len = torch.empty(n, dtype=torch.int32, device=dev)
+        out_tok = torch.empty(n, dtype=torch.int32, device=dev)
+        vws = torch.empty(D.verify_workspace_bytes(n, B), dtype=torch.uint8, device=dev)
+        def verify():
+            D.verify(tokens, dlog, tlog, r, 1.0, D.VERIFY_BLOCK, out_len, out_tok, workspace=vws)
+
+        for _ in range(args.warmup):
+            verify()
+        torch.cuda.synchronize()
+        # eager calls through the Python binding are host-bound (four small
+        # launches): the device time is taken from a captured graph's replays
+        vs = torch.cuda.Stream()
+        vs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(vs):
+            verify()
+        torch.cuda.current_stream().wait_stream(vs)
+        vg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(vg):
+            verify()
+        vg.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(K):
+            vg.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ver_ms = a.elapsed_time(b) / K
+        ver_bytes = 4 * n * V * (2 * B + 1)  # draft and target logits once
+        sampling = {"sampled_pass_us": round(samp_ms * 1e3, 2), "verify_block_us": round(ver_ms * 1e3, 2),
+                    "verify_algorithmic_bytes": ver_bytes,
+                    "verify_gbs": round(ver_bytes / (ver_ms * 1e-3) / 1e9, 1),
+                    "accepted": out_len.cpu().tolist()}
+        log(f"[bench] sampled pass {samp_ms * 1e3:.1f} us; block verification {ver_ms * 1e3:.1f} us")
+
     copy_gbs = copy_probe_gbs(torch)
     log(f"[bench] device copy probe: {copy_gbs:.0f} GB/s")
     total_bytes = A.total_bytes(wl)
@@ -317,6 +379,7 @@ def main():
                      "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "cache_append": append,
+        "sampling": sampling,
     }
     print(json.dumps(out), flush=True)
 

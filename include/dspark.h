@@ -292,7 +292,7 @@ int32_t dspark_cache_append(const dspark_model* m, const dspark_append_in* in, v
 #define DSPARK_VERIFY_TOKEN 0
 #define DSPARK_VERIFY_BLOCK 1
 typedef struct dspark_verify_in {
-  int32_t n_seq, block, vocab, method;
+  int32_t n_seq, block, vocab, method;  /* 1 <= block <= 63                       */
   float temperature;            /* > 0                                           */
   int32_t pad_;
   const int32_t* draft;         /* [n_seq][block]                                */
@@ -301,7 +301,9 @@ typedef struct dspark_verify_in {
   const float* u;               /* [n_seq][block + 1] uniforms in [0, 1)          */
 } dspark_verify_in;
 
-/* Workspace bytes dspark_verify needs (0 and the error text on bad sizes). */
+/* Workspace bytes dspark_verify needs (0 and the error text on bad sizes):
+ * per-chunk normalisers and residual masses and per-row scalars, caller-owned
+ * device memory, 256-byte aligned. */
 size_t dspark_verify_workspace_bytes(int32_t n_seq, int32_t block);
 
 /* Errors: EINVAL (nulls, sizes, method, temperature), EWORKSPACE, EHIP. */

@@ -1217,19 +1217,20 @@ int32_t dspark_cache_append(const dspark_model* m, const dspark_append_in* in, v
 // ------------------------------------------------------------ verification --
 size_t dspark_verify_workspace_bytes(int32_t n_seq, int32_t block) {
   g_err.clear();
-  if (n_seq < 1 || block < 1 || block > 64) {
+  if (n_seq < 1 || block < 1 || block > 63) {
     fail(DSPARK_EINVAL, "verify workspace: bad n_seq / block");
     return 0;
   }
   const long long nch = verify_nch();
-  return (size_t)(rup((long long)n_seq * (block + 1) * nch * 4 * 4, 256) + (long long)n_seq * block * nch * 2 * 4);
+  return (size_t)(rup((long long)n_seq * (block + 1) * nch * 4 * 4, 256) + rup((long long)n_seq * block * nch * 2 * 4, 256) +
+                  (long long)n_seq * (block + 1) * 8 * 4);
 }
 
 int32_t dspark_verify(const dspark_verify_in* in, int32_t* out_len, int32_t* out_token, void* workspace,
                       size_t ws_bytes, void* stream) {
   g_err.clear();
   if (!in || !out_len || !out_token) return fail(DSPARK_EINVAL, "in / out_len / out_token is NULL");
-  if (in->n_seq < 1 || in->block < 1 || in->block > 64 || in->vocab < 1)
+  if (in->n_seq < 1 || in->block < 1 || in->block > 63 || in->vocab < 1)
     return fail(DSPARK_EINVAL, "bad n_seq / block / vocab");
   if (in->method != DSPARK_VERIFY_TOKEN && in->method != DSPARK_VERIFY_BLOCK) return fail(DSPARK_EINVAL, "bad method");
   if (!(in->temperature > 0.f)) return fail(DSPARK_EINVAL, "temperature must be > 0");
@@ -1248,7 +1249,9 @@ int32_t dspark_verify(const dspark_verify_in* in, int32_t* out_len, int32_t* out
   a.tlog = in->target_logits;
   a.u = in->u;
   a.stats = (float*)workspace;
-  a.resid = (float*)((unsigned char*)workspace + rup((long long)in->n_seq * (in->block + 1) * verify_nch() * 4 * 4, 256));
+  const long long stats_b = rup((long long)in->n_seq * (in->block + 1) * verify_nch() * 4 * 4, 256);
+  a.resid = (float*)((unsigned char*)workspace + stats_b);
+  a.probs = (float*)((unsigned char*)workspace + stats_b + rup((long long)in->n_seq * in->block * verify_nch() * 2 * 4, 256));
   a.out_len = out_len;
   a.out_token = out_token;
   HIPCHK(launch_verify(a, (hipStream_t)stream));

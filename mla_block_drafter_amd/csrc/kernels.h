@@ -238,6 +238,7 @@ struct VerifyArgs {
   const float* u;             // [n_seq][block + 1] uniforms: acceptance, then the draw
   float* stats;               // [n_seq][block + 1][verify_nch()][4]
   float* resid;               // [n_seq][block][verify_nch()][2]
+  float* probs;               // [n_seq][block + 1][8] row normalisers, p(x), q(x), prefix weight
   int32_t* out_len; int32_t* out_token;
 };
 int verify_nch();

@@ -304,10 +304,11 @@ class Model:
 
 
 def verify(draft, draft_logits, target_logits, u, temperature: float, method: int, out_len, out_token,
-           stream=None) -> None:
+           stream=None, workspace=None) -> None:
     """Verification of sampled draft blocks (include/dspark.h, dspark_verify).
     draft int32 [n_seq][block]; draft_logits [n_seq][block][vocab];
-    target_logits [n_seq][block + 1][vocab]; u [n_seq][block + 1]."""
+    target_logits [n_seq][block + 1][vocab]; u [n_seq][block + 1]; workspace: a
+    uint8 device tensor of at least verify_workspace_bytes (allocated here if None)."""
     import torch
     n_seq, block = draft.shape
     vi = VerifyIn()
@@ -319,9 +320,16 @@ def verify(draft, draft_logits, target_logits, u, temperature: float, method: in
     nb = L.dspark_verify_workspace_bytes(int(n_seq), int(block))
     if nb == 0:
         raise DsparkError(EINVAL, last_error())
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    check(L.dspark_verify(C.byref(vi), out_len.data_ptr(), out_token.data_ptr(), ws.data_ptr(), nb,
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if workspace is None else workspace
+    check(L.dspark_verify(C.byref(vi), out_len.data_ptr(), out_token.data_ptr(), ws.data_ptr(), ws.numel(),
                           _stream_ptr(stream)))
+
+
+def verify_workspace_bytes(n_seq: int, block: int) -> int:
+    nb = lib().dspark_verify_workspace_bytes(int(n_seq), int(block))
+    if nb == 0:
+        raise DsparkError(EINVAL, last_error())
+    return int(nb)
 
 
 def accept_len(draft, verifier, out, stream=None) -> None:
