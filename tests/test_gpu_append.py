@@ -76,6 +76,13 @@ def test_append_small_q8_five_rows():
     _append_case(wl, 5, 100, 6, 1e-2)
 
 
+@pytest.mark.parametrize("name,formats", [("fp8", C.FP8_PC), ("mxfp4", C.MX4)])
+def test_append_small_fp8_mxfp4_fc(name, formats):
+    """fc in FP8 or MXFP4 (bf16 hi/lo activation fragments for the fc GEMM)."""
+    wl = C.Workload(f"append_small_{name}", C.small_model(), formats, seed=904, kv_lens=(10,), fixture_gains=True)
+    _append_case(wl, 6, 120, 9, 1e-2)
+
+
 def test_append_tiny_f32():
     _append_case(C.CFG1.replace(fixture_gains=True), 7, 64, 7, 1e-4)
 

@@ -103,6 +103,18 @@ def test_full_size_mxfp4_layer_with_mlp_ctx8192():
     _layer_case_with_inputs(one, stored, np.ascontiguousarray(x_in), inp, with_mlp=True)
 
 
+def test_full_size_mxfp4_layer_with_mlp_four_ragged_sequences():
+    """As above for four sequences (28 activation rows: the MXFP4 GEMMs take
+    two 16-row m-tiles instead of the hi/lo split) with ragged cache lengths."""
+    full = C.CFG3.replace(name="full_mxfp4_4seq", formats=C.MX4, kv_lens=(300, 2048, 77, 5000))
+    one = full.replace(model=C.ModelConfig(n_layers=1), attn_only=False)
+    names = [n for n in C.tensor_names(full.model) if n.startswith("L0.")]
+    stored = gen.make_weights(full, names=names)
+    inp = gen.make_inputs(full.replace(model=C.ModelConfig(n_layers=1)))
+    x_in = gen.normal((4 * 7, full.model.hidden), full.seed, 4244)
+    _layer_case_with_inputs(one, stored, np.ascontiguousarray(x_in), inp, with_mlp=True)
+
+
 def _golden(k):
     path = os.path.join(GOLDEN, f"pass_cfg{k}.npz")
     if not os.path.exists(path):
