@@ -625,6 +625,68 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
           }
         }
       }
+    } else if constexpr (FMT == DT_FP8 && MT == 1 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
+      // FP8 weights, prepared fragments: a 1 KiB chunk holds a pair of k
+      // blocks of a tile; its two activation fragments are loaded with it,
+      // stage by stage (U pairs x TPW tiles, 8 KiB of weights per stage).
+      // The per-row scales are applied in the epilogue.
+      constexpr int U = 8 / TPW;
+      const int KP = KB >> 1, p1 = kb1 >> 1;
+      const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)t0 * KP * 1024,
+                                                 (uint32_t)(TPW * KP * 1024));
+      const __amdgpu_buffer_rsrc_t ar = buf_rsrc(afrag, (uint32_t)(KB * 1024));
+      const uint32_t l16 = lane * 16;
+      struct Stage {
+        u32x4 w[U][TPW];
+        u32x4 x[U][2];
+      };
+      auto load_stage = [&](Stage& st, int q0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int p = q0 + u;
+          const bool ok = p < p1;
+#pragma unroll
+          for (int j = 0; j < TPW; ++j)
+            st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                wr, ok ? (uint32_t)((j * KP + p) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            st.x[u][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                ar, ok ? (uint32_t)((2 * p + h) * 1024) + l16 : BUF_OOB, 0, 0));
+        }
+      };
+      auto compute_stage = [&](const Stage& st, int q0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (q0 + u >= p1) break;
+          const bf16x8 A0 = __builtin_bit_cast(bf16x8, st.x[u][0]), A1 = __builtin_bit_cast(bf16x8, st.x[u][1]);
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, fp8x8_to_bf16x8(st.w[u][j][0], st.w[u][j][1]),
+                                                                acc[0][j], 0, 0, 0);
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, fp8x8_to_bf16x8(st.w[u][j][2], st.w[u][j][3]),
+                                                                acc[0][j], 0, 0, 0);
+          }
+        }
+      };
+      Stage sa, sb;
+      const int q0 = kb0 >> 1;
+      const int nst = (p1 - q0 + U - 1) / U;
+      load_stage(sa, q0);
+      int q = q0, st = 0;
+      for (; st + 2 < nst; st += 2, q += 2 * U) {
+        load_stage(sb, q + U);
+        compute_stage(sa, q);
+        load_stage(sa, q + 2 * U);
+        compute_stage(sb, q + U);
+      }
+      if (st + 1 < nst) {
+        load_stage(sb, q + U);
+        compute_stage(sa, q);
+        compute_stage(sb, q + U);
+      } else if (nst > 0) {
+        compute_stage(sa, q);
+      }
     } else if constexpr (FMT == DT_BF16 && AMODE == A_GLOBAL && MODE != GEMV_MARKOV) {
       // bf16 weights, prepared bf16 activation fragments: both loaded per
       // stage of U k blocks (tile j, k block kb: 1 KiB of weights; m-tile mt:

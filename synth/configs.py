@@ -135,7 +135,8 @@ CFG4 = Workload("full_bf16_bs1_ctx98304", FULL, ALL_BF16, SEED_BASE + 4, (98304,
 CFG5 = Workload("full_fp8_bs16_ragged", FULL, FP8_PC, SEED_BASE + 5, _cfg5_lens())
 
 CFG6 = Workload("full_mxfp4_bs1_ctx8192", FULL, MX4, SEED_BASE + 6, (8192,))
-PRESETS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5, 6: CFG6}
+CFG7 = Workload("full_fp8_bs1_ctx8192", FULL, FP8_PC, SEED_BASE + 7, (8192,))
+PRESETS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5, 6: CFG6, 7: CFG7}
 
 
 def small_model(**kw) -> ModelConfig:

@@ -2,7 +2,7 @@
 
 Calls only synth (seeded inputs) and oracle (float64 reference).  Usage:
 
-    python tests/golden/make_golden.py 3 4 5 6
+    python tests/golden/make_golden.py 3 4 5 6 7
 
 Per workload it stores, in tests/golden/pass_cfg<k>.npz:
   tokens [n_seq, block], conf [n_seq, block]      free-running oracle draft

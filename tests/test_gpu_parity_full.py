@@ -122,7 +122,7 @@ def _golden(k):
     return np.load(path)
 
 
-@pytest.mark.parametrize("k", [3, 4, 5, 6])
+@pytest.mark.parametrize("k", [3, 4, 5, 6, 7])
 def test_full_pass_vs_oracle_golden(k):
     from tests.gpu_common import GpuWorkload
     gold = _golden(k)
