@@ -1,4 +1,4 @@
-"""Drift report at the full geometry (run on a GPU machine, not collected by pytest):
+"""Drift report at the full geometry (needs the GPU; not collected by pytest):
 
     python -m tests.drift_report [--dist gauss|heavy] [--n-seq 16] [--formats q8_0,fp8,mxfp4,bf16]
 
