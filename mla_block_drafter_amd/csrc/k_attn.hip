@@ -469,8 +469,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 
 // Merge the slots of each (sequence, row) in slot order and write the
 // un-absorb fragments: with w_p = exp(m_p - M) l_p and the stored
-// Ohat_p = O_p / l_p, O = sum_p w_p Ohat_p / sum_p w_p.  Each thread owns two
-// adjacent dims (one 32-bit word of the fp16 row).
+// Ohat_p = O_p / l_p, O = sum_p w_p Ohat_p / sum_p w_p.  Each lane owns eight
+// adjacent dims (one 16-byte load of the fp16 row per slot); wave g sums the
+// slots p = g mod 4 in slot order, the four waves' sums are added in a fixed
+// order, and each wave writes a quarter of the dims.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   __shared__ float wgt[MAX_COMBINE_SLOTS];
   __shared__ float red[4];
@@ -498,26 +500,46 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   const float invL = 1.f / l;
   const int i = row / a.nh, h = row % a.nh;
   const int m = s * a.block + i;
-  const int rw = a.r / 2;  // 32-bit words per stored row
-  const uint32_t* op = (const uint32_t*)(a.o_part + ((long long)row * a.slots + base) * a.r);
-  for (int d2 = threadIdx.x; d2 < rw; d2 += 256) {
-    float o0[4] = {0.f, 0.f, 0.f, 0.f}, o1[4] = {0.f, 0.f, 0.f, 0.f};
-    int p = 0;
-    for (; p + 4 <= ns; p += 4) {
+  // lane ln of wave g holds dims 8 ln .. 8 ln + 7 (one 16-byte load per
+  // slot) over slots g, g + 4, ...; four slots per lane in flight; the four
+  // waves' sums are added in a fixed order
+  const int g = threadIdx.x >> 6, ln = threadIdx.x & 63;
+  const int nl = a.r / 8;  // lanes holding data (kv_lora % 16 == 0)
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (ln < nl) {
+    const u32x4* op = (const u32x4*)(a.o_part + ((long long)row * a.slots + base) * a.r) + ln;
+    for (int p0 = g; p0 < ns; p0 += 16) {
+      u32x4 v[4];
+      float w[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t v = op[(long long)(p + u) * rw + d2];
-        o0[u] += wgt[p + u] * fp16_bits_to_f32(v & 0xFFFFu);
-        o1[u] += wgt[p + u] * fp16_bits_to_f32(v >> 16);
+        const int p = p0 + 4 * u;
+        v[u] = p < ns ? op[(long long)p * nl] : u32x4{0u, 0u, 0u, 0u};
+        w[u] = p < ns ? wgt[p] : 0.f;
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += w[u] * fp16_bits_to_f32(v[u][e] & 0xFFFFu);
+          acc[2 * e + 1] += w[u] * fp16_bits_to_f32(v[u][e] >> 16);
+        }
     }
-    for (; p < ns; ++p) {
-      const uint32_t v = op[(long long)p * rw + d2];
-      o0[0] += wgt[p] * fp16_bits_to_f32(v & 0xFFFFu);
-      o1[0] += wgt[p] * fp16_bits_to_f32(v >> 16);
+  }
+  // every wave stores its sums, then wave g writes dims 8 ln + 2g, 8 ln + 2g + 1
+  __shared__ float gsum[4][8][64];
+  if (ln < nl) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gsum[g][e][ln] = acc[e];
+  }
+  __syncthreads();
+  if (ln < nl) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = 2 * g + k;
+      frag_put(a.fd_uv, h, m, 8 * ln + e,
+               ((gsum[0][e][ln] + gsum[1][e][ln]) + (gsum[2][e][ln] + gsum[3][e][ln])) * invL);
     }
-    frag_put(a.fd_uv, h, m, 2 * d2, ((o0[0] + o0[1]) + (o0[2] + o0[3])) * invL);
-    frag_put(a.fd_uv, h, m, 2 * d2 + 1, ((o1[0] + o1[1]) + (o1[2] + o1[3])) * invL);
   }
 }
 
@@ -605,7 +627,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st) {
-  if (a.slots > MAX_COMBINE_SLOTS || a.r % 2) return hipErrorInvalidValue;
+  if (a.slots > MAX_COMBINE_SLOTS || a.r % 8 || a.r > 512) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_attn_combine, dim3(a.rows, a.n_seq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
