@@ -981,6 +981,17 @@ hipError_t dispatch_out(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
     if (p.TPW == 2) return go<FMT, 1, 2, MODE>(a, p, st);
     return go<FMT, 1, 1, MODE>(a, p, st);
   }
+  if (p.TPW == 4) {
+    switch (p.MT) {
+      case 2: return go<FMT, 2, 4, MODE>(a, p, st);
+      case 3: return go<FMT, 3, 4, MODE>(a, p, st);
+      case 4: return go<FMT, 4, 4, MODE>(a, p, st);
+      case 5: return go<FMT, 5, 4, MODE>(a, p, st);
+      case 6: return go<FMT, 6, 4, MODE>(a, p, st);
+      case 7: return go<FMT, 7, 4, MODE>(a, p, st);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (p.MT) {
     case 2: return go<FMT, 2, 1, MODE>(a, p, st);
     case 3: return go<FMT, 3, 1, MODE>(a, p, st);

@@ -33,6 +33,13 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
     // (q_b's 1536) two tiles per wave measured faster
     if (w.TG % 4 == 0 && w.KB >= 128 && T / 4 >= (allow_split ? 64 : 256)) p.TPW = 4;
     else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 64 : 256)) p.TPW = 2;
+  } else if (p.MT > 1) {
+    // several m-tiles: four tiles per wave share every activation fragment
+    // load (with one, the fragments of all m-tiles were re-read from L2 for
+    // every 16 weight rows).  Not for eight m-tiles (their accumulators alone
+    // take 128 registers) nor for the per-head W_UK / W_UV groups (measured
+    // slower there).
+    if (!gather && p.MT <= 7 && w.ngroups == 1 && w.TG % 4 == 0 && T / 4 >= 64) p.TPW = 4;
   } else if (p.MT == 1) {
     if (w.TG % 4 == 0 && ((gather && T / 4 >= 256) || (allow_split && T / 4 >= 448))) p.TPW = 4;
     else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 128 : 256)) p.TPW = 2;
