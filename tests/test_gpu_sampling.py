@@ -201,3 +201,54 @@ def test_verify_matches_oracle(method, V):
         assert int(out_len[s]) == tau and int(out_tok[s]) == y, (s, int(out_len[s]), tau, int(out_tok[s]), y)
         lens.append(tau)
     print(method, V, "accepted", lens, flush=True)
+
+
+@pytest.mark.parametrize("method", ["token", "block"])
+def test_verify_single_token_blocks(method):
+    """Blocks of one drafted token (the degenerate block length) over five
+    sequences: the same decisions as the oracle."""
+    from mla_block_drafter_amd import dspark as D
+    n, B, T, V = 5, 1, 1.0, 1000
+    rng = np.random.default_rng(77 + (method == "block"))
+    drafts, dls, tls, us = [], [], [], []
+    while len(drafts) < n:
+        dl = (2.0 * rng.standard_normal((B, V))).astype(np.float32)
+        tl = (dl[np.r_[0:B, B - 1]] + rng.uniform(0.0, 2.0) * rng.standard_normal((B + 1, V))).astype(np.float32)
+        q = VF.softmax_t(dl, T)
+        draft = np.array([VF.inverse_cdf(q[0], rng.random())], np.int32)
+        r = rng.random(B + 1).astype(np.float32)
+        if _margins_ok(draft, np.asarray(dl, np.float64), np.asarray(tl, np.float64), np.asarray(r, np.float64),
+                       T, method):
+            drafts.append(draft), dls.append(dl), tls.append(tl), us.append(r)
+    out_len = torch.full((n,), -5, dtype=torch.int32, device="cuda")
+    out_tok = torch.full((n,), -5, dtype=torch.int32, device="cuda")
+    D.verify(torch.from_numpy(np.stack(drafts)).cuda(), torch.from_numpy(np.stack(dls)).cuda(),
+             torch.from_numpy(np.stack(tls)).cuda(), torch.from_numpy(np.stack(us)).cuda(), T,
+             D.VERIFY_TOKEN if method == "token" else D.VERIFY_BLOCK, out_len, out_tok)
+    torch.cuda.synchronize()
+    fn = VF.token_verify if method == "token" else VF.block_verify
+    for s in range(n):
+        tau, y = fn(drafts[s], VF.softmax_t(np.asarray(dls[s], np.float64), T),
+                    VF.softmax_t(np.asarray(tls[s], np.float64), T), np.asarray(us[s][:B], np.float64), float(us[s][B]))
+        assert (int(out_len[s]), int(out_tok[s])) == (tau, y), s
+
+
+def test_sampled_draft_paged_matches_packed():
+    """Sampling over page pools draws exactly the packed pass's tokens."""
+    from tests.gpu_common import GpuWorkload
+    wl = C.Workload("sample_paged", C.small_model(), C.ALL_BF16, seed=1103, kv_lens=(0, 37, 300), fixture_gains=True)
+    g = GpuWorkload(wl)
+    m = wl.model
+    du = torch.from_numpy(_uniforms((wl.n_seq, m.block, m.vocab), 8)).cuda()
+    outs = []
+    for paged in (False, True):
+        if paged:
+            g.use_pages(64, seed=3)
+        tokens = torch.empty((wl.n_seq, m.block), dtype=torch.int32, device="cuda")
+        conf = torch.empty((wl.n_seq, m.block), dtype=torch.float32, device="cuda")
+        g.model.draft_block(g.cap, g.kv, g.offs, g.prev, wl.total_ctx, tokens, conf, g.ws, sample_u=du,
+                            temperature=0.8, page_size=g.page_size, block_table=g.table)
+        torch.cuda.synchronize()
+        outs.append((tokens.cpu().numpy(), conf.cpu().numpy()))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
