@@ -186,7 +186,7 @@ typedef struct dspark_block_in {
 } dspark_block_in;
 
 typedef struct dspark_block_out {
-  int32_t* tokens;  /* device int32 [n_seq][block], greedy draft (required)      */
+  int32_t* tokens;  /* device int32 [n_seq][block]: the draft, greedy or sampled (required) */
   float* conf;      /* device float [n_seq][block] confidence (required)         */
   float* logits;    /* optional device float [n_seq][block][vocab]: backbone
                        logits plus the Markov term, the argmax input; NULL = skip */
