@@ -149,8 +149,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the draft pass is not "
-              "sharded across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the draft pass is not "
+              "sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
