@@ -42,6 +42,9 @@ extern "C" {
 #define DSPARK_EWORKSPACE (-3)   /* buffer smaller than the size query returned  */
 #define DSPARK_EHIP (-4)         /* HIP runtime error; message has the HIP text  */
 #define DSPARK_ENODEVICE (-5)    /* no usable gfx950 device                      */
+#define DSPARK_EPLANONLY (-6)    /* every argument passed validation, but the model
+                                    is a plan-only handle (DSPARK_CFG_PLAN_ONLY):
+                                    it has no packed weights, nothing was enqueued */
 
 /* ---- storage formats of weights and activations ---- */
 #define DSPARK_DT_F32 0
@@ -95,6 +98,16 @@ extern "C" {
 #define DSPARK_CFG_LAYERS_ONLY 1 /* the table holds decoder layers only (no fc,
                                     lm_head, Markov or confidence tensors): only
                                     dspark_layer_forward may be called */
+#define DSPARK_CFG_PLAN_ONLY 2   /* dspark_model_create validates the config and
+                                    the table (data pointers must be non-NULL but
+                                    are never read) and plans the layouts without
+                                    a device: packed_buf may be NULL, no HIP call
+                                    is made.  The handle answers the size queries;
+                                    draft / layer / append / dequant calls on it
+                                    run their whole argument validation and then
+                                    return DSPARK_EPLANONLY (sizing buffers before
+                                    any device work, and host-side tests of the
+                                    validation) */
 
 typedef struct dspark_config {
   int32_t hidden, n_layers, n_heads, q_lora, kv_lora, qk_nope, qk_rope, v_head;
@@ -182,11 +195,20 @@ typedef struct dspark_block_in {
      Markov weights and n_seq <= 16 (EUNSUPPORTED otherwise).               */
   const float* sample_u;      /* device float [n_seq][block][vocab], in (0, 1)  */
   float temperature;          /* > 0 when sample_u is set                       */
-  int32_t pad2_;
+  /* Bound of the Markov rollout's wait for the previous position's argmax
+     (the rollout is one launch whose workgroups exchange each position's
+     argmax through memory): 0 = the library's bound (~4M polls, seconds);
+     n > 0: at most n polls per position; < 0: no wait at all, the rollout
+     expires at once (host-forced failure path for tests).  On expiry every
+     kernel still finishes, every token of the call is -1 and *status = 1. */
+  int32_t poll_limit;
 } dspark_block_in;
 
 typedef struct dspark_block_out {
-  int32_t* tokens;  /* device int32 [n_seq][block]: the draft, greedy or sampled (required) */
+  int32_t* tokens;  /* device int32 [n_seq][block]: the draft, greedy or sampled
+                       (required); all -1 when the Markov rollout's bounded wait
+                       expired (see poll_limit and status): never pass -1 tokens
+                       on to acceptance or verification                       */
   float* conf;      /* device float [n_seq][block] confidence (required)         */
   float* logits;    /* optional device float [n_seq][block][vocab]: backbone
                        logits plus the Markov term, the argmax input; NULL = skip */
@@ -196,6 +218,11 @@ typedef struct dspark_block_out {
                        hipEvent_t: events[2s] / events[2s+1] are recorded on the
                        stream right before / after stage s (profiling aid);
                        NULL = none                                               */
+  int32_t* status;  /* optional device int32 [1]: 0 when the pass completed, 1
+                       when the Markov rollout's wait expired (tokens are then
+                       -1); NULL = skip.  The library's bound is only reached
+                       when the rollout's workgroups cannot all be resident,
+                       e.g. kernels of other streams hold CUs for seconds     */
 } dspark_block_out;
 
 /* stages of one draft pass, for dspark_block_out.stage_events */
@@ -214,7 +241,11 @@ typedef struct dspark_block_out {
  * w_m . W1[t_{i-1}] + b).  Position of block token i = that sequence's cache
  * length + i.  Asynchronous on `stream`.  `workspace` must hold
  * dspark_workspace_bytes(m, in->n_seq, in->total_ctx) bytes, 256-byte aligned.
- * Errors: EINVAL (nulls, n_seq < 1, dtype mismatch), EWORKSPACE, EHIP. */
+ * Alignment: kv caches 16 bytes, captured / outputs / int arrays 4 bytes.
+ * Errors: EINVAL (nulls, misaligned pointers, n_seq < 1, total_ctx out of
+ * range, dtypes, bad page geometry, temperature <= 0 with sample_u),
+ * EUNSUPPORTED (n_seq > 16, sampling without the bf16 rollout, latent sizes
+ * without a kernel), EWORKSPACE, EPLANONLY, EHIP. */
 int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in,
                            dspark_block_out* out, void* workspace, size_t ws_bytes,
                            void* stream);
@@ -313,7 +344,10 @@ int32_t dspark_verify(const dspark_verify_in* in, int32_t* out_len, int32_t* out
 /* Acceptance length (huggingface.co card, "Why acceptance is so sensitive":
  * a block is accepted up to its first mismatch): out_len[s] = the largest
  * k <= block with draft[s][j] == verifier[s][j] for all j < k.  Device
- * pointers, asynchronous on `stream`.  Token values are not range-checked. */
+ * pointers, asynchronous on `stream` (NULL is the device's null stream, as
+ * everywhere in this header; the host form is dspark_accept_len_host).
+ * Token values are not range-checked.  Errors: EINVAL (nulls, negative
+ * sizes), EHIP. */
 int32_t dspark_accept_len(const int32_t* draft, const int32_t* verifier, int32_t n_seq,
                           int32_t block, int32_t* out_len, void* stream);
 

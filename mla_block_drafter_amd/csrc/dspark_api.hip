@@ -82,6 +82,7 @@ struct dspark_model {
   unsigned char* base = nullptr;
   long long bytes = 0;
   bool layers_only = false;
+  bool plan_only = false;  // DSPARK_CFG_PLAN_ONLY: validated and planned, no packed weights
   Mat fc, lm, w2;
   long long fc_norm = -1, final_norm = -1, conf_w = -1, conf_b = -1, w1 = -1, freqs = -1;
   int w1_fmt = DT_BF16, w1_ld = 0;
@@ -100,6 +101,7 @@ const dspark_weight* find_w(const dspark_weight* w, int n, int id) {
 
 int32_t check_cfg(const dspark_config* c) {
   if (!c) return fail(DSPARK_EINVAL, "config is NULL");
+  if (c->flags & ~(DSPARK_CFG_LAYERS_ONLY | DSPARK_CFG_PLAN_ONLY)) return fail(DSPARK_EINVAL, "unknown config flags");
   if (c->hidden <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->q_lora <= 0 || c->kv_lora <= 0 ||
       c->qk_nope <= 0 || c->qk_rope <= 0 || c->v_head <= 0 || c->block <= 0)
     return fail(DSPARK_EINVAL, "config has a non-positive dimension");
@@ -152,6 +154,7 @@ int32_t build_plan(const dspark_config* c, const dspark_weight* w, int n, dspark
   if (!w || n <= 0) return fail(DSPARK_EINVAL, "weight table empty");
   m.c = *c;
   m.layers_only = (c->flags & DSPARK_CFG_LAYERS_ONLY) != 0;
+  m.plan_only = (c->flags & DSPARK_CFG_PLAN_ONLY) != 0;
   const long long H = c->hidden, nh = c->n_heads, r = c->kv_lora, dr = c->qk_rope, dn = c->qk_nope, dv = c->v_head;
   const long long latent = r + dr;
   long long off = 0;
@@ -644,6 +647,8 @@ ResidPost resid_base(Ctx& C) {
   return a;
 }
 
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p) % a != 0; }
+
 int32_t check_ws(const Plan& P, void* ws, size_t ws_bytes) {
   if (!ws) return fail(DSPARK_EINVAL, "workspace is NULL");
   if ((uintptr_t)ws % 256) return fail(DSPARK_EINVAL, "workspace must be 256-byte aligned");
@@ -670,13 +675,20 @@ int32_t dspark_model_create(const dspark_config* cfg, const dspark_weight* w, in
   g_err.clear();
   if (!out) return fail(DSPARK_EINVAL, "out is NULL");
   *out = nullptr;
-  int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(DSPARK_ENODEVICE, "no HIP device");
   dspark_model* m = new dspark_model();
   int32_t rc = build_plan(cfg, w, n, *m);
   if (rc) {
     delete m;
     return rc;
+  }
+  if (m->plan_only) {  // no device, no packed buffer: sizes and validation only
+    *out = m;
+    return DSPARK_OK;
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    delete m;
+    return fail(DSPARK_ENODEVICE, "no HIP device");
   }
   if (!packed_buf || (uintptr_t)packed_buf % 256) {
     delete m;
@@ -778,12 +790,19 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   if (in->total_ctx < 0 || in->total_ctx > (1ll << 30)) return fail(DSPARK_EINVAL, "total_ctx out of range");
   if (!in->captured || !in->kv || !in->kv_offsets || !in->prev_token || !out->tokens || !out->conf)
     return fail(DSPARK_EINVAL, "a required pointer is NULL");
+  if (misaligned(in->captured, 4) || misaligned(in->kv_offsets, 4) || misaligned(in->prev_token, 4) ||
+      misaligned(in->forced_prev, 4) || misaligned(in->sample_u, 4) || misaligned(in->block_table, 4) ||
+      misaligned(out->tokens, 4) || misaligned(out->conf, 4) || misaligned(out->logits, 4) ||
+      misaligned(out->hidden, 4) || misaligned(out->status, 4))
+    return fail(DSPARK_EINVAL, "an input or output pointer is not 4-byte aligned");
   if (in->act_dtype != DSPARK_DT_F32 && in->act_dtype != DSPARK_DT_BF16)
     return fail(DSPARK_EINVAL, "act_dtype must be F32 or BF16");
   if (in->kv_dtype != DSPARK_DT_F32 && in->kv_dtype != DSPARK_DT_BF16)
     return fail(DSPARK_EINVAL, "kv_dtype must be F32 or BF16");
-  for (int l = 0; l < c.n_layers; ++l)
+  for (int l = 0; l < c.n_layers; ++l) {
     if (!in->kv[l] && in->total_ctx > 0) return fail(DSPARK_EINVAL, "kv[%d] is NULL", l);
+    if (misaligned(in->kv[l], 16)) return fail(DSPARK_EINVAL, "kv[%d] is not 16-byte aligned", l);
+  }
   const bool kv_f32 = in->kv_dtype == DSPARK_DT_F32;
   int page_log2 = -1;
   if (in->page_size != 0) {
@@ -807,6 +826,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   if (kv_f32 && (c.kv_lora + c.qk_rope > 1024)) return fail(DSPARK_EUNSUPPORTED, "f32 latent > 1024");
   int32_t rc = check_ws(C.P, workspace, ws_bytes);
   if (rc) return rc;
+  if (m->plan_only) return fail(DSPARK_EPLANONLY, "plan-only model: arguments valid, nothing enqueued");
   C.ws = (unsigned char*)workspace;
   C.st = (hipStream_t)stream;
   C.table = in->block_table;
@@ -904,6 +924,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.err = (unsigned*)(C.ws + P.merr);
     a.sample_u = in->sample_u;
     a.inv_temp = in->sample_u ? 1.f / in->temperature : 1.f;
+    a.spin_limit = in->poll_limit;
     HIPCHK(launch_markov_rollout(a, m->w2.pm.KB, C.st));
   }
   for (int i = 0; !rollout && i < c.block; ++i) {
@@ -948,6 +969,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.slots = rollout ? (const unsigned long long*)(C.ws + P.mslots) : nullptr;
     a.nwg = rollout ? markov_rollout_wgs(m->w2.pm.ngroups * m->w2.pm.TG) : 0;
     a.rollout_err = rollout ? (const unsigned*)(C.ws + P.merr) : nullptr;
+    a.status = out->status;
     HIPCHK(launch_markov_final(a, C.st));
   }
   HIPCHK(mark(2 * DSPARK_STAGE_MARKOV + 1));
@@ -974,6 +996,9 @@ int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_
     return fail(DSPARK_EUNSUPPORTED, "no bf16 attention kernel for this latent size");
   int32_t rc = check_ws(C.P, workspace, ws_bytes);
   if (rc) return rc;
+  if (misaligned(x_in, 16) || misaligned(x_out, 16) || misaligned(kv, 16) || misaligned(kv_offsets, 4))
+    return fail(DSPARK_EINVAL, "x_in / x_out / kv not 16-byte or kv_offsets not 4-byte aligned");
+  if (m->plan_only) return fail(DSPARK_EPLANONLY, "plan-only model: arguments valid, nothing enqueued");
   C.ws = (unsigned char*)workspace;
   C.st = (hipStream_t)stream;
   Plan& P = C.P;
@@ -1027,7 +1052,8 @@ bool row_view(const Mat& mt, int row0, int nrows, PackedMat& out) {
   if (!mt.present || p.ngroups != 1 || row0 % 16 || row0 + nrows > p.G) return false;
   const long long t0 = row0 / 16;
   out = p;
-  out.codes = p.codes + t0 * 16 * code_bytes(p.fmt, p.Kp);
+  // (a plan-only model has no packed buffer: its views stay null)
+  if (p.codes) out.codes = p.codes + t0 * 16 * code_bytes(p.fmt, p.Kp);
   if (p.scales) out.scales = (const unsigned char*)p.scales + t0 * scale_tile_bytes(p);
   out.G = nrows;
   out.TG = (int)cdiv(nrows, 16);
@@ -1101,6 +1127,11 @@ int32_t dspark_cache_append(const dspark_model* m, const dspark_append_in* in, v
   if (in->kv_dtype != DSPARK_DT_F32 && in->kv_dtype != DSPARK_DT_BF16) return fail(DSPARK_EINVAL, "bad kv_dtype");
   if (!workspace || (uintptr_t)workspace % 256) return fail(DSPARK_EINVAL, "workspace NULL or not 256-byte aligned");
   if ((long long)ws_bytes < A.total) return fail(DSPARK_EWORKSPACE, "workspace %zu bytes, need %lld", ws_bytes, A.total);
+  if (misaligned(in->captured, 4) || misaligned(in->positions, 4) || misaligned(in->slot_mapping, 8))
+    return fail(DSPARK_EINVAL, "captured / positions not 4-byte or slot_mapping not 8-byte aligned");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (misaligned(in->kv[l], 16)) return fail(DSPARK_EINVAL, "kv[%d] is not 16-byte aligned", l);
+  if (m->plan_only) return fail(DSPARK_EPLANONLY, "plan-only model: arguments valid, nothing enqueued");
   unsigned char* ws = (unsigned char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   bind_frag(A.f_fc, ws);
@@ -1303,6 +1334,7 @@ int32_t dspark_dequant(const dspark_model* m, int32_t id, float* out, void* stre
     }
   }
   if (!mt || !mt->present) return fail(DSPARK_EINVAL, "weight id %d has no packed matrix to decode", id);
+  if (m->plan_only) return fail(DSPARK_EPLANONLY, "plan-only model: arguments valid, nothing enqueued");
   HIPCHK(launch_dequant(mt->pm, out, (hipStream_t)stream));
   return DSPARK_OK;
 }

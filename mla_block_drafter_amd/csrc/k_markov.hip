@@ -72,9 +72,19 @@ __device__ __forceinline__ unsigned long long mk_wave_max(unsigned long long v) 
 
 // Argmax keys of position `pos` for every sequence (into tok[m]), polling the
 // slots of all workgroups until each is written.  All threads take part; wave
-// w reduces sequences w, w + MK_WAVES, ...
+// w reduces sequences w, w + MK_WAVES, ...  The wait is bounded (spin_limit
+// polls, default MK_SPIN_LIMIT): on expiry the error flag is raised and the
+// predecessors become -1, and the workgroup carries on, so every workgroup
+// still publishes every position and the grid drains.
 __device__ void mk_poll(const MarkovArgs& a, int pos, int nwg, unsigned long long* red, int* tok) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (a.spin_limit < 0) {  // host-forced expiry: no wait at all
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < 16) tok[threadIdx.x] = -1;
+    __syncthreads();
+    return;
+  }
+  const unsigned limit = a.spin_limit > 0 ? (unsigned)a.spin_limit : MK_SPIN_LIMIT;
   unsigned spins = 0;
   for (;;) {
     int missing = 0;
@@ -95,7 +105,7 @@ __device__ void mk_poll(const MarkovArgs& a, int pos, int nwg, unsigned long lon
       return;
     }
     __builtin_amdgcn_s_sleep(1);
-    if (++spins == MK_SPIN_LIMIT) {
+    if (++spins >= limit) {
       if (threadIdx.x == 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (threadIdx.x < 16) tok[threadIdx.x] = -1;
       __syncthreads();

@@ -99,6 +99,7 @@ __global__ __launch_bounds__(256) void k_markov_final(MarkovFinalArgs a) {
     }
   }
   d = block_sum256(d, red);
+  if (a.status && s == 0 && i == 0 && threadIdx.x == 0) *a.status = failed ? 1 : 0;
   if (threadIdx.x == 0) {
     a.tokens[m] = failed ? -1 : ti;
     const float x = rs * hd + d + a.conf_b[0];

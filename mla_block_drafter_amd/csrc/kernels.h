@@ -222,6 +222,7 @@ struct MarkovArgs {
   unsigned* err;              // error flag, zeroed
   const float* sample_u;      // optional [n_seq][block][vocab] uniforms: Gumbel-max draws
   float inv_temp;             // 1 / temperature (with sample_u)
+  int spin_limit;             // polls per position before expiry: 0 default, < 0 expire at once
 };
 int markov_rollout_wgs(int tiles);
 bool markov_rollout_supported(int KB, int M, int vocab);
@@ -259,6 +260,7 @@ struct MarkovFinalArgs {
   // instead of keys; nonzero *rollout_err (an expired poll) gives tokens of -1
   const unsigned long long* slots; int nwg;
   const unsigned* rollout_err;
+  int32_t* status;            // optional [1]: 1 if the rollout expired, else 0
 };
 hipError_t launch_markov_final(const MarkovFinalArgs& a, hipStream_t st);
 

@@ -14,14 +14,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 # ---- constants mirrored from include/dspark.h ----
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENODEVICE = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENODEVICE, EPLANONLY = 0, -1, -2, -3, -4, -5, -6
 DT_F32, DT_BF16, DT_Q8_0, DT_FP8_E4M3, DT_MXFP4 = 0, 1, 2, 3, 4
 W_FC, W_FC_NORM, W_FINAL_NORM, W_LM_HEAD = 0, 1, 2, 3
 W_MARKOV_W1, W_MARKOV_W2, W_CONF_W, W_CONF_B = 4, 5, 6, 7
 W_LAYER_BASE, W_LAYER_STRIDE = 16, 16
 L_KEYS = ["in_norm", "q_a", "q_a_norm", "kv_a", "kv_a_norm", "q_b", "kv_b", "o",
           "post_norm", "gate", "up", "down"]
-CFG_LAYERS_ONLY = 1
+CFG_LAYERS_ONLY, CFG_PLAN_ONLY = 1, 2
 
 FMT_CODE = {"f32": DT_F32, "bf16": DT_BF16, "q8_0": DT_Q8_0, "fp8_e4m3": DT_FP8_E4M3, "mxfp4": DT_MXFP4}
 TOP_IDS = {"fc": W_FC, "fc_norm": W_FC_NORM, "final_norm": W_FINAL_NORM, "lm_head": W_LM_HEAD,
@@ -64,7 +64,7 @@ class BlockIn(C.Structure):
                 ("total_ctx", C.c_int64), ("captured", C.c_void_p), ("kv", C.POINTER(C.c_void_p)),
                 ("kv_offsets", C.c_void_p), ("prev_token", C.c_void_p), ("forced_prev", C.c_void_p),
                 ("page_size", C.c_int32), ("max_pages", C.c_int32), ("block_table", C.c_void_p),
-                ("sample_u", C.c_void_p), ("temperature", C.c_float), ("pad2_", C.c_int32)]
+                ("sample_u", C.c_void_p), ("temperature", C.c_float), ("poll_limit", C.c_int32)]
 
 
 class VerifyIn(C.Structure):
@@ -87,7 +87,7 @@ APPEND_MAX = 128
 
 class BlockOut(C.Structure):
     _fields_ = [("tokens", C.c_void_p), ("conf", C.c_void_p), ("logits", C.c_void_p), ("hidden", C.c_void_p),
-                ("stage_events", C.POINTER(C.c_void_p))]
+                ("stage_events", C.POINTER(C.c_void_p)), ("status", C.c_void_p)]
 
 
 N_STAGES = 4
@@ -157,13 +157,13 @@ def check(rc: int) -> None:
         raise DsparkError(rc, last_error())
 
 
-def make_config(m, layers_only: bool = False) -> Config:
+def make_config(m, layers_only: bool = False, plan_only: bool = False) -> Config:
     """Fill the C config from any object with the ModelConfig attribute names."""
     c = Config()
     for f in ["hidden", "n_layers", "n_heads", "q_lora", "kv_lora", "qk_nope", "qk_rope", "v_head",
               "inter", "vocab", "markov_rank", "block", "n_captured"]:
         setattr(c, f, int(getattr(m, f)))
-    c.flags = CFG_LAYERS_ONLY if layers_only else 0
+    c.flags = (CFG_LAYERS_ONLY if layers_only else 0) | (CFG_PLAN_ONLY if plan_only else 0)
     c.rms_eps, c.rope_theta, c.yarn_factor = float(m.rms_eps), float(m.rope_theta), float(m.yarn_factor)
     c.yarn_orig_ctx = int(m.yarn_orig_ctx)
     c.yarn_beta_fast, c.yarn_beta_slow = float(m.yarn_beta_fast), float(m.yarn_beta_slow)
@@ -233,10 +233,12 @@ class Model:
     def draft_block(self, captured, kv: Sequence, kv_offsets, prev_token, total_ctx: int, tokens, conf,
                     workspace, logits=None, hidden=None, forced_prev=None, stream=None,
                     stage_events=None, page_size: int = 0, block_table=None, sample_u=None,
-                    temperature: float = 1.0) -> None:
+                    temperature: float = 1.0, status=None, poll_limit: int = 0) -> None:
         """stage_events: optional list of 2*N_STAGES torch.cuda.Event (enable_timing).
         page_size > 0: kv holds page pools and block_table (int32 [n_seq][max_pages])
-        maps each sequence's pages."""
+        maps each sequence's pages.  status: optional int32 device tensor [1]
+        (1 when the Markov rollout's bounded wait expired; tokens are then -1);
+        poll_limit: that wait's bound (0 default, < 0 expire at once)."""
         import torch
         n_seq = int(prev_token.shape[0])
         kv_arr = (C.c_void_p * len(kv))(*[t.data_ptr() if t is not None else None for t in kv])
@@ -257,7 +259,8 @@ class Model:
             bi.page_size = int(page_size)
             bi.max_pages = int(block_table.shape[1])
             bi.block_table = block_table.data_ptr()
-        bo = BlockOut(tokens.data_ptr(), conf.data_ptr(), _ptr(logits), _ptr(hidden), None)
+        bi.poll_limit = int(poll_limit)
+        bo = BlockOut(tokens.data_ptr(), conf.data_ptr(), _ptr(logits), _ptr(hidden), None, _ptr(status))
         if stage_events is not None:
             evs = (C.c_void_p * (2 * N_STAGES))(*[e.cuda_event for e in stage_events])
             bo.stage_events = evs

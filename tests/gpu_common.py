@@ -39,9 +39,18 @@ def device_inputs(wl, inp):
     return cap, kv, offs, prev
 
 
+# Byte patterns a workspace and the optional outputs are filled with before a
+# poisoned call: 0xFF is NaN in fp32, bf16 and fp16 (and -1 as int8); 0x3C is
+# a finite value in each (fp32 ~0.0115, bf16 ~0.0115, fp16 ~1.06).  A pass
+# that reads memory it has not written either produces NaN or depends on the
+# pattern; a pass that does not gives the same bits under every pattern.
+POISON_PATTERNS = (0xFF, 0x3C)
+
+
 class GpuWorkload:
     def __init__(self, wl, stored=None, inputs=None):
         self.wl = wl
+        self.poison = None  # byte pattern filled into the workspace and outputs before each call
         self.stored = stored if stored is not None else gen.make_weights(wl)
         self.inputs = inputs if inputs is not None else gen.make_inputs(wl)
         tens = D.upload_stored(self.stored)
@@ -68,6 +77,10 @@ class GpuWorkload:
         conf = torch.full((n, B), float("nan"), dtype=torch.float32, device=dev)
         logits = torch.empty((n, B, m.vocab), dtype=torch.float32, device=dev) if want_logits else None
         hidden = torch.empty((n * B, m.hidden), dtype=torch.float32, device=dev) if want_hidden else None
+        if self.poison is not None:
+            for t in (self.ws, logits, hidden):
+                if t is not None:
+                    t.view(torch.uint8).fill_(self.poison)
         fp = None if forced is None else torch.from_numpy(np.asarray(forced, np.int32)).to(dev)
         self.model.draft_block(self.cap, self.kv, self.offs, self.prev, self.wl.total_ctx, tokens, conf,
                                self.ws, logits=logits, hidden=hidden, forced_prev=fp,

@@ -72,6 +72,32 @@ def test_yarn_frequencies_limits():
     assert O.yarn_logit_scale(C.TINY) == 1.0
 
 
+@pytest.mark.parametrize("k", [3, 7, 11])
+def test_yarn_ramp_interior(k):
+    """Inside the band alpha < r_k < beta the NTK-by-parts ramp is linear in
+    the rotation count r_k (YaRN paper, Peng et al. 2023): the pair whose
+    window holds exactly (alpha + beta) / 2 rotations gets the mean of the
+    interpolated and the original frequency, and the pair at alpha + (beta -
+    alpha) / 4 rotations three quarters interpolated, one quarter original.
+    The original window is chosen so that pair k sits at that point; a log
+    ramp, swapped alpha / beta roles or swapped f / (f / s) roles each move
+    one of the two points."""
+    base = C.FULL
+    d, s = base.qk_rope, base.yarn_factor
+    alpha, beta = base.yarn_beta_slow, base.yarn_beta_fast
+    theta_k = base.rope_theta ** (-2.0 * k / d)
+    for frac, want_interp in ((0.5, 0.5), (0.25, 0.75)):
+        r_k = alpha + frac * (beta - alpha)
+        L = 2 * math.pi * r_k / theta_k                    # window with r_k rotations at pair k
+        m = C.ModelConfig(**{**base.__dict__, "yarn_orig_ctx": L})
+        f = O.rope_frequencies(m)
+        want = want_interp * theta_k / s + (1 - want_interp) * theta_k
+        assert f[k] == pytest.approx(want, rel=1e-12), (k, frac)
+        # pairs below / above in index sit at more / fewer rotations: the
+        # ramp is monotone and the endpoints are reached outside the band
+        assert f[k - 1] / (base.rope_theta ** (-2.0 * (k - 1) / d)) > f[k] / theta_k
+
+
 # ----------------------------------------------------------- acceptance ----
 def test_accept_len_brute_force():
     for alpha, blk in [(3, 1), (3, 2), (3, 3), (3, 4), (3, 5), (2, 7)]:
