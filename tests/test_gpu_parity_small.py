@@ -157,3 +157,42 @@ def test_determinism_bitwise():
     b = g.draft()
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_determinism_interleaved_workloads():
+    """Passes of three different workloads interleaved (different geometries
+    and kernels run in between, leaving other data in LDS, registers, the
+    caches and the workspaces' previous owners): every repeat of a workload
+    reproduces its first pass bit for bit, greedy and sampled, packed and
+    paged."""
+    from tests.gpu_common import GpuWorkload
+    wa = C.Workload("det_a", SMALL, C.ALL_BF16, seed=1103, kv_lens=(0, 37, 300), fixture_gains=True)
+    wb = C.Workload("det_b", C.small_model(hidden=256, vocab=777), C.Q8, seed=31, kv_lens=(129,))
+    wc = C.CFG1.replace(fixture_gains=True)
+    ga, gb, gc = GpuWorkload(wa), GpuWorkload(wb), GpuWorkload(wc)
+    m = wa.model
+    u = torch.from_numpy(np.random.default_rng(8).uniform(1e-6, 1 - 1e-6, (wa.n_seq, m.block, m.vocab))
+                         .astype(np.float32)).cuda()
+
+    def sampled(g):
+        tokens = torch.empty((wa.n_seq, m.block), dtype=torch.int32, device="cuda")
+        conf = torch.empty((wa.n_seq, m.block), dtype=torch.float32, device="cuda")
+        g.model.draft_block(g.cap, g.kv, g.offs, g.prev, wa.total_ctx, tokens, conf, g.ws, sample_u=u,
+                            temperature=0.8, page_size=g.page_size, block_table=g.table)
+        torch.cuda.synchronize()
+        return dict(tokens=tokens.cpu().numpy(), conf=conf.cpu().numpy())
+
+    first = {}
+    for rep in range(4):
+        runs = [("a", ga.draft), ("b", gb.draft), ("as", lambda: sampled(ga)), ("c", gc.draft)]
+        if rep == 2:
+            ga.use_pages(64, seed=3)   # same rows, paged: same bits
+        for name, fn in (runs if rep % 2 == 0 else runs[::-1]):
+            out = fn()
+            if name not in first:
+                first[name] = out
+                continue
+            for k in out:
+                np.testing.assert_array_equal(np.ascontiguousarray(out[k]).view(np.uint8),
+                                              np.ascontiguousarray(first[name][k]).view(np.uint8),
+                                              err_msg=f"{name} repeat {rep}: {k}")
