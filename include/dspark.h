@@ -250,6 +250,23 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in,
                            dspark_block_out* out, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/* The same draft pass for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument and no allocation of any kind; the
+ * pass's scratch lives in a static device array of the library
+ * (DSPARK_STATIC_SCRATCH_BYTES, one copy per GPU, held until the process
+ * ends).  Same arguments, semantics and results as dspark_draft_block.
+ * Calls whose workspace would exceed the array (see dspark_workspace_bytes;
+ * e.g. one sequence with more than ~28k cached tokens at the full geometry)
+ * fail with DSPARK_EWORKSPACE and enqueue nothing.  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (concurrent streams, or
+ * threads) race and must be ordered by the caller.  The array keeps the last
+ * call's contents; the pass clears what it needs zeroed itself, with a kernel
+ * (no memset node under capture). */
+#define DSPARK_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int32_t dspark_draft_block_static(const dspark_model* m, const dspark_block_in* in,
+                                  dspark_block_out* out, void* stream);
+
 /* One decoder layer on a given residual stream (the single-layer unit):
  * x_out = x_in + o_proj(MLA(RMSNorm(x_in))) and, when with_mlp != 0, then
  * x_out += SwiGLU(RMSNorm(x_out)).  x_in, x_out: device float

@@ -976,6 +976,25 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   return DSPARK_OK;
 }
 
+int32_t dspark_draft_block_static(const dspark_model* m, const dspark_block_in* in, dspark_block_out* out,
+                                  void* stream) {
+  g_err.clear();
+  if (!m || !in || !out) return fail(DSPARK_EINVAL, "model / in / out is NULL");
+  if (in->n_seq < 1) return fail(DSPARK_EINVAL, "n_seq < 1");
+  if (in->total_ctx < 0 || in->total_ctx > (1ll << 30)) return fail(DSPARK_EINVAL, "total_ctx out of range");
+  const size_t need = dspark_workspace_bytes(m, in->n_seq, in->total_ctx);
+  if (need == 0) return DSPARK_EINVAL;  // message set by the query
+  if (need > DSPARK_STATIC_SCRATCH_BYTES)
+    return fail(DSPARK_EWORKSPACE,
+                "this call needs %zu bytes of workspace; the static scratch holds %zu (use dspark_draft_block "
+                "with a caller workspace)", need, (size_t)DSPARK_STATIC_SCRATCH_BYTES);
+  if (m->plan_only) return dspark_draft_block(m, in, out, (void*)(uintptr_t)256, need, stream);
+  void* ws = nullptr;
+  size_t bytes = 0;
+  HIPCHK(static_scratch(&ws, &bytes));
+  return dspark_draft_block(m, in, out, ws, bytes, stream);
+}
+
 int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_mlp, int32_t n_seq, const float* x_in,
                              float* x_out, const void* kv, int32_t kv_dtype, const int32_t* kv_offsets,
                              int64_t total_ctx, void* workspace, size_t ws_bytes, void* stream) {

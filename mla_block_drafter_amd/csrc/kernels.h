@@ -267,6 +267,11 @@ hipError_t launch_markov_final(const MarkovFinalArgs& a, hipStream_t st);
 hipError_t launch_accept_len(const int32_t* d, const int32_t* v, int n_seq, int block, int32_t* out,
                              hipStream_t st);
 
+// -------------------------------------------------------- static scratch --
+// Address and size of this device's copy of the library's static scratch
+// (dspark_static.hip); the address is looked up once per device.
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 // ---------------------------------------------------------------- repack --
 enum { XF_NORMAL = 0, XF_UK = 1, XF_UV = 2 };
 struct RepackArgs {

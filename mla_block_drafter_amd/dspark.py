@@ -31,7 +31,9 @@ EXPORTS = ["dspark_packed_bytes", "dspark_model_create", "dspark_model_destroy",
            "dspark_workspace_bytes", "dspark_draft_block", "dspark_layer_forward",
            "dspark_append_workspace_bytes", "dspark_cache_append",
            "dspark_verify_workspace_bytes", "dspark_verify",
-           "dspark_accept_len", "dspark_accept_len_host", "dspark_dequant", "dspark_last_error"]
+           "dspark_accept_len", "dspark_accept_len_host", "dspark_dequant", "dspark_last_error",
+           "dspark_draft_block_static"]
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def layer_id(layer: int, key: str) -> int:
@@ -124,6 +126,8 @@ def lib():
     L.dspark_draft_block.restype = C.c_int32
     L.dspark_draft_block.argtypes = [C.c_void_p, C.POINTER(BlockIn), C.POINTER(BlockOut), C.c_void_p, C.c_size_t,
                                      C.c_void_p]
+    L.dspark_draft_block_static.restype = C.c_int32
+    L.dspark_draft_block_static.argtypes = [C.c_void_p, C.POINTER(BlockIn), C.POINTER(BlockOut), C.c_void_p]
     L.dspark_layer_forward.restype = C.c_int32
     L.dspark_layer_forward.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_size_t,
@@ -238,7 +242,9 @@ class Model:
         page_size > 0: kv holds page pools and block_table (int32 [n_seq][max_pages])
         maps each sequence's pages.  status: optional int32 device tensor [1]
         (1 when the Markov rollout's bounded wait expired; tokens are then -1);
-        poll_limit: that wait's bound (0 default, < 0 expire at once)."""
+        poll_limit: that wait's bound (0 default, < 0 expire at once).
+        workspace None: dspark_draft_block_static (the library's static
+        scratch, for callers that cannot allocate)."""
         import torch
         n_seq = int(prev_token.shape[0])
         kv_arr = (C.c_void_p * len(kv))(*[t.data_ptr() if t is not None else None for t in kv])
@@ -264,8 +270,11 @@ class Model:
         if stage_events is not None:
             evs = (C.c_void_p * (2 * N_STAGES))(*[e.cuda_event for e in stage_events])
             bo.stage_events = evs
-        check(lib().dspark_draft_block(self.handle, C.byref(bi), C.byref(bo), workspace.data_ptr(),
-                                       workspace.numel(), _stream_ptr(stream)))
+        if workspace is None:   # the library's static scratch (no allocation anywhere)
+            check(lib().dspark_draft_block_static(self.handle, C.byref(bi), C.byref(bo), _stream_ptr(stream)))
+        else:
+            check(lib().dspark_draft_block(self.handle, C.byref(bi), C.byref(bo), workspace.data_ptr(),
+                                           workspace.numel(), _stream_ptr(stream)))
 
     def layer_forward(self, layer: int, with_mlp: bool, x_in, x_out, kv, kv_offsets, total_ctx: int,
                       workspace, stream=None) -> None:

@@ -291,6 +291,21 @@ void draft_checks(const dspark_model* m, const dspark_model* layers_only) {
     expect(dspark_draft_block(m, &d.in, nullptr, d.ws, d.ws_bytes, nullptr), DSPARK_EINVAL, "out NULL");
     expect(run(layers_only, d), DSPARK_EINVAL, "draft on a layers-only model");
   }
+  {
+    // the static-scratch form: same validation; sizes past the static array are refused
+    DraftCall d = valid_draft(m);
+    expect(dspark_draft_block_static(m, &d.in, &d.out, nullptr), DSPARK_EPLANONLY, "static: valid");
+    d.in.n_seq = 0;
+    expect(dspark_draft_block_static(m, &d.in, &d.out, nullptr), DSPARK_EINVAL, "static: n_seq 0");
+    d = valid_draft(m);
+    d.in.total_ctx = 1 << 26;
+    expect(dspark_draft_block_static(m, &d.in, &d.out, nullptr), DSPARK_EWORKSPACE, "static: too large");
+    expect_true(std::strstr(dspark_last_error(), "static scratch") != nullptr, "static: message");
+    d = valid_draft(m);
+    d.out.conf = nullptr;
+    expect(dspark_draft_block_static(m, &d.in, &d.out, nullptr), DSPARK_EINVAL, "static: conf NULL");
+    expect(dspark_draft_block_static(nullptr, &d.in, &d.out, nullptr), DSPARK_EINVAL, "static: model NULL");
+  }
   expect_true(dspark_workspace_bytes(nullptr, 1, 10) == 0, "workspace query, model NULL");
   expect_true(dspark_workspace_bytes(m, 0, 10) == 0, "workspace query, n_seq 0");
   expect_true(dspark_workspace_bytes(m, 1, -1) == 0, "workspace query, total_ctx < 0");

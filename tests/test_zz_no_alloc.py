@@ -1,0 +1,80 @@
+"""dspark_draft_block_static, the entry point that allocates nothing (for
+callers that cannot allocate): its outputs equal dspark_draft_block's with a
+caller workspace, bit for bit, on two calls in a row, the second with a
+smaller input (the static scratch keeps the first call's contents); a call
+larger than the static scratch is refused before anything is enqueued."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from synth import configs as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mla_block_drafter_amd import dspark as D
+    D.lib()
+
+
+def _pass(g, total_ctx, offs, static):
+    m = g.wl.model
+    n, B = g.wl.n_seq, m.block
+    tokens = torch.full((n, B), -7, dtype=torch.int32, device="cuda")
+    conf = torch.full((n, B), float("nan"), dtype=torch.float32, device="cuda")
+    logits = torch.full((n, B, m.vocab), float("nan"), dtype=torch.float32, device="cuda")
+    hidden = torch.full((n * B, m.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    ws = None if static else g.model.workspace(n, total_ctx)
+    g.model.draft_block(g.cap, g.kv, offs, g.prev, total_ctx, tokens, conf, ws, logits=logits, hidden=hidden)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in (tokens, conf, logits, hidden)]
+
+
+def _same(a, b):
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(np.ascontiguousarray(x).view(np.uint8), np.ascontiguousarray(y).view(np.uint8))
+
+
+def test_static_scratch_matches_caller_workspace_full_q8_0():
+    from mla_block_drafter_amd import dspark as D
+    from tests.gpu_common import GpuWorkload
+    g = GpuWorkload(C.CFG3)
+    long_ctx, short_ctx = 8192, 3001
+    offs_long = g.offs
+    offs_short = torch.tensor([0, short_ctx], dtype=torch.int32, device="cuda")
+    ref_long = _pass(g, long_ctx, offs_long, static=False)
+    ref_short = _pass(g, short_ctx, offs_short, static=False)
+    got_long = _pass(g, long_ctx, offs_long, static=True)
+    got_short = _pass(g, short_ctx, offs_short, static=True)   # second call, smaller input
+    _same(got_long, ref_long)
+    _same(got_short, ref_short)
+    assert not np.array_equal(ref_long[2], ref_short[2])       # the two inputs really differ
+    # a call beyond the static scratch is refused, nothing enqueued
+    m = g.wl.model
+    tokens = torch.full((1, m.block), -7, dtype=torch.int32, device="cuda")
+    conf = torch.zeros((1, m.block), dtype=torch.float32, device="cuda")
+    with pytest.raises(D.DsparkError) as e:
+        g.model.draft_block(g.cap, g.kv, torch.tensor([0, 1 << 17], dtype=torch.int32, device="cuda"), g.prev,
+                            1 << 17, tokens, conf, None)
+    assert e.value.code == D.EWORKSPACE and "static scratch" in str(e.value)
+    torch.cuda.synchronize()
+    assert (tokens.cpu().numpy() == -7).all()
+
+
+def test_static_scratch_small_ragged_then_one_sequence():
+    from tests.gpu_common import GpuWorkload
+    wl = C.Workload("static_small", C.small_model(), C.Q8, seed=1501, kv_lens=(0, 37, 300), fixture_gains=True)
+    g = GpuWorkload(wl)
+    ref = _pass(g, wl.total_ctx, g.offs, static=False)
+    got = _pass(g, wl.total_ctx, g.offs, static=True)
+    _same(got, ref)
+    # one sequence of the same model after the three-sequence call
+    one = wl.replace(kv_lens=(120,))
+    g1 = GpuWorkload(one, stored=g.stored)
+    ref1 = _pass(g1, one.total_ctx, g1.offs, static=False)
+    got1 = _pass(g1, one.total_ctx, g1.offs, static=True)
+    _same(got1, ref1)
