@@ -218,11 +218,16 @@ typedef struct dspark_block_out {
                        hipEvent_t: events[2s] / events[2s+1] are recorded on the
                        stream right before / after stage s (profiling aid);
                        NULL = none                                               */
-  int32_t* status;  /* optional device int32 [1]: 0 when the pass completed, 1
-                       when the Markov rollout's wait expired (tokens are then
-                       -1); NULL = skip.  The library's bound is only reached
-                       when the rollout's workgroups cannot all be resident,
-                       e.g. kernels of other streams hold CUs for seconds     */
+  int32_t* status;  /* optional device int32 [1]: 0 when the pass completed
+                       by the full Markov rollout, 2 when it completed by the
+                       candidate rollout (greedy passes without logits or
+                       hidden outputs: only the rows that can still be the
+                       argmax, by a Cauchy-Schwarz bound on the Markov term,
+                       are evaluated; same tokens up to rounding ties), 1 when
+                       the full rollout's wait expired (tokens are then -1);
+                       NULL = skip.  The library's bound is only reached when
+                       the rollout's workgroups cannot all be resident, e.g.
+                       kernels of other streams hold CUs for seconds          */
 } dspark_block_out;
 
 /* stages of one draft pass, for dspark_block_out.stage_events */

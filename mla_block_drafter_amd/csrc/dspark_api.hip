@@ -85,6 +85,7 @@ struct dspark_model {
   bool plan_only = false;  // DSPARK_CFG_PLAN_ONLY: validated and planned, no packed weights
   Mat fc, lm, w2;
   long long fc_norm = -1, final_norm = -1, conf_w = -1, conf_b = -1, w1 = -1, freqs = -1;
+  long long w2n = -1, w1max = -1;  // row-norm bounds of W2 and the largest of W1 (candidate pruning)
   int w1_fmt = DT_BF16, w1_ld = 0;
   std::vector<Layer> L;
   float tau = 1.f;
@@ -243,6 +244,8 @@ int32_t build_plan(const dspark_config* c, const dspark_weight* w, int n, dspark
     m.w1_fmt = a->dtype;
     m.w1_ld = m.w2.pm.Kp;
     m.w1 = take((long long)c->vocab * m.w1_ld * (a->dtype == DSPARK_DT_F32 ? 4 : 2));
+    m.w2n = take((long long)c->vocab * 4);
+    m.w1max = take(4);
     if ((rc = get_vec(w, n, DSPARK_W_CONF_W, H + c->markov_rank, &v))) return rc;
     m.conf_w = take((H + c->markov_rank) * 4);
     if ((rc = get_vec(w, n, DSPARK_W_CONF_B, 1, &v))) return rc;
@@ -347,6 +350,8 @@ struct Plan {
   long long total_ctx = 0;
   bool kv_f32 = false;
   long long x = 0, part = 0, q = 0, bkeys = 0, opart = 0, mlpart = 0, z = 0, keys = 0, mslots = 0, merr = 0, total = 0;
+  long long mfall = 0, mlmax = 0, mlcnt = 0, mlist = 0;  // candidate pruning of the Markov rollout
+  int nch_v = 0;
   int mwgs = 0;
   long long ssq_a = 0, ssq_b = 0, ssq_cq = 0, dot = 0, rope = 0;
   long long zero_begin = 0, zero_end = 0;
@@ -379,17 +384,23 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
     if (split) part = std::max(part, (long long)gpn.S * M * mt.pm.ngroups * mt.pm.G * 4);
   };
   gp(P.p_qkva, L0.qkva, true, true);
-  gp(P.p_qb, L0.qb, true, true);
   gp(P.p_uk, L0.uk, false, false);  // epilogue writes the query buffer
   gp(P.p_uv, L0.uv, false, false);  // epilogue writes the o_proj fragments
   const bool uv_i8 = P.p_uv.MT == 1 && P.p_uv.TPW % 2 == 0 && L0.uv.pm.TG % 2 == 0 && L0.uv.pm.G % 32 == 0;
-  gp(P.p_o, L0.o, true, uv_i8);
+  // column-owning GEMMs (split inside the workgroup, fused epilogue) where
+  // the shape and format are covered, else split-K plus a reduction kernel
+  auto own = [&](GemvPlan& gpn, const Mat& mt, bool swiglu, bool i8) {
+    gpn = plan_own(mt.pm, M, swiglu, i8);
+    return gpn.nw > 0;
+  };
+  gp(P.p_qb, L0.qb, true, true);  // (a column-owning q_b measured slower than split-K + the fused absorb)
+  if (!own(P.p_o, L0.o, false, uv_i8)) gp(P.p_o, L0.o, true, uv_i8);
   if (m.has_mlp) {
-    gp(P.p_gu, L0.gu, true, true);
-    gp(P.p_down, L0.down, true, true);
+    if (!own(P.p_gu, L0.gu, true, true)) gp(P.p_gu, L0.gu, true, true);
+    if (!own(P.p_down, L0.down, false, true)) gp(P.p_down, L0.down, true, true);
   }
   if (!m.layers_only) {
-    gp(P.p_fc, m.fc, true, true);
+    if (!own(P.p_fc, m.fc, false, true)) gp(P.p_fc, m.fc, true, true);
     P.p_lm = plan_gemv(m.lm.pm, M, false, false, true);
     P.p_w2 = plan_gemv(m.w2.pm, n_seq, false, true);
   }
@@ -416,6 +427,9 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
     P.mwgs = markov_rollout_wgs(m.w2.pm.ngroups * m.w2.pm.TG);
     P.mslots = take((long long)c.block * n_seq * P.mwgs * 8);
     P.merr = take(16);
+    P.mfall = take(16);
+    P.mlmax = take((long long)M * 4);
+    P.mlcnt = take((long long)M * 4);
   }
   P.rows = c.block * c.n_heads;
   P.rows_pad = (int)rup(P.rows, 64);
@@ -436,7 +450,11 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   P.ssq_cq = take(ssq);
   P.dot = take(ssq);
   P.rope = take((long long)M * (c.qk_rope / 2) * 8);
-  if (!m.layers_only) P.z = take((long long)M * c.vocab * 4);
+  if (!m.layers_only) {
+    P.z = take((long long)M * c.vocab * 4);
+    P.nch_v = markov_prune_chunks(c.vocab);
+    P.mlist = take((long long)M * MK_CAPR * 16);
+  }
   P.total = off;
 }
 
@@ -478,10 +496,17 @@ struct Ctx {
   float* part() const { return (float*)(ws + P.part); }
   float* x() const { return (float*)(ws + P.x); }
   float* ssq(long long off) const { return (float*)(ws + off); }
+  // chunk counts of the sums of squares now in ssq_a / ssq_b: 256-column
+  // chunks from the column-parallel kernels, OWN_COLS-column chunks from the
+  // column-owning GEMM epilogues
+  int nch_a = 0, nch_b = 0;
+  int nch_of(long long off, int n) const {
+    return off == P.ssq_a && nch_a ? nch_a : off == P.ssq_b && nch_b ? nch_b : (n + 255) / 256;
+  }
   RowScale rs(long long off, int n) const {
     RowScale r{};
     r.ssq = (const float*)(ws + off);
-    r.nch = (n + 255) / 256;
+    r.nch = nch_of(off, n);
     r.invn = 1.f / (float)n;
     r.eps = m->c.rms_eps;
     return r;
@@ -614,7 +639,47 @@ int32_t attn_half(Ctx& C, int l, long long x_ssq, const void* kv, const int32_t*
     }
     if (!fused) HIPCHK(launch_gemv(g, P.p_uv, GEMV_FRAG, C.st));
   }
-  HIPCHK(run_gemv(L.o, P.p_o, P.f_o, M, C.part(), C.st));
+  return DSPARK_OK;
+}
+
+// The residual update x_out = x_in + W a of o_proj or down, the chunk sums
+// of x_out^2 into `ssq_out` and, with g1, the fragments of g1 * x_out for
+// the next GEMM (`fd`; with dotw also the confidence dot chunks): one
+// column-owning launch, or split-K plus the residual kernel.
+int32_t resid_gemm(Ctx& C, const Mat& mt, const GemvPlan& p, const Frag& f, const float* x_in, float* x_out,
+                   const float* g1, const FragDesc* fd, long long ssq_out, const float* dotw) {
+  Plan& P = C.P;
+  const int H = C.m->c.hidden;
+  if (p.nw) {
+    GemvArgs a = gemv_base(mt, p, f, P.M);
+    a.epi = OWN_RESID;
+    a.x_in = x_in;
+    a.x_out = x_out;
+    a.g1 = g1;
+    if (fd) a.fd = *fd;
+    a.ssq_out = ssq_out >= 0 ? C.ssq(ssq_out) : nullptr;
+    a.dotw = dotw;
+    a.dot_out = dotw ? C.ssq(P.dot) : nullptr;
+    HIPCHK(launch_gemv(a, p, GEMV_OWN, C.st));
+  } else {
+    HIPCHK(run_gemv(mt, p, f, P.M, C.part(), C.st));
+    ResidPost a{};
+    a.p = C.pin(p, mt);
+    a.mode = RP_ADD;
+    a.x_in = x_in;
+    a.x_out = x_out;
+    a.M = P.M;
+    a.H = H;
+    a.g1 = g1;
+    if (fd) a.fd = *fd;
+    a.ssq_out = ssq_out >= 0 ? C.ssq(ssq_out) : nullptr;
+    a.dotw = dotw;
+    a.dot_out = dotw ? C.ssq(P.dot) : nullptr;
+    HIPCHK(launch_post_resid(a, C.st));
+  }
+  const int nch = p.nw ? H / OWN_COLS : (H + 255) / 256;
+  if (ssq_out == P.ssq_a) C.nch_a = nch;
+  if (ssq_out == P.ssq_b) C.nch_b = nch;
   return DSPARK_OK;
 }
 
@@ -625,6 +690,15 @@ int32_t mlp_half(Ctx& C, int l, long long x_ssq) {
   const Layer& L = m.L[l];
   Plan& P = C.P;
   const int M = P.M;
+  if (P.p_gu.nw) {  // gate/up with the SwiGLU fused: workgroup gi owns gate and up columns 32 gi .. + 31
+    GemvArgs a = gemv_base(L.gu, P.p_gu, P.f_gu, M);
+    a.epi = OWN_SWIGLU;
+    a.rs = C.rs(x_ssq, m.c.hidden);
+    a.tile_jump = L.gu.pm.TG / 2 - 2;  // up tiles follow the gate tiles
+    a.fd = P.f_down.fd;
+    HIPCHK(launch_gemv(a, P.p_gu, GEMV_OWN, C.st));
+    return DSPARK_OK;
+  }
   HIPCHK(run_gemv(L.gu, P.p_gu, P.f_gu, M, C.part(), C.st));
   SwigluPost a{};
   a.p = C.pin(P.p_gu, L.gu);
@@ -633,7 +707,6 @@ int32_t mlp_half(Ctx& C, int l, long long x_ssq) {
   a.inter = m.c.inter;
   a.fd = P.f_down.fd;
   HIPCHK(launch_post_swiglu(a, C.st));
-  HIPCHK(run_gemv(L.down, P.p_down, P.f_down, M, C.part(), C.st));
   return DSPARK_OK;
 }
 
@@ -743,6 +816,12 @@ int32_t dspark_model_create(const dspark_config* cfg, const dspark_weight* w, in
       const size_t esz = m->w1_fmt == DT_F32 ? 4 : 2;
       HIPCHK(hipMemcpy2DAsync(m->base + m->w1, (size_t)m->w1_ld * esz, w1->data, (size_t)c.markov_rank * esz,
                               (size_t)c.markov_rank * esz, (size_t)c.vocab, hipMemcpyDeviceToDevice, st));
+      // row-norm bounds for the exact candidate pruning of the Markov rollout
+      const dspark_weight* w2s = find_w(w, n, DSPARK_W_MARKOV_W2);
+      HIPCHK(launch_row_norms(w2s->data, w2s->dtype == DSPARK_DT_F32, w2s->cols, c.markov_rank, c.vocab,
+                              (float*)(m->base + m->w2n), nullptr, st));
+      HIPCHK(launch_row_norms(w1->data, w1->dtype == DSPARK_DT_F32, w1->cols, c.markov_rank, c.vocab, nullptr,
+                              (unsigned*)(m->base + m->w1max), st));
       if ((r2 = copy_vec(*m, m->fc_norm, find_w(w, n, DSPARK_W_FC_NORM), st))) return r2;
       if ((r2 = copy_vec(*m, m->final_norm, find_w(w, n, DSPARK_W_FINAL_NORM), st))) return r2;
       if ((r2 = copy_vec(*m, m->conf_w, find_w(w, n, DSPARK_W_CONF_W), st))) return r2;
@@ -852,13 +931,21 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     set_rope(C, a, in->kv_offsets);
     HIPCHK(launch_init(a, C.st));
   }
-  HIPCHK(run_gemv(m->fc, P.p_fc, P.f_fc, M, C.part(), C.st));
-  {
+  if (P.p_fc.nw) {                        // y = fc output, chunk sums of y^2 (one launch)
+    GemvArgs a = gemv_base(m->fc, P.p_fc, P.f_fc, M);
+    a.epi = OWN_STORE;
+    a.x_out = C.x();
+    a.ssq_out = C.ssq(P.ssq_a);
+    HIPCHK(launch_gemv(a, P.p_fc, GEMV_OWN, C.st));
+    C.nch_a = c.hidden / OWN_COLS;
+  } else {
+    HIPCHK(run_gemv(m->fc, P.p_fc, P.f_fc, M, C.part(), C.st));
     ResidPost a = resid_base(C);          // y = fc output, chunk sums of y^2
     a.mode = RP_SUM;
     a.p = C.pin(P.p_fc, m->fc);
     a.ssq_out = C.ssq(P.ssq_a);
     HIPCHK(launch_post_resid(a, C.st));
+    C.nch_a = (c.hidden + 255) / 256;
   }
   {
     ResidPost a = resid_base(C);          // x = RMSNorm(y; g_fc), fragments of in_norm * x
@@ -869,35 +956,24 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.fd = P.f_qkva.fd;
     a.ssq_out = C.ssq(P.ssq_b);
     HIPCHK(launch_post_resid(a, C.st));
+    C.nch_b = (c.hidden + 255) / 256;
   }
   HIPCHK(mark(2 * DSPARK_STAGE_FC + 1));
   HIPCHK(mark(2 * DSPARK_STAGE_LAYERS));
   for (int l = 0; l < c.n_layers; ++l) {
+    const Layer& L = m->L[l];
     if ((rc = attn_half(C, l, P.ssq_b, in->kv[l], in->kv_offsets))) return rc;
-    {
-      ResidPost a = resid_base(C);        // x += o_proj; fragments of post_norm * x
-      a.p = C.pin(P.p_o, m->L[l].o);
-      a.g1 = (const float*)(m->base + m->L[l].post_norm);
-      a.fd = P.f_gu.fd;
-      a.ssq_out = C.ssq(P.ssq_a);
-      HIPCHK(launch_post_resid(a, C.st));
-    }
+    // x += o_proj; fragments of post_norm * x
+    if ((rc = resid_gemm(C, L.o, P.p_o, P.f_o, C.x(), C.x(), (const float*)(m->base + L.post_norm), &P.f_gu.fd,
+                         P.ssq_a, nullptr)))
+      return rc;
     if ((rc = mlp_half(C, l, P.ssq_a))) return rc;
-    {
-      ResidPost a = resid_base(C);        // x += down; fragments of the next norm * x
-      a.p = C.pin(P.p_down, m->L[l].down);
-      a.ssq_out = C.ssq(P.ssq_b);
-      if (l + 1 < c.n_layers) {
-        a.g1 = (const float*)(m->base + m->L[l + 1].in_norm);
-        a.fd = P.f_qkva.fd;
-      } else {
-        a.g1 = (const float*)(m->base + m->final_norm);
-        a.fd = P.f_lm.fd;
-        a.dotw = (const float*)(m->base + m->conf_w);
-        a.dot_out = C.ssq(P.dot);
-      }
-      HIPCHK(launch_post_resid(a, C.st));
-    }
+    // x += down; fragments of the next norm * x (the last layer: final norm, confidence dot)
+    const bool last = l + 1 == c.n_layers;
+    const float* g1 = (const float*)(m->base + (last ? m->final_norm : m->L[l + 1].in_norm));
+    if ((rc = resid_gemm(C, L.down, P.p_down, P.f_down, C.x(), C.x(), g1, last ? &P.f_lm.fd : &P.f_qkva.fd, P.ssq_b,
+                         last ? (const float*)(m->base + m->conf_w) : nullptr)))
+      return rc;
   }
   HIPCHK(mark(2 * DSPARK_STAGE_LAYERS + 1));
   float* z = (float*)(C.ws + P.z);
@@ -906,6 +982,42 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   HIPCHK(mark(2 * DSPARK_STAGE_LM_HEAD + 1));
   HIPCHK(mark(2 * DSPARK_STAGE_MARKOV));
   const bool rollout = m->w2.pm.fmt == DT_BF16 && markov_rollout_supported(m->w2.pm.KB, in->n_seq, c.vocab);
+  // greedy passes that need neither the full logits nor the hidden state:
+  // the candidate rollout first; the full rollout only if it falls back
+  const bool prune = rollout && !in->sample_u && !out->logits && !out->hidden && in->poll_limit == 0 &&
+                     markov_prune_supported(c.markov_rank, c.block, c.vocab);
+  const int* fallback = prune ? (const int*)(C.ws + P.mfall) : nullptr;
+  if (prune) {
+    MarkovPruneArgs a{};
+    a.z = z;
+    a.n2 = (const float*)(m->base + m->w2n);
+    a.w1max = (const unsigned*)(m->base + m->w1max);
+    a.vocab = c.vocab;
+    a.n_seq = in->n_seq;
+    a.block = c.block;
+    a.R = c.markov_rank;
+    a.KB = m->w2.pm.KB;
+    a.nch = P.nch_v;
+    a.w2 = m->w2.pm.codes;
+    a.w1 = m->base + m->w1;
+    a.w1_f32 = m->w1_fmt == DT_F32;
+    a.w1_ld = m->w1_ld;
+    a.prev_token = in->prev_token;
+    a.forced = in->forced_prev;
+    a.lmax = (unsigned*)(C.ws + P.mlmax);
+    a.lcnt = (int*)(C.ws + P.mlcnt);
+    a.list = (u32x4*)(C.ws + P.mlist);
+    a.fallback = (int*)(C.ws + P.mfall);
+    a.rs_final = C.rs(P.ssq_b, c.hidden);
+    a.dot = C.ssq(P.dot);
+    a.nch_dot = C.nch_of(P.ssq_b, c.hidden);
+    a.conf_wm = (const float*)(m->base + m->conf_w) + c.hidden;
+    a.conf_b = (const float*)(m->base + m->conf_b);
+    a.tokens = out->tokens;
+    a.conf = out->conf;
+    a.status = out->status;
+    HIPCHK(launch_markov_prune(a, C.st));
+  }
   if (rollout) {
     MarkovArgs a{};
     a.w2 = m->w2.pm.codes;
@@ -925,6 +1037,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.sample_u = in->sample_u;
     a.inv_temp = in->sample_u ? 1.f / in->temperature : 1.f;
     a.spin_limit = in->poll_limit;
+    a.fallback = fallback;
     HIPCHK(launch_markov_rollout(a, m->w2.pm.KB, C.st));
   }
   for (int i = 0; !rollout && i < c.block; ++i) {
@@ -955,7 +1068,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.conf_wm = (const float*)(m->base + m->conf_w) + c.hidden;
     a.conf_b = (const float*)(m->base + m->conf_b);
     a.dot = C.ssq(P.dot);
-    a.nch = (c.hidden + 255) / 256;
+    a.nch = C.nch_of(P.ssq_b, c.hidden);  // the dot chunks come with the last sums of squares
     a.rs_final = C.rs(P.ssq_b, c.hidden);
     a.x = C.x();
     a.g_final = (const float*)(m->base + m->final_norm);
@@ -970,6 +1083,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.nwg = rollout ? markov_rollout_wgs(m->w2.pm.ngroups * m->w2.pm.TG) : 0;
     a.rollout_err = rollout ? (const unsigned*)(C.ws + P.merr) : nullptr;
     a.status = out->status;
+    a.fallback = fallback;
     HIPCHK(launch_markov_final(a, C.st));
   }
   HIPCHK(mark(2 * DSPARK_STAGE_MARKOV + 1));
@@ -1042,23 +1156,12 @@ int32_t dspark_layer_forward(const dspark_model* m, int32_t layer, int32_t with_
     HIPCHK(launch_post_resid(a, C.st));
   }
   if ((rc = attn_half(C, layer, P.ssq_b, kv, kv_offsets))) return rc;
-  ResidPost a = resid_base(C);
-  a.p = C.pin(P.p_o, L.o);
-  if (!with_mlp) {
-    a.x_out = x_out;
-    HIPCHK(launch_post_resid(a, C.st));
-    return DSPARK_OK;
-  }
-  a.g1 = (const float*)(m->base + L.post_norm);
-  a.fd = P.f_gu.fd;
-  a.ssq_out = C.ssq(P.ssq_a);
-  HIPCHK(launch_post_resid(a, C.st));
+  if (!with_mlp) return resid_gemm(C, L.o, P.p_o, P.f_o, C.x(), x_out, nullptr, nullptr, -1, nullptr);
+  if ((rc = resid_gemm(C, L.o, P.p_o, P.f_o, C.x(), C.x(), (const float*)(m->base + L.post_norm), &P.f_gu.fd,
+                       P.ssq_a, nullptr)))
+    return rc;
   if ((rc = mlp_half(C, layer, P.ssq_a))) return rc;
-  ResidPost b = resid_base(C);
-  b.p = C.pin(P.p_down, L.down);
-  b.x_out = x_out;
-  HIPCHK(launch_post_resid(b, C.st));
-  return DSPARK_OK;
+  return resid_gemm(C, L.down, P.p_down, P.f_down, C.x(), x_out, nullptr, nullptr, -1, nullptr);
 }
 
 // ---------------------------------------------------------- cache append --

@@ -73,8 +73,7 @@ __device__ __forceinline__ void gemv_row_scales(const RowScale& s, int M, int la
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int m = mt * 16 + j;
-      const float* p = s.ssq + (long long)m * SSQ_LD;
-      t[j] = m < M ? (lane < s.nch ? p[lane] : 0.f) + (lane + 64 < s.nch ? p[lane + 64] : 0.f) : 0.f;
+      t[j] = m < M ? chunk_lane_sum(s.ssq + (long long)m * SSQ_LD, s.nch, lane) : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) t[j] = wave_sum(t[j]);
@@ -238,6 +237,145 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
   }
 }
 
+// Inputs of the column-owning epilogue that do not depend on the product,
+// loaded by wave 0 before its weight stream starts (their latency then hides
+// under the stream instead of following it): per lane rows 4 (lane >> 4) + r,
+// columns 16 jo + (lane & 15) of the workgroup's 32 columns.
+struct OwnPre {
+  float x[4][2];     // RESID: residual stream
+  float g1[2], dw[2];  // gain of the next input, confidence weights
+  float ck[8];       // row-scale chunk sums, per lane (summed over the wave later)
+  float fs[4];       // FP8 column scales of the TPW tiles
+};
+
+template <int TPW>
+__device__ __forceinline__ void own_prefetch(const GemvArgs& a, int t0, int lane, OwnPre& pre) {
+  const int M = a.M, G = a.w.G;
+  constexpr int TO = 2;
+  const bool swiglu = TPW == 2 * TO;
+  const int outG = swiglu ? G / 2 : G;
+  const int c0 = blockIdx.x * (16 * TO);
+#pragma unroll
+  for (int jo = 0; jo < TO; ++jo) {
+    const int col = c0 + 16 * jo + (lane & 15);
+    const bool cok = col < outG;
+    pre.g1[jo] = a.g1 && cok ? a.g1[col] : 0.f;
+    pre.dw[jo] = a.dotw && cok ? a.dotw[col] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = (lane >> 4) * 4 + r;
+      const bool ok = lane < 32 && m < M && cok;
+      pre.x[r][jo] = a.epi == OWN_RESID && ok ? a.x_in[(long long)m * outG + col] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) pre.ck[m] = a.rs.ssq && m < M ? chunk_lane_sum(a.rs.ssq + (long long)m * SSQ_LD, a.rs.nch, lane) : 0.f;
+#pragma unroll
+  for (int j = 0; j < TPW && j < 4; ++j)
+    pre.fs[j] = a.w.fmt == DT_FP8 ? ((const float*)a.w.scales)[(long long)(t0 + j + (j >= TPW / 2 ? a.tile_jump : 0)) * 16 +
+                                                                 (lane & 15)]
+                                  : 1.f;
+}
+
+// Epilogue of the column-owning GEMM (NW waves share TPW tiles, each wave
+// summed its own k range).  The waves' accumulators meet in LDS and wave 0
+// adds them in wave order (fixed: deterministic), folds the hi/lo rows, and
+// writes the fused outputs of the workgroup's 32 columns: lane l < 32 holds
+// rows 4 (l >> 4) + r, column 16 jo + (l & 15) of output tile jo (jo = 0, 1;
+// for SWIGLU tiles 0, 1 are the gate and 2, 3 the up columns).  Per-row sums
+// over the 32 columns (RMSNorm statistics, the int8 block maximum) are taken
+// over each 16-lane DPP row, every lane taking part.
+template <int TPW, int NW>
+__device__ __forceinline__ void own_epilogue(const GemvArgs& a, const f32x4 (&acc)[TPW], int t0, int lane, int wave,
+                                             const OwnPre& pre) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char gemv_smem[];
+  f32x4* red = (f32x4*)gemv_smem;  // [NW][TPW][64]
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) red[(wave * TPW + j) * 64 + lane] = acc[j];
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 v[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    v[j] = red[j * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v[j] += red[(w * TPW + j) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[j][r] += __shfl_xor(v[j][r], 32, 64);
+  }
+  const int M = a.M, G = a.w.G;
+  constexpr int TO = 2;  // output tiles: 32 columns
+  static_assert(TPW == TO || TPW == 2 * TO, "plain (2 tiles) or gate/up (2 + 2 tiles)");
+  const bool swiglu = TPW == 2 * TO;
+  const int outG = swiglu ? G / 2 : G;      // output columns of the matrix
+  const int c0 = blockIdx.x * (16 * TO);    // first output column of the workgroup
+  // row scales from the prefetched chunk sums (the order gemv_row_scales uses)
+  float rsv[1][4] = {{1.f, 1.f, 1.f, 1.f}};
+  if (a.rs.ssq) {
+    float t[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) t[m] = wave_sum(pre.ck[m]);
+    const int q = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rsv[0][r] = rsqrtf((q == 0 ? t[r] : t[4 + r]) * a.rs.invn + a.rs.eps);
+  }
+  float fsv[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) fsv[j] = pre.fs[j];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = (lane >> 4) * 4 + r;
+    const bool rowok = lane < 32 && m < M;
+    float fin[TO], sq = 0.f, dt = 0.f, bm = 0.f;
+    int col[TO];
+    bool ok[TO];
+#pragma unroll
+    for (int jo = 0; jo < TO; ++jo) {
+      col[jo] = c0 + 16 * jo + (lane & 15);
+      ok[jo] = rowok && col[jo] < outG;
+      const long long xi = (long long)m * outG + col[jo];
+      float y = 0.f;
+      fin[jo] = 0.f;
+      if (ok[jo]) {
+        if (swiglu) {
+          const float g = v[jo][r] * fsv[jo] * rsv[0][r], u = v[jo + TO][r] * fsv[jo + TO] * rsv[0][r];
+          fin[jo] = g / (1.f + __expf(-g)) * u;
+        } else {
+          y = v[jo][r] * fsv[jo] * rsv[0][r];
+          if (a.epi == OWN_RESID) y += pre.x[r][jo];
+          a.x_out[xi] = y;
+          sq += y * y;
+          if (a.g1) {
+            fin[jo] = pre.g1[jo] * y;
+            if (a.dotw) dt += fin[jo] * pre.dw[jo];
+          }
+        }
+      }
+      bm = fmaxf(bm, fabsf(fin[jo]));
+    }
+    if (a.ssq_out) {
+      sq = row16_sum(sq);
+      if ((lane & 15) == 0 && rowok) a.ssq_out[m * SSQ_LD + blockIdx.x] = sq;
+    }
+    if (a.dot_out) {
+      dt = row16_sum(dt);
+      if ((lane & 15) == 0 && rowok) a.dot_out[m * SSQ_LD + blockIdx.x] = dt;
+    }
+    if (a.fd.ptr && (swiglu || a.g1)) {
+      if (a.fd.i8) {
+        bm = row16_max(bm);
+#pragma unroll
+        for (int jo = 0; jo < TO; ++jo)
+          if (ok[jo]) frag_put_i8(a.fd, 0, m, col[jo], fin[jo], bm);
+      } else {
+#pragma unroll
+        for (int jo = 0; jo < TO; ++jo)
+          if (ok[jo]) frag_put(a.fd, 0, m, col[jo], fin[jo]);
+      }
+    }
+  }
+}
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2, A_GLOBAL_I8 = 3, A_LDS_I8 = 4 };
@@ -282,18 +420,31 @@ __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, 
 //             block (factor d_w); s is applied once at the end.
 // Weight loads are issued in stages of U k steps x TPW tiles before any of
 // them is consumed.
-template <int FMT, int MT, int TPW, int MODE, int AMODE>
-__global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
+//
+// NW > 0 (GEMV_OWN): the workgroup's NW waves share its tiles and split the
+// reduction (wave w takes k range w); see own_epilogue.  NW == 0: the four
+// waves of a workgroup own consecutive tile sets and the k range is the
+// workgroup's split-K slice (blockIdx.y).
+template <int FMT, int MT, int TPW, int MODE, int AMODE, int NW = 0>
+__global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gemv_smem[];
   // wave index made wave-uniform (scalar): tile bases and buffer resources
   // derived from it live in scalar registers
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = a.w.ngroups * a.w.TG;
-  const int t0 = (blockIdx.x * 4 + wave) * TPW;
+  const int t0 = NW ? blockIdx.x * (a.tile_jump ? TPW / 2 : TPW) : (blockIdx.x * 4 + wave) * TPW;
   const bool active = t0 < T;
+  // tile j of this wave is t0 + tj(j); the span of tiles its loads cover
+  const int jump = NW ? a.tile_jump : 0;
+  auto tj = [&](int j) { return j + (j >= TPW / 2 ? jump : 0); };
+  const int span = TPW + jump;
   const int KB = a.w.KB;
-  const int kb0 = blockIdx.y * a.ksteps_per_split;
+  const int kb0 = (NW ? wave : (int)blockIdx.y) * a.ksteps_per_split;
   const int kb1 = min(KB, kb0 + a.ksteps_per_split);
+  OwnPre pre{};
+  if constexpr (NW > 0) {
+    if (wave == 0 && active) own_prefetch<TPW>(a, t0, lane, pre);
+  }
   const int nkb = kb1 - kb0;
   const int g = (AMODE == A_ROWS_BF || AMODE == A_ROWS_I8) ? min(blockIdx.x * 4 * TPW, T - 1) / a.w.TG
                                                              : (active ? t0 / a.w.TG : 0);
@@ -387,10 +538,10 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
     constexpr bool SL = AMODE == A_LDS_I8;
     constexpr int U = 8 / TPW;
     const int KP = KB >> 1, P0 = kb0 >> 1, P1 = kb1 >> 1;
-    const uint32_t wbytes = active ? (uint32_t)(TPW * KP * 1024) : 0u;
+    const uint32_t wbytes = active ? (uint32_t)(span * KP * 1024) : 0u;
     const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)(active ? t0 : 0) * KP * 1024, wbytes);
     const __amdgpu_buffer_rsrc_t sr = buf_rsrc((const unsigned char*)a.w.scales + (long long)(active ? t0 : 0) * KP * 64,
-                                               active ? (uint32_t)(TPW * KP * 64) : 0u);
+                                               active ? (uint32_t)(span * KP * 64) : 0u);
     const unsigned char* abase = (const unsigned char*)a.act + (long long)g * a.act_gstride;
     const __amdgpu_buffer_rsrc_t ar = buf_rsrc(abase, (uint32_t)(KB * 520));
     const uint32_t lw = lane * 16, ls = (lane & 15) * 4, la = lane * 8;
@@ -420,8 +571,8 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
           st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-              wr, ok ? (uint32_t)((j * KP + p) * 1024) + lw : BUF_OOB, 0, BUF_NT));
-          st.s[u][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, ok ? (uint32_t)((j * KP + p) * 64) + ls : BUF_OOB, 0, 0);
+              wr, ok ? (uint32_t)((tj(j) * KP + p) * 1024) + lw : BUF_OOB, 0, BUF_NT));
+          st.s[u][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, ok ? (uint32_t)((tj(j) * KP + p) * 64) + ls : BUF_OOB, 0, 0);
         }
         if constexpr (!SL) {
 #pragma unroll
@@ -528,9 +679,9 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
       // Split-K ranges are whole quads (KB % 4 == 0, unit 4).
       const int KQ = KB >> 2, q1 = kb1 >> 2;
       const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)t0 * KQ * 1024,
-                                                 (uint32_t)(TPW * KQ * 1024));
+                                                 (uint32_t)(span * KQ * 1024));
       const __amdgpu_buffer_rsrc_t sr = buf_rsrc((const unsigned char*)a.w.scales + (long long)t0 * KQ * 64,
-                                                 (uint32_t)(TPW * KQ * 64));
+                                                 (uint32_t)(span * KQ * 64));
       const uint32_t l16 = lane * 16, ls = (lane & 15) * 4;
       auto scale = [](uint32_t w, int i) {
         return i == 0 ? e8m0_f32<0>(w) : i == 1 ? e8m0_f32<1>(w) : i == 2 ? e8m0_f32<2>(w) : e8m0_f32<3>(w);
@@ -554,8 +705,8 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
               st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                  wr, ok ? (uint32_t)((j * KQ + p) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
-              st.s[u][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, ok ? (uint32_t)((j * KQ + p) * 64) + ls : BUF_OOB,
+                  wr, ok ? (uint32_t)((tj(j) * KQ + p) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
+              st.s[u][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, ok ? (uint32_t)((tj(j) * KQ + p) * 64) + ls : BUF_OOB,
                                                                 0, 0);
             }
 #pragma unroll
@@ -633,7 +784,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
       constexpr int U = 8 / TPW;
       const int KP = KB >> 1, p1 = kb1 >> 1;
       const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)t0 * KP * 1024,
-                                                 (uint32_t)(TPW * KP * 1024));
+                                                 (uint32_t)(span * KP * 1024));
       const __amdgpu_buffer_rsrc_t ar = buf_rsrc(afrag, (uint32_t)(KB * 1024));
       const uint32_t l16 = lane * 16;
       struct Stage {
@@ -648,7 +799,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
 #pragma unroll
           for (int j = 0; j < TPW; ++j)
             st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                wr, ok ? (uint32_t)((j * KP + p) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
+                wr, ok ? (uint32_t)((tj(j) * KP + p) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             st.x[u][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -693,7 +844,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
       // 1 KiB of activations).
       constexpr int U = (MT == 1 ? 8 : 4) / TPW;
       const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)t0 * KB * 1024,
-                                                 (uint32_t)(TPW * KB * 1024));
+                                                 (uint32_t)(span * KB * 1024));
       const __amdgpu_buffer_rsrc_t ar = buf_rsrc(afrag, (uint32_t)(MT * KB * 1024));
       const uint32_t l16 = lane * 16;
       struct Stage {
@@ -708,7 +859,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
 #pragma unroll
           for (int j = 0; j < TPW; ++j)
             st.w[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                wr, ok ? (uint32_t)((j * KB + kb) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
+                wr, ok ? (uint32_t)((tj(j) * KB + kb) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             st.x[u][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -887,7 +1038,12 @@ __global__ __launch_bounds__(256) void k_gemv_bf(GemvArgs a) {
       for (int j = 0; j < TPW; ++j) acc[0][j][r] *= f;
     }
   }
-  gemv_epilogue<MT, TPW, MODE>(a, acc, active, t0, lane, wave);
+  if constexpr (NW > 0) {
+    static_assert(MT == 1, "column-owning GEMMs take M <= 8 rows (hi/lo)");
+    own_epilogue<TPW, NW>(a, acc[0], t0, lane, wave, pre);
+  } else {
+    gemv_epilogue<MT, TPW, MODE>(a, acc, active, t0, lane, wave);
+  }
 }
 
 // F32 weights on v_mfma_f32_16x16x4_f32: four MFMAs per 16-wide k group.
@@ -1012,9 +1168,37 @@ hipError_t dispatch_markov(const GemvArgs& a, const GemvPlan& p, hipStream_t st)
   return go<FMT, 1, 1, GEMV_MARKOV>(a, p, st);
 }
 
+// Column-owning launches: one workgroup of 64 nw threads per 32 output
+// columns; weights in bf16 fragments order (BF16 / FP8 / MXFP4 with bf16
+// hi/lo activation fragments) or Q8_0 on int8 activation fragments.
+template <int FMT, int TPW, int NW>
+hipError_t go_own(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  const size_t lds = (size_t)NW * TPW * 64 * 16;
+  if constexpr (FMT == DT_Q8_0)
+    hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, GEMV_OWN, A_GLOBAL_I8, NW>), dim3(p.grid_x), dim3(64 * NW), lds, st, a);
+  else
+    hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, GEMV_OWN, A_GLOBAL, NW>), dim3(p.grid_x), dim3(64 * NW), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t dispatch_own(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+  if constexpr (FMT == DT_F32) {
+    return hipErrorInvalidValue;
+  } else {
+    if (p.MT != 1 || p.S != 1 || (FMT == DT_Q8_0) != (p.amode == A_GLOBAL_I8)) return hipErrorInvalidValue;
+    if (p.TPW == 2 && p.nw == 8) return go_own<FMT, 2, 8>(a, p, st);
+    if (p.TPW == 2 && p.nw == 4) return go_own<FMT, 2, 4>(a, p, st);
+    if (p.TPW == 4 && p.nw == 8) return go_own<FMT, 4, 8>(a, p, st);
+    if (p.TPW == 4 && p.nw == 4) return go_own<FMT, 4, 4>(a, p, st);
+    return hipErrorInvalidValue;
+  }
+}
+
 template <int FMT>
 hipError_t dispatch_fmt(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st) {
   switch (mode) {
+    case GEMV_OWN: return dispatch_own<FMT>(a, p, st);
     case GEMV_STORE: return dispatch_out<FMT, GEMV_STORE>(a, p, st);
     case GEMV_QLAT: return dispatch_out<FMT, GEMV_QLAT>(a, p, st);
     case GEMV_FRAG: return dispatch_out<FMT, GEMV_FRAG>(a, p, st);

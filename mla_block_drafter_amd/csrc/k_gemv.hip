@@ -76,6 +76,34 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   return p;
 }
 
+// Column-owning plan: a workgroup per OWN_COLS output columns, its waves
+// splitting the reduction.  About 2000 waves in all (eight per workgroup for
+// the 224-workgroup hidden-size outputs, four for the 448 of the fused
+// gate/up), each with at least one k unit.
+GemvPlan plan_own(const PackedMat& w, int M, bool swiglu, bool i8_in) {
+  GemvPlan p{};
+  if (M < 1 || M > 8 || w.ngroups != 1 || w.fmt == DT_F32) return p;
+  if (w.fmt == DT_Q8_0 && !i8_in) return p;
+  if (swiglu && (w.G % 2 || w.TG * 16 != w.G)) return p;
+  const int outG = swiglu ? w.G / 2 : w.G;
+  if (outG % OWN_COLS) return p;
+  const int nwg = outG / OWN_COLS;
+  const int unit = w.fmt == DT_MXFP4 ? 4 : (w.fmt == DT_Q8_0 || w.fmt == DT_FP8) ? 2 : 1;
+  const int units = (w.KB + unit - 1) / unit;
+  int nw = nwg >= 384 ? 4 : 8;
+  if (units < nw) nw = 4;
+  int per = (units + nw - 1) / nw * unit;
+  p.hilo = 1;
+  p.MT = 1;
+  p.TPW = swiglu ? 4 : 2;
+  p.nw = nw;
+  p.grid_x = nwg;
+  p.S = 1;
+  p.ksteps_per_split = per;
+  p.amode = w.fmt == DT_Q8_0 ? 3 : 0;
+  return p;
+}
+
 hipError_t launch_gemv_bf16(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 hipError_t launch_gemv_q8_0(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 hipError_t launch_gemv_fp8(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
@@ -84,6 +112,7 @@ hipError_t launch_gemv_f32(const GemvArgs& a, const GemvPlan& p, int mode, hipSt
 
 hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st) {
   if (mode != GEMV_STORE && mode != GEMV_MARKOV && p.S != 1) return hipErrorInvalidValue;
+  if ((mode == GEMV_OWN) != (p.nw > 0)) return hipErrorInvalidValue;
   switch (a.w.fmt) {
     case DT_BF16: return launch_gemv_bf16(a, p, mode, st);
     case DT_Q8_0: return launch_gemv_q8_0(a, p, mode, st);

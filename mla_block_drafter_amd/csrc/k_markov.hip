@@ -129,6 +129,7 @@ __device__ __forceinline__ void mk_fetch_z(const MarkovArgs& a, int step, int t0
 
 template <int KB>
 __global__ __launch_bounds__(MK_THREADS, 1) void k_markov_rollout(MarkovArgs a) {
+  if (a.fallback && *a.fallback == 0) return;  // the candidate rollout drafted the block
   __shared__ unsigned long long red[MK_WAVES * 16];
   __shared__ __attribute__((aligned(16))) float zl[MK_WAVES][16][MK_ZCOLS];  // lm_head logits [sequence][column], current step
   __shared__ int tok[16];

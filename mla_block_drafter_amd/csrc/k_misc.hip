@@ -55,6 +55,7 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
 // Tokens from the argmax keys, confidence sigmoid(w_h . hf_i + w_m . u_i + b)
 // with hf_i = rs_final * g_final * x, and the optional hidden output.
 __global__ __launch_bounds__(256) void k_markov_final(MarkovFinalArgs a) {
+  if (a.fallback && *a.fallback == 0) return;  // the candidate rollout wrote tokens and confidences
   __shared__ float red[4];
   __shared__ unsigned long long kred[4];
   const int s = blockIdx.x, i = blockIdx.y;  // one workgroup per (sequence, position)

@@ -11,10 +11,24 @@ namespace dspark {
 // ------------------------------------------------------------- skinny GEMM --
 // out[split][m][col] = sum over the split's k range of act[m][k] * W[col][k]
 // for the M activation rows (M = 7 per sequence), W streamed once from HBM.
-enum { GEMV_STORE = 0, GEMV_MARKOV = 1, GEMV_QLAT = 2, GEMV_FRAG = 3 };
+enum { GEMV_STORE = 0, GEMV_MARKOV = 1, GEMV_QLAT = 2, GEMV_FRAG = 3, GEMV_OWN = 4 };
 
-// Partial sums of squares per (row, 256-column chunk), row stride SSQ_LD.
-constexpr int SSQ_LD = 128;
+// Column-owning GEMM (GEMV_OWN): one workgroup owns 32 output columns (two
+// 16-row tiles; for the fused gate/up matrix the two gate tiles and the two
+// up tiles of those columns), its waves split the reduction and add their
+// partial sums in LDS in a fixed order, and one wave runs a fused epilogue:
+//   OWN_STORE:  x_out = W a (rows of the residual-stream layout) + chunk sums of x^2;
+//   OWN_RESID:  x_out = x_in + W a, chunk sums of x^2, fragments of g1 * x_out
+//               for the next GEMM, optional chunk sums of g1 * x_out * dotw;
+//   OWN_SWIGLU: fragments of silu(W_g a) * (W_u a) for the next GEMM.
+// Chunks are the workgroup's 32 columns (chunk index = workgroup index).
+enum { OWN_STORE = 1, OWN_RESID = 2, OWN_SWIGLU = 3 };
+constexpr int OWN_COLS = 32;
+
+// Partial sums of squares per (row, column chunk), row stride SSQ_LD: chunks
+// of 256 columns from the column-parallel kernels, of OWN_COLS columns from
+// the column-owning GEMMs.
+constexpr int SSQ_LD = 256;
 
 // Per-row RMSNorm scale rs[m] = 1/sqrt(sum_c ssq[m][c] * invn + eps); ssq = null: 1.
 struct RowScale {
@@ -25,12 +39,16 @@ struct RowScale {
 
 // Sum of the nch <= SSQ_LD chunk values of one row, by a whole wave (all 64
 // lanes call it with the same arguments): every chunk is loaded at once and
-// added in a fixed butterfly order, so the cost is one memory round trip and
-// every lane returns the same bits.
+// added in a fixed order (per lane, then a butterfly), so the cost is one
+// memory round trip and every lane returns the same bits.
+__device__ __forceinline__ float chunk_lane_sum(const float* row, int nch, int lane) {
+  float t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = lane + 64 * i < nch ? row[lane + 64 * i] : 0.f;
+  return (t[0] + t[1]) + (t[2] + t[3]);
+}
 __device__ __forceinline__ float chunk_sum_wave(const float* row, int nch) {
-  const int lane = threadIdx.x & 63;
-  const float t = (lane < nch ? row[lane] : 0.f) + (lane + 64 < nch ? row[lane + 64] : 0.f);
-  return wave_sum(t);
+  return wave_sum(chunk_lane_sum(row, nch, threadIdx.x & 63));
 }
 
 __device__ __forceinline__ float row_scale_wave(const RowScale& s, int m) {
@@ -63,10 +81,20 @@ struct GemvArgs {
   int step, block;
   const float* z;         // [n_seq*block][V]
   float* logits;          // optional [n_seq][block][V]
+  // OWN (column-owning GEMM, see GEMV_OWN): fused epilogue
+  int epi;                // OWN_STORE / OWN_RESID / OWN_SWIGLU
+  int tile_jump;          // tiles j >= TPW/2 of a workgroup sit tile_jump tiles further (gate/up: up rows)
+  const float* x_in;      // RESID: residual stream in [M][G]
+  float* x_out;           // STORE / RESID: output [M][G] (may alias x_in)
+  const float* g1;        // RESID: gain of the next GEMM's input (fragments of g1 * x_out); null: none
+  float* ssq_out;         // STORE / RESID: [M][SSQ_LD] chunk sums of x_out^2
+  const float* dotw;      // RESID: chunk sums of g1 * x_out * dotw -> dot_out (null: none)
+  float* dot_out;
 };
 
 struct GemvPlan {
   int MT, TPW, S, ksteps_per_split, hilo;
+  int nw;                 // GEMV_OWN: waves per workgroup splitting the reduction; 0: split-K over workgroups
   int grid_x;
   int amode;              // activation operand: 0 prepared global fragments,
                           // 1 fp32 rows -> bf16 fragments in LDS,
@@ -77,6 +105,11 @@ struct GemvPlan {
 // i8_in: the producer of the input can write int8 fragments (frag_put_wave /
 // the int8 FRAG epilogue), which Q8_0 weights with M <= 8 then read directly.
 GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather = false, bool i8_in = false);
+// Column-owning plan (M <= 8; 32 output columns per workgroup).  swiglu: the
+// fused gate/up matrix (G = 2 inter rows, gate then up).  Returns a plan with
+// nw == 0 when the shape or format is not covered (the caller then uses
+// plan_gemv and separate reduction kernels).
+GemvPlan plan_own(const PackedMat& w, int M, bool swiglu, bool i8_in);
 hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& p, int mode, hipStream_t st);
 
 // --------------------------------------------------------------- attention --
@@ -223,8 +256,38 @@ struct MarkovArgs {
   const float* sample_u;      // optional [n_seq][block][vocab] uniforms: Gumbel-max draws
   float inv_temp;             // 1 / temperature (with sample_u)
   int spin_limit;             // polls per position before expiry: 0 default, < 0 expire at once
+  const int* fallback;        // candidate pruning ran: nothing to do unless *fallback (null: always run)
 };
 int markov_rollout_wgs(int tiles);
+
+// Markov rollout by exact candidate pruning (k_markov_prune.hip).
+constexpr int MK_CHUNK = 2048;    // vocabulary rows per candidate workgroup
+constexpr int MK_CAPR = 512;      // list entries kept per position (all chunks)
+constexpr int MK_CAPG = 16;       // candidates kept per position after the global threshold
+constexpr int MK_MAX_BLOCK = 8;   // positions per block
+inline int markov_prune_chunks(int vocab) { return (vocab + MK_CHUNK - 1) / MK_CHUNK; }
+struct MarkovPruneArgs {
+  const float* z;             // lm_head logits [n_seq * block][vocab]
+  const float* n2;            // [vocab] upper bounds of W2's row norms
+  const unsigned* w1max;      // upper bound of W1's largest row norm (float bits)
+  int vocab, n_seq, block, R, KB, nch;
+  const void* w2;             // packed bf16 W2 (16-row tiles, KB k blocks)
+  const void* w1; int w1_f32, w1_ld;
+  const int32_t* prev_token; const int32_t* forced;
+  unsigned* lmax;             // [M] zeroed: order-preserving bits of the largest lower end so far
+  int* lcnt;                  // [M] zeroed: list entries appended
+  u32x4* list;                // [M][MK_CAPR] (row, z bits, bound bits, 0)
+  int* fallback;              // zeroed; 1 = too many candidates: the full rollout runs
+  RowScale rs_final; const float* dot; int nch_dot;
+  const float* conf_wm; const float* conf_b;
+  int32_t* tokens; float* conf; int32_t* status;
+};
+bool markov_prune_supported(int R, int block, int vocab);
+hipError_t launch_markov_prune(const MarkovPruneArgs& a, hipStream_t st);
+// Upper bounds of the row L2 norms of rows [V][R] (row stride ld, bf16 or
+// f32): nrm[v] (optional) and their maximum into *maxbits (optional, zeroed).
+hipError_t launch_row_norms(const void* rows, int f32, long long ld, int R, int V, float* nrm, unsigned* maxbits,
+                            hipStream_t st);
 bool markov_rollout_supported(int KB, int M, int vocab);
 hipError_t launch_markov_rollout(const MarkovArgs& a, int KB, hipStream_t st);
 
@@ -261,6 +324,7 @@ struct MarkovFinalArgs {
   const unsigned long long* slots; int nwg;
   const unsigned* rollout_err;
   int32_t* status;            // optional [1]: 1 if the rollout expired, else 0
+  const int* fallback;        // candidate pruning ran: nothing to do unless *fallback (null: always run)
 };
 hipError_t launch_markov_final(const MarkovFinalArgs& a, hipStream_t st);
 

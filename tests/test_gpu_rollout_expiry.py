@@ -45,16 +45,17 @@ def test_forced_expiry_is_loud_and_harmless(wl):
     from tests.gpu_common import GpuWorkload
     g = GpuWorkload(wl)
     t0, c0, s0 = _call(g, 0)
-    assert s0 == 0 and (t0 >= 0).all()
+    assert s0 in (0, 2) and (t0 >= 0).all()   # 2: drafted by the candidate rollout
     t1, c1, s1 = _call(g, -1)
     assert s1 == 1
     assert (t1 == -1).all(), t1
     assert np.isfinite(c1).all()
     t2, c2, s2 = _call(g, 0)
-    assert s2 == 0
+    assert s2 == s0
     np.testing.assert_array_equal(t2, t0)
     np.testing.assert_array_equal(c2.view(np.int32), c0.view(np.int32))
-    # a generous explicit bound behaves like the default one
+    # a generous explicit bound: the full rollout, the same draft (up to
+    # rounding ties against the candidate rollout, none in these fixtures)
     t3, c3, s3 = _call(g, 1 << 20)
     assert s3 == 0
     np.testing.assert_array_equal(t3, t0)
