@@ -428,8 +428,6 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
     P.mslots = take((long long)c.block * n_seq * P.mwgs * 8);
     P.merr = take(16);
     P.mfall = take(16);
-    P.mlmax = take((long long)M * 4);
-    P.mlcnt = take((long long)M * 4);
   }
   P.rows = c.block * c.n_heads;
   P.rows_pad = (int)rup(P.rows, 64);
@@ -453,7 +451,9 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   if (!m.layers_only) {
     P.z = take((long long)M * c.vocab * 4);
     P.nch_v = markov_prune_chunks(c.vocab);
-    P.mlist = take((long long)M * MK_CAPR * 16);
+    P.mlmax = take((long long)M * P.nch_v * 4);
+    P.mlcnt = take((long long)M * P.nch_v * 4);
+    P.mlist = take((long long)M * P.nch_v * MK_CAPC * 16);
   }
   P.total = off;
 }
@@ -985,7 +985,7 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
   // greedy passes that need neither the full logits nor the hidden state:
   // the candidate rollout first; the full rollout only if it falls back
   const bool prune = rollout && !in->sample_u && !out->logits && !out->hidden && in->poll_limit == 0 &&
-                     markov_prune_supported(c.markov_rank, c.block, c.vocab);
+                     m->w1_fmt == DT_BF16 && markov_prune_supported(c.markov_rank, c.block, c.vocab);
   const int* fallback = prune ? (const int*)(C.ws + P.mfall) : nullptr;
   if (prune) {
     MarkovPruneArgs a{};
@@ -1004,8 +1004,8 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in, dsp
     a.w1_ld = m->w1_ld;
     a.prev_token = in->prev_token;
     a.forced = in->forced_prev;
-    a.lmax = (unsigned*)(C.ws + P.mlmax);
-    a.lcnt = (int*)(C.ws + P.mlcnt);
+    a.lch = (float*)(C.ws + P.mlmax);
+    a.ccnt = (int*)(C.ws + P.mlcnt);
     a.list = (u32x4*)(C.ws + P.mlist);
     a.fallback = (int*)(C.ws + P.mfall);
     a.rs_final = C.rs(P.ssq_b, c.hidden);

@@ -261,8 +261,9 @@ struct MarkovArgs {
 int markov_rollout_wgs(int tiles);
 
 // Markov rollout by exact candidate pruning (k_markov_prune.hip).
-constexpr int MK_CHUNK = 2048;    // vocabulary rows per candidate workgroup
-constexpr int MK_CAPR = 512;      // list entries kept per position (all chunks)
+constexpr int MK_CHUNK = 8192;    // vocabulary rows per candidate workgroup (1024 threads)
+constexpr int MK_CAPC = 8;        // list entries kept per (position, chunk)
+constexpr int MK_MAXCH = 32;      // chunks per position: vocab <= MK_MAXCH * MK_CHUNK
 constexpr int MK_CAPG = 16;       // candidates kept per position after the global threshold
 constexpr int MK_MAX_BLOCK = 8;   // positions per block
 inline int markov_prune_chunks(int vocab) { return (vocab + MK_CHUNK - 1) / MK_CHUNK; }
@@ -274,9 +275,9 @@ struct MarkovPruneArgs {
   const void* w2;             // packed bf16 W2 (16-row tiles, KB k blocks)
   const void* w1; int w1_f32, w1_ld;
   const int32_t* prev_token; const int32_t* forced;
-  unsigned* lmax;             // [M] zeroed: order-preserving bits of the largest lower end so far
-  int* lcnt;                  // [M] zeroed: list entries appended
-  u32x4* list;                // [M][MK_CAPR] (row, z bits, bound bits, 0)
+  float* lch;                 // [M][nch] largest lower end of each chunk
+  int* ccnt;                  // [M][nch] rows of the chunk whose upper end reaches it
+  u32x4* list;                // [M][nch][MK_CAPC] the first of them: (row, z bits, bound bits, 0)
   int* fallback;              // zeroed; 1 = too many candidates: the full rollout runs
   RowScale rs_final; const float* dot; int nch_dot;
   const float* conf_wm; const float* conf_b;
