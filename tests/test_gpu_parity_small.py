@@ -1,7 +1,8 @@
 """GPU parity at sizes the oracle finishes in seconds: the tiny all-fp32
-drafter and a ragged mid-size geometry (hidden 352, vocab 1000, inter 480,
+drafter, a ragged mid-size geometry (hidden 352, vocab 1000, inter 480,
 v_head 24, three sequences with cache lengths 0 / 37 / 300) in every weight
-format, plus decoding and acceptance checks."""
+format, the same geometry with the full model's MLA head sizes, plus decoding
+and acceptance checks."""
 import itertools
 
 import numpy as np
@@ -80,6 +81,24 @@ def test_small_bs1_formats(fmt):
     g = _gw(wl)
     ref = O.draft_block(wl, g.stored, g.inputs)
     full_parity(g, ref, tol=2e-2, max_ties=1)
+
+
+# The full model's MLA head geometry (qk_nope 128, qk_rope 64, kv_lora 512)
+# with the other sizes small: one sequence (7 rows) takes the per-head fused
+# q_b + absorb kernel with Q8_0 q_b weights and the fused post + absorb with
+# bf16 ones; three sequences (21 rows) the split-K q_b GEMM.
+MLA_MID = C.small_model(n_heads=4, q_lora=256, kv_lora=512, qk_nope=128, qk_rope=64, v_head=128)
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "bf16"])
+@pytest.mark.parametrize("lens", [(77,), (0, 37, 300)])
+def test_mla_head_geometry(fmt, lens):
+    from tests.gpu_common import full_parity
+    wl = C.Workload(f"mla_mid_{fmt}", MLA_MID, FORMATS[fmt], seed=781, kv_lens=lens, fixture_gains=True)
+    print("case", fmt, lens, flush=True)
+    g = _gw(wl)
+    ref = O.draft_block(wl, g.stored, g.inputs)
+    full_parity(g, ref, tol=2e-2, max_ties=2)
 
 
 def test_small_sharp_attention_bf16():
