@@ -436,7 +436,19 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   P.zero_end = off;
   P.part = take(part);
   P.bkeys = take((long long)M * (c.kv_lora + c.qk_rope) * (kv_f32 ? 4 : 2));
-  P.C = 256;
+  // Keys per attention slot: 256, doubled (up to 2048) while the slot
+  // partials, written and read back once, would outweigh the cache bytes the
+  // slots cover, as long as the attention grid keeps at least two workgroups
+  // per CU (256 CUs).  Long contexts get large slots; short ones keep the
+  // parallelism.
+  {
+    const long long keys = total_ctx + (long long)n_seq * c.block;
+    const long long part_slot = 2LL * P.rows_pad * ((long long)c.kv_lora * 2 + 8);
+    const long long kv_row = (long long)(c.kv_lora + c.qk_rope) * (kv_f32 ? 4 : 2);
+    auto nslots = [&](long long cc) { return cdiv(keys, cc) + n_seq; };
+    P.C = 256;
+    while (P.C < 2048 && part_slot > P.C * kv_row && (P.rows_pad / 64) * nslots(2LL * P.C) >= 512) P.C *= 2;
+  }
   P.slots = (int)(cdiv(total_ctx + (long long)n_seq * c.block, P.C) + n_seq);
   if (!kv_f32) {
     P.opart = take((long long)P.slots * P.rows_pad * c.kv_lora * 2);

@@ -29,7 +29,7 @@ namespace {
 
 constexpr int KT = 32;  // keys per LDS tile
 constexpr int NBUF = 4;  // key tile buffers: three tiles in flight while one computes
-constexpr float REDO_SLACK = 60.f;  // natural-log units: e^60 * 256 keys stays far below fp32 max
+constexpr float REDO_SLACK = 60.f;  // natural-log units: e^60 * 2048 keys stays far below fp32 max
 constexpr int MAX_COMBINE_SLOTS = 4096;
 
 __device__ __forceinline__ void slot_lookup(const AttnArgs& a, int slot, int& s, int& p, int& len,
@@ -112,7 +112,7 @@ struct TileGeom {
 // Paged caches: the cache row of key kt0 (kt0 < len, wave-uniform) of a slot
 // whose first page is pfirst, lane i of pgv holding the slot's page i.
 __device__ __forceinline__ int paged_row(const AttnArgs& a, int kt0, int pfirst, int pgv) {
-  const int i = __builtin_amdgcn_readfirstlane((kt0 >> a.page_log2) - pfirst);  // 0 .. 7
+  const int i = __builtin_amdgcn_readfirstlane((kt0 >> a.page_log2) - pfirst);  // 0 .. 63
   const int page = __builtin_amdgcn_readlane(pgv, i);
   return (page << a.page_log2) + (kt0 & ((1 << a.page_log2) - 1));
 }
@@ -250,15 +250,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   const uint16_t* cache = (const uint16_t*)a.cache;
   const uint16_t* bk = (const uint16_t*)a.bkeys;
   const uint16_t* dummy = bk + (long long)s * a.block * a.latent;
-  // paged caches: the page indices of this slot's keys (at most C / 32 = 8),
+  // paged caches: the page indices of this slot's keys (at most C / 32 = 64),
   // one per lane of a VGPR, read once here: no memory load may enter the tile
-  // loop, whose LDS waits count on the shared counter (and eight scalar
-  // registers more would spill under this register pressure)
+  // loop, whose LDS waits count on the shared counter (and more scalar
+  // registers would spill under this register pressure)
   const int pfirst = PAGED ? k_begin >> a.page_log2 : 0;
   int pgv = 0;
   if (PAGED) {
     const int32_t* tb = a.table + (long long)s * a.max_pages;
-    pgv = tb[min(pfirst + (lane & 7), a.max_pages - 1)];
+    pgv = tb[min(pfirst + lane, a.max_pages - 1)];
   }
 
   // Q fragments (B operand of S^T = K Q^T): row myrow, dims 32kb + 8 grp.
@@ -608,9 +608,10 @@ bool attn_bf16_supported(int DQ, int r) {
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (a.rows_pad % 64 || (long long)(a.rows_pad / 64) * a.slots > INT32_MAX) return hipErrorInvalidValue;
-  // pages of at least one key tile; a slot's keys span at most 8 pages
-  if (a.page_log2 >= 0 && (a.page_log2 < 5 || a.page_log2 > 24 || !a.table || a.max_pages < 1 ||
-                           a.C % KT || a.C / KT > 8))
+  // slots of whole key tiles, at most 2048 keys; pages of at least one key
+  // tile, so a slot's keys span at most 64 pages (one per lane)
+  if (a.C < KT || a.C % KT || a.C > 2048) return hipErrorInvalidValue;
+  if (a.page_log2 >= 0 && (a.page_log2 < 5 || a.page_log2 > 24 || !a.table || a.max_pages < 1))
     return hipErrorInvalidValue;
   dim3 grid((a.rows_pad / 64) * a.slots), block(256);
   const bool paged = a.page_log2 >= 0;

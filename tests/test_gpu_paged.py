@@ -61,6 +61,22 @@ def test_full_size_q8_paged_equals_packed():
     print("cfg3 paged tokens", paged["tokens"].tolist(), flush=True)
 
 
+@pytest.mark.parametrize("lens", [(40960,), (30000, 50000, 20000)])
+def test_full_size_long_context_paged_equals_packed(lens):
+    """Long contexts take larger attention slots (512 keys for one sequence
+    at 40,960, 1024 keys for the three sequences), so with pages of 32 keys
+    a slot spans 16 or 32 pages."""
+    from tests.gpu_common import GpuWorkload
+    wl = C.CFG3.replace(name=f"long_paged_{len(lens)}", kv_lens=lens)
+    print("case", lens, flush=True)
+    g = GpuWorkload(wl)
+    packed = g.draft()
+    assert (packed["tokens"] >= 0).all()
+    g.use_pages(32, seed=7)
+    paged = g.draft()
+    _same(paged, packed)
+
+
 def test_paged_rejects_bad_page_size():
     from mla_block_drafter_amd import dspark as D
     from tests.gpu_common import GpuWorkload
