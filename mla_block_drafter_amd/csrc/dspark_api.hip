@@ -317,8 +317,9 @@ struct Frag {
   long long off = 0, bytes = 0;
 };
 
-// Input buffer of one GEMM: fp32 rows when the GEMM stages its activations
-// in LDS (plan.amode != 0), else prepared fragments.
+// Input buffer of one GEMM: int8 hi/lo codes (plan.amode 3), fp32 rows when
+// the GEMM converts its activations in LDS (amode 1 and 2), else prepared
+// fragments (amode 0).
 void frag_geom(Frag& f, const PackedMat& w, int M, const GemvPlan& p) {
   f.fd = FragDesc{};
   if (p.amode == 3) {  // int8 codes [KB][64][8 B] + exponents [KB][8]
@@ -328,7 +329,7 @@ void frag_geom(Frag& f, const PackedMat& w, int M, const GemvPlan& p) {
     f.bytes = f.fd.gstride * w.ngroups;
     return;
   }
-  if (p.amode != 0) {
+  if (p.amode == 1 || p.amode == 2) {
     f.fd.rows = 1;
     f.fd.ld = w.K;
     f.fd.gstride = (long long)M * w.K;

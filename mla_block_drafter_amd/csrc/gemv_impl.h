@@ -380,6 +380,19 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2, A_GLOBAL_I8 = 3, A_LDS_I8 = 4 };
 
+// Wait until at most N vector memory operations of this wave are outstanding:
+// the compiler's own builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their maxima), so that it knows which loads are
+// complete (its own analysis would wait for every load issued before the
+// direct-to-LDS copies), and a scheduling barrier, so that no use of those
+// loads is moved above it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Eight fp32 activations of row `row` from column k0 (zero outside M x K).
 __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, int row, int k0, float (&v)[8]) {
   const int K = a.w.K;
@@ -627,14 +640,12 @@ __global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
     const int nst = (P1 - P0 + U - 1) / U;
     load_stage(sa, P0);
     if constexpr (SL) {
-      // this wave's copies are done once at most the first stage's loads are
-      // outstanding; the barrier then covers every wave's copies.  The wait
-      // is the builtin (gfx9 encoding: vmcnt split over bits 3:0 and 15:14,
-      // expcnt and lgkmcnt left at their maxima) so that the compiler knows
-      // the copies are complete and adds no wait for them in the loop.
-      constexpr int NV = 2 * U * TPW;
-      static_assert(NV < 64, "vmcnt range");
-      __builtin_amdgcn_s_waitcnt((NV & 15) | (7 << 4) | (15 << 8) | ((NV >> 4) << 14));
+      // Direct-to-LDS copies complete in no fixed order with the other
+      // vector memory operations, so only a count of zero proves this wave's
+      // copies landed (the first weight stage, issued after them, is waited
+      // for as well); the barrier then covers every wave's copies.  The
+      // builtin lets the compiler know the copies are complete.
+      vm_wait<0>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }

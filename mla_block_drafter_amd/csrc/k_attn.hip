@@ -98,7 +98,6 @@ struct TileGeom {
   static constexpr int NB_B = KT / KPB;           // loads for region B
   static constexpr int NBLK = NB_A + NB_B;
   static constexpr int BUF = SIZE_A + KT * CB * 8;  // elements per tile buffer
-  static constexpr int NMIN = NBLK / 4;           // loads per wave per tile (at least)
   static_assert(64 % CB == 0 && KT % KPB == 0 && CA <= 64, "tile geometry");
 };
 
@@ -228,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   constexpr int CA = R / 8, CB = (DQ - R) / 8;
   using G = TileGeom<CA, CB>;
   static_assert(CA % 4 == 0, "each k-step reads one region");
-  static_assert(NBUF == 4 && 2 * G::NMIN <= 63, "vmcnt range");
+  static_assert(NBUF == 4, "tile buffers");
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF * G::BUF];
 
   const int ngrp = a.rows_pad / 64;
@@ -305,17 +304,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
       issue_tile<CA, CB, PAGED>(a, lane, wave, k_begin + i * KT, k_end, s, len, PAGED ? paged_row(a, k_begin + i * KT, pfirst, pgv) : off + k_begin + i * KT, cache, bk, dummy,
                          k_lds + i * G::BUF);
 
-  // One barrier per tile.  Tile t is in LDS once at most the loads of the
-  // tiles issued after it (t + 1 .. t + NBUF - 2, at least NMIN loads per
-  // tile for every wave) are outstanding; after the barrier every wave has
-  // also finished tile t - 1, whose buffer then receives tile t + NBUF - 1.
+  // One barrier per tile.  Direct-to-LDS copies complete in no fixed order
+  // with respect to each other, so a partial count does not prove that tile
+  // t has landed (waiting for "at most the later tiles' copies outstanding"
+  // let a late copy of tile t be read, now and then, as a slightly different
+  // result): each wave waits for all of its copies, then the barrier covers
+  // every wave's.  Tiles t + 1 and t + 2 are then in LDS early; tile
+  // t + NBUF - 1 goes out after the barrier (every wave has finished tile
+  // t - 1, whose buffer it takes) and streams in during this tile's compute.
   for (int t = 0; t < ntiles; ++t) {
     const int kt0 = k_begin + t * KT;
     const int buf = t % NBUF;
-    const int after = min(NBUF - 2, ntiles - 1 - t);
-    if (after >= 2) wait_vmcnt<2 * G::NMIN>();
-    else if (after == 1) wait_vmcnt<G::NMIN>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<0>();
     // the barrier intrinsic has no memory semantics of its own, so the
     // compiler fences keep LDS accesses on their side of it (a __syncthreads
     // would also drain the prefetch of the next tiles)

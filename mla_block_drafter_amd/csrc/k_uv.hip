@@ -29,19 +29,6 @@ constexpr int UVC_CHUNK = 40;  // slots whose partials are requested together
 constexpr int UVC_OLD = UVC_TILES * 16 + 4;  // LDS row stride of the GEMM outputs
 constexpr int UVC_RPW = 2;     // block rows per workgroup
 
-// Wait until at most N vector memory operations of this wave are outstanding:
-// the compiler's own builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt and lgkmcnt left at their maxima), so that it knows which loads are
-// complete (its own analysis would wait for every load issued before the
-// direct-to-LDS copies), and a scheduling barrier, so that no use of those
-// loads is moved above it.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Slot U of the first chunk (weight in lane U of e0), then the next slot:
 // each waits only for its own partials (issued in slot order, NAFTER more
 // operations issued after the chunk).
