@@ -10,15 +10,17 @@
 //
 // bf16 path (split-K, flash-decoding style): a workgroup of 4 waves owns 64
 // query rows and one slot of C keys.  Key tiles of 32 rows are staged in LDS
-// row-major, four buffers deep.  S^T = K Q^T takes the key rows as the A operand (16-byte LDS
-// reads), so the probabilities land with one query row per lane column,
-// which is already the B-operand layout of P^T for O^T = V^T P^T: the
-// probabilities never leave registers (the 32 keys' order inside the MFMA
+// row-major, four buffers deep, by direct-to-LDS copies.  S^T = K Q^T takes
+// the key rows as the A operand (16-byte LDS reads), so the probabilities
+// land with one query row per lane column, which is already the B-operand
+// layout of P^T for O^T = V^T P^T (the 32 keys' order inside the MFMA
 // reduction is permuted identically on both operands).  The V^T operand is
-// gathered from the same row-major tile with 2-byte LDS reads (the value is
-// c_kv, the first kv_lora columns of the key row), so no transposed copy is
-// staged.  Online softmax state (m, l) is per lane column.  Partials per slot
-// are merged by k_attn_combine in a fixed order.
+// gathered from the same row-major tile with transposing LDS reads (the
+// value is c_kv, the first kv_lora columns of the key row), so no transposed
+// copy is staged.  Two waves share 32 query rows and split the work so that
+// every fragment read from LDS feeds two matrix instructions (see the
+// kernel).  Partials per slot are merged in a fixed order by k_attn_combine
+// or k_uv_combine.
 #include <type_traits>
 
 #include "kernels.h"
@@ -137,13 +139,15 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, int lane, int wave
     }
     return;
   }
+  // a slot's last tile, or one that reaches the block's own keys: each row
+  // chosen on its own (a runtime loop: this path runs once or twice per slot)
   auto row_ptr = [&](int j) {
     const uint16_t* c = cache + (long long)(trow + j - kt0) * a.latent;
     const uint16_t* k = bk + (long long)(s * a.block + (j - len)) * a.latent;
     const uint16_t* r = j < len ? c : k;
     return j < k_end ? r : dummy;
   };
-#pragma unroll
+#pragma unroll 1
   for (int i = 0; i < G::NB_A / 4; ++i) {
     const int b = wave + 4 * i;
     const uint16_t* src = row_ptr(kt0 + b) + 8 * lane;
@@ -155,6 +159,13 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, int lane, int wave
     const uint16_t* src = 8 * c < a.latent ? row_ptr(kt0 + r) + 8 * c : dummy;
     __builtin_amdgcn_global_load_lds(src, dst + G::SIZE_A + wave * 512, 16, 0, 0);
   }
+}
+
+// One wave-wide 16-byte-per-lane direct-to-LDS copy.  (Called from the
+// kernel's lambdas through this device function: a lambda that names the
+// builtin itself makes the host compilation drop the kernel's launch stub.)
+__device__ __forceinline__ void copy_lds16(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
 // Workgroups go to the 8 XCDs round-robin (linear id L to XCD L % 8), and
@@ -218,21 +229,66 @@ __device__ __forceinline__ void lds_wait_pair(u32x2& lo, u32x2& hi) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo), "+v"(hi) : "n"(N));
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <int N>
+__device__ __forceinline__ void lds_wait_pair_x(u32x2& lo, u32x2& hi, u32x4& x) {
+  asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(lo), "+v"(hi), "+v"(x) : "n"(N));
+}
 
+// Items of a tile step.  With the next-but-one tile's scores to compute
+// (KEYS), value-fragment pairs and key fragments alternate (V0 K0 V1 K1 ...,
+// then the rest of the longer list), so that the LDS-bound value reads and
+// the matrix-core-bound score products overlap; otherwise only value pairs.
+template <int ND, int NKB, bool KEYS>
+struct StepItems {
+  static constexpr int NP = KEYS ? (ND < NKB ? ND : NKB) : 0;  // alternating pairs
+  static constexpr int N = ND + (KEYS ? NKB : 0);
+  static constexpr bool is_v(int i) { return i < 2 * NP ? i % 2 == 0 : (KEYS ? ND > NKB : true); }
+  static constexpr int idx(int i) { return i < 2 * NP ? i / 2 : i - NP; }
+  static constexpr int ops(int i) { return is_v(i) ? 2 : 1; }  // LDS reads per item
+  // LDS reads issued after item i when items up to i + W are issued
+  template <int W>
+  static constexpr int after(int i) {
+    int n = 0;
+    const int last = i + W < N - 1 ? i + W : N - 1;
+    for (int j = i + 1; j <= last; ++j) n += ops(j);
+    return n;
+  }
+};
+
+// Waves 2p and 2p + 1 form pair p and share the query rows 32p .. 32p + 31
+// of the workgroup's 64 (two 16-row MFMA blocks rb).  For S^T = K Q^T member
+// h of the pair takes the keys of tile half h (16 keys) over every query
+// dim, so each key fragment read from LDS feeds both row blocks; for
+// O^T = V^T P^T it takes value dims h * R/2 .. (h + 1) * R/2 - 1 over all 32
+// keys, so each value fragment also feeds both row blocks.  The members
+// swap their bf16 probabilities through LDS (1 KiB per wave and tile).
+// Per wave and tile this reads half the LDS bytes of one wave per 16 rows
+// for the same matrix-core work.
+//
+// Software pipeline, one barrier per tile: step t multiplies P(t) by tile
+// t's values, computes the scores of tile t + 2, and between those matrix
+// instructions turns the scores of tile t + 1 (computed by the previous
+// step) into probabilities, which the next barrier makes visible to the
+// partner.  One wave per SIMD then keeps its matrix core busy while its LDS
+// reads and exponentials are in flight.
 template <int NKB, int NDT, bool PAGED>
 __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   constexpr int DQ = NKB * 32;
   constexpr int R = NDT * 16;
   constexpr int CA = R / 8, CB = (DQ - R) / 8;
+  constexpr int ND = NDT / 2;  // value dim tiles per wave
   using G = TileGeom<CA, CB>;
-  static_assert(CA % 4 == 0, "each k-step reads one region");
+  static_assert(CA % 4 == 0 && NDT % 2 == 0, "each k-step reads one region; value dims split in two");
   static_assert(NBUF == 4, "tile buffers");
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[NBUF * G::BUF];
+  __shared__ __attribute__((aligned(16))) u32x4 xp[2][4][64];  // own probabilities, by tile parity and wave
+  __shared__ float xm[4][2][16];                              // row maxima of a wave's keys
+  __shared__ float xl[4][2][16];                              // row sums of a wave's keys
+  __shared__ int xv[4];                                       // redo votes
 
   const int ngrp = a.rows_pad / 64;
-  const int pair = xcd_pair(blockIdx.x, gridDim.x);
-  const int slot = pair / ngrp, rgrp = pair % ngrp;
+  const int pair_id = xcd_pair(blockIdx.x, gridDim.x);
+  const int slot = pair_id / ngrp, rgrp = pair_id % ngrp;
   int s, p, len, off, J;
   slot_lookup(a, slot, s, p, len, off, J);
   if (s < 0) return;  // uniform over the workgroup
@@ -242,8 +298,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile loads scalar
-  const int row0 = rgrp * 64 + wave * 16;
-  const int myrow = row0 + (lane & 15);
+  const int mem = wave & 1;                                          // key half (S), value half (O)
+  const int prow0 = rgrp * 64 + (wave >> 1) * 32;                    // the pair's first row
   const int grp = lane >> 4;
 
   const uint16_t* cache = (const uint16_t*)a.cache;
@@ -251,219 +307,342 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
   const uint16_t* dummy = bk + (long long)s * a.block * a.latent;
   // paged caches: the page indices of this slot's keys (at most C / 32 = 64),
   // one per lane of a VGPR, read once here: no memory load may enter the tile
-  // loop, whose LDS waits count on the shared counter (and more scalar
-  // registers would spill under this register pressure)
+  // loop, whose LDS waits count on the shared counter
   const int pfirst = PAGED ? k_begin >> a.page_log2 : 0;
   int pgv = 0;
   if (PAGED) {
     const int32_t* tb = a.table + (long long)s * a.max_pages;
     pgv = tb[min(pfirst + lane, a.max_pages - 1)];
   }
+  auto tile_row = [&](int kt0) { return PAGED ? paged_row(a, kt0, pfirst, pgv) : off + kt0; };
+  auto issue = [&](int i) {  // key tile i of the slot into buffer i % NBUF
+    const int kt0 = k_begin + i * KT;
+    issue_tile<CA, CB, PAGED>(a, lane, wave, kt0, k_end, s, len, tile_row(kt0), cache, bk, dummy,
+                              k_lds + (i % NBUF) * G::BUF);
+  };
 
-  // Q fragments (B operand of S^T = K Q^T): row myrow, dims 32kb + 8 grp.
-  bf16x8 qf[NKB];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((long long)s * a.rows_pad + myrow) * DQ + 8 * grp;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) qf[kb] = *(const bf16x8*)(qrow + 32 * kb);
-  }
-  // LDS element offsets inside a tile buffer
-  const int kA = key_perm(lane & 15);                 // key of this lane's A-operand row
-  const int offA = kA * G::ROW_A + 8 * grp;           // + 16 h ROW_A + 32 kb
-  const int offB = G::SIZE_A + kA * CB * 8;           // + 16 h CB 8 + chunk
-  // byte offsets of chunks 4 k + grp (k < CB / 4) of region B for this lane's key
-  uint32_t bx[CB / 4];
-#pragma unroll
-  for (int k = 0; k < CB / 4; ++k) bx[k] = 16 * ((4 * k + grp) ^ bswz<CB>(kA));
-  const int kV = key_perm(4 * grp + ((lane & 15) >> 2));  // key this lane addresses for V
-  const int offV = kV * G::ROW_A + 4 * (lane & 3);    // + 16 h ROW_A + 16 d
-  int keyS[4];                                        // keys of this lane's score entries
-#pragma unroll
-  for (int j = 0; j < 4; ++j) keyS[j] = key_perm(4 * grp + j);
-
-  // Softmax reference: the first tile's row maximum (pass 0).  The tile loop
-  // never rescales the accumulators (they stay in AGPRs untouched by the
-  // VALU); if a later score exceeds the reference by more than REDO_SLACK,
-  // where exp() could approach the fp32 range, the workgroup redoes the slot
-  // once with the exact row maximum as the reference (pass 1).
-  // The running maximum and sum stay per lane inside the tile loop (no
-  // cross-lane traffic there); the four lanes of a row are combined after it.
-  __shared__ int redo_flag;
-  const float c2 = a.tau * 1.4426950408889634f;  // base-2 score scale
-  f32x4 acc[NDT];
-  float m_run = -INFINITY, l_run = 0.f, m_all = -INFINITY;
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-  for (int d = 0; d < NDT; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  l_run = 0.f;
-  if (pass == 1) m_run = m_all;
-  // prologue: tiles 0 .. NBUF - 2 in flight
-#pragma unroll 1
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (i < ntiles)
-      issue_tile<CA, CB, PAGED>(a, lane, wave, k_begin + i * KT, k_end, s, len, PAGED ? paged_row(a, k_begin + i * KT, pfirst, pgv) : off + k_begin + i * KT, cache, bk, dummy,
-                         k_lds + i * G::BUF);
-
-  // One barrier per tile.  Direct-to-LDS copies complete in no fixed order
-  // with respect to each other, so a partial count does not prove that tile
-  // t has landed (waiting for "at most the later tiles' copies outstanding"
-  // let a late copy of tile t be read, now and then, as a slightly different
-  // result): each wave waits for all of its copies, then the barrier covers
-  // every wave's.  Tiles t + 1 and t + 2 are then in LDS early; tile
-  // t + NBUF - 1 goes out after the barrier (every wave has finished tile
-  // t - 1, whose buffer it takes) and streams in during this tile's compute.
-  for (int t = 0; t < ntiles; ++t) {
-    const int kt0 = k_begin + t * KT;
-    const int buf = t % NBUF;
-    wait_vmcnt<0>();
-    // the barrier intrinsic has no memory semantics of its own, so the
-    // compiler fences keep LDS accesses on their side of it (a __syncthreads
-    // would also drain the prefetch of the next tiles)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (t + NBUF - 1 < ntiles)
-      issue_tile<CA, CB, PAGED>(a, lane, wave, kt0 + (NBUF - 1) * KT, k_end, s, len, PAGED ? paged_row(a, kt0 + (NBUF - 1) * KT, pfirst, pgv) : off + kt0 + (NBUF - 1) * KT, cache,
-                         bk, dummy,
-                         k_lds + ((t + NBUF - 1) % NBUF) * G::BUF);
-    const uint16_t* tb = k_lds + buf * G::BUF;
-
-    // ---- S^T for 32 keys x 16 rows: two 16-key MFMA tiles, read n = 2 kb + h
-    //      feeding accumulator h; the two chains alternate ----
-    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    {
-      constexpr int NR = 2 * NKB;
-      const uint32_t abase = lds_addr(tb + offA), bbase = lds_addr(tb + offB);
-      u32x4 kf[QK_AHEAD + 1];
-      auto issue = [&](auto NI) {
-        constexpr int n = decltype(NI)::value, kb = n / 2, h = n % 2;
-        if constexpr (4 * kb < CA)
-          lds_read_b128<2 * (16 * h * G::ROW_A + 32 * kb)>(abase, kf[n % (QK_AHEAD + 1)]);
-        else
-          lds_read_b128<2 * 16 * h * CB * 8>(bbase + bx[kb - CA / 4], kf[n % (QK_AHEAD + 1)]);
-      };
-      static_for<QK_AHEAD < NR ? QK_AHEAD : NR>(issue);
-      static_for<NR>([&](auto NI) {
-        constexpr int n = decltype(NI)::value;
-        if constexpr (n + QK_AHEAD < NR) issue(std::integral_constant<int, n + QK_AHEAD>{});
-        constexpr int ahead = NR - 1 - n < QK_AHEAD ? NR - 1 - n : QK_AHEAD;
-        u32x4& f = kf[n % (QK_AHEAD + 1)];
-        lds_wait<ahead>(f);
-        st[n % 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f), qf[n / 2], st[n % 2], 0, 0, 0);
-      });
-    }
-    // the first V fragments do not depend on P: their reads go out now and
-    // arrive while the probabilities are computed
-    const uint32_t vaddr = lds_addr(tb + offV);
-    u32x2 vlo[PV_AHEAD + 1], vhi[PV_AHEAD + 1];
-    auto issue_v = [&](auto DI) {
-      constexpr int d = decltype(DI)::value;
-      tr_read_pair<32 * d, 32 * d + 2 * 16 * G::ROW_A>(vaddr, vlo[d % (PV_AHEAD + 1)], vhi[d % (PV_AHEAD + 1)]);
-    };
-    static_for<PV_AHEAD < NDT ? PV_AHEAD : NDT>(issue_v);
-
-    // lane holds keys kt0 + 16 h + keyS[r] for query row myrow.  Scores are
-    // kept in base-2 units x = s * tau * log2(e) (tau > 0, so the maximum of
-    // the raw products gives the maximum of x); keys past the slot (last
-    // tile only) get -inf.
-    if (kt0 + KT > k_end) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kt0 + 16 * h + keyS[r] >= k_end) st[h][r] = -INFINITY;
-    }
-    float tmax = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
-                       fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3]))) * c2;
-    m_all = fmaxf(m_all, tmax);  // this lane's keys only
-    if (pass == 0 && t == 0) {
-      // the reference: the row maximum over tile 0 (finite: tile 0 holds a
-      // valid key).  These shuffles are LDS operations issued after the V
-      // reads above; the compiler waits for them (and so for the V reads)
-      // before m_run is used.
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      m_run = tmax;
-    }
-    u32x4 pw;
+  // Q fragments (B operand of S^T = K Q^T): rows prow0 + 16 rb + (lane & 15),
+  // dims 32 kb + 8 grp; read from LDS after the workgroup's copy (pass 0)
+  bf16x8 qf[2][NKB];
+  // The workgroup's 64 query rows into tile buffers 2 and 3 (rows 32 h ..
+  // 32 h + 31 into buffer 2 + h) in the key tiles' layout, so that they are
+  // read back like key fragments: one copy per workgroup instead of one load
+  // per wave.
+  auto issue_q = [&]() {
+    const uint16_t* q = (const uint16_t*)a.q + ((long long)s * a.rows_pad + rgrp * 64) * DQ;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float pr[4];
+      uint16_t* dst = k_lds + (2 + h) * G::BUF;
+      const uint16_t* src = q + (long long)(32 * h + wave) * DQ + 8 * lane;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[h][r], c2, -m_run));
-        l_run += pr[r];  // this lane's keys only
+      for (int i = 0; i < G::NB_A / 4; ++i, src += 4 * DQ)
+        if (CA == 64 || lane < CA) copy_lds16(src, dst + (wave + 4 * i) * G::ROW_A);
+      if (wave < G::NB_B) {
+        const int r = wave * G::KPB + lane / CB, c = CA + ((lane % CB) ^ bswz<CB>(r));
+        copy_lds16(q + (long long)(32 * h + r) * DQ + 8 * c, dst + G::SIZE_A + wave * 512);
       }
-      pw[2 * h] = pack_bf16x2(pr[0], pr[1]);
-      pw[2 * h + 1] = pack_bf16x2(pr[2], pr[3]);
     }
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-
-    // ---- O^T += V^T P^T.  k slots 0..3 of lane group g are keys keyS[] of
-    //      the first half, slots 4..7 those of the second half, matching P.
-    //      The transposing read hands lane 4a + e of each 16-lane group
-    //      element e of the rows addressed by lanes a, a+4, a+8, a+12: lane
-    //      (lane & 15) = 4 j + a addresses key keyS[j], dims 16 d + 4 a, so
-    //      lane 4a + e receives dim 16 d + 4a + e of keys keyS[0..3] ----
-    {
-      static_for<NDT>([&](auto DI) {
-        constexpr int d = decltype(DI)::value;
-        if constexpr (d + PV_AHEAD < NDT) issue_v(std::integral_constant<int, d + PV_AHEAD>{});
-        constexpr int ahead = NDT - 1 - d < PV_AHEAD ? NDT - 1 - d : PV_AHEAD;
-        u32x2& lo = vlo[d % (PV_AHEAD + 1)];
-        u32x2& hi = vhi[d % (PV_AHEAD + 1)];
-        lds_wait_pair<2 * ahead>(lo, hi);
-        const u32x4 v4 = {lo[0], lo[1], hi[0], hi[1]};
-        acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v4), pf, acc[d], 0, 0, 0);
-      });
-    }
-  }
-    // combine the four lanes of each row (fixed butterfly: same bits in all)
-    m_all = fmaxf(m_all, __shfl_xor(m_all, 16, 64));
-    m_all = fmaxf(m_all, __shfl_xor(m_all, 32, 64));
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    if (pass == 1) break;
-    // every wave has finished its tile reads; decide the redo together (the
-    // barriers also keep the redo's tile loads off buffers still being read)
-    if (threadIdx.x == 0) redo_flag = 0;
-    __syncthreads();
-    if (__any(m_all > m_run + REDO_SLACK * 1.4426950408889634f) && lane == 0) atomicOr(&redo_flag, 1);
-    __syncthreads();
-    if (!redo_flag) break;
-  }
-
-  // ---- partials: O^T[dim = 16d + 4(lane>>4) + r][row = myrow] divided by
-  //      l, a convex combination of value rows, stored as fp16 (half the
-  //      bytes of fp32; 11-bit significand, finer than the bf16 operands).
-  //      Layout [row][slot][dim] so the combine of one row reads contiguous
-  //      memory.  l >= 1: the reference key of the slot contributes exp(0). ----
-  //      Each wave stages its 16 rows in LDS and stores them as whole rows
-  //      (one 1 KiB row per store instead of 16 scattered 32-byte pieces).
-  const long long prow = (long long)myrow * a.slots + slot;
-  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-  __syncthreads();  // every wave is done with the tile buffers
-  constexpr int RB = R * 2 + 16;  // bytes per staged row (the pad spreads the banks)
-  unsigned char* stage = (unsigned char*)k_lds + wave * 16 * RB;
+  };
+  // LDS element offsets inside a tile buffer
+  const int kA = key_perm(lane & 15);                                 // key of this lane's A-operand row
+  const int offA = (16 * mem + kA) * G::ROW_A + 8 * grp;              // + 32 kb
+  const int offB = G::SIZE_A + (16 * mem + kA) * CB * 8;              // + chunk
+  uint32_t bx[CB / 4];  // byte offsets of chunks 4 k + grp of region B for this lane's key
 #pragma unroll
-  for (int d = 0; d < NDT; ++d) {
-    u32x2 h;
-    h[0] = pack_f16x2(acc[d][0] * inv_l, acc[d][1] * inv_l);
-    h[1] = pack_f16x2(acc[d][2] * inv_l, acc[d][3] * inv_l);
-    *(u32x2*)(stage + (lane & 15) * RB + (16 * d + 4 * grp) * 2) = h;
+  for (int k = 0; k < CB / 4; ++k) bx[k] = 16 * ((4 * k + grp) ^ bswz<CB>(kA));
+  const int kV = key_perm(4 * grp + ((lane & 15) >> 2));              // key this lane addresses for V
+  const int offV = kV * G::ROW_A + 4 * (lane & 3) + 16 * ND * mem;   // + 16 h ROW_A + 16 d
+  int keyS[4];                                                        // keys of this lane's score entries
+#pragma unroll
+  for (int j = 0; j < 4; ++j) keyS[j] = 16 * mem + key_perm(4 * grp + j);
+  const uint32_t xp_par = lds_addr((const uint16_t*)&xp[0][wave ^ 1][lane]);
+  constexpr uint32_t XP_PARITY = 4 * 64 * 16;  // bytes between the two tile parities
+
+  const float c2 = a.tau * 1.4426950408889634f;  // base-2 score scale
+  f32x4 acc[2][ND];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, m_all[2] = {-INFINITY, -INFINITY};
+  u32x4 pown;          // this wave's bf16 probabilities of a tile: row block rb in dwords 2 rb, 2 rb + 1
+  f32x4 scn[2];        // scores of the tile after the current one (row block rb)
+  float pr[2][4];      // probabilities being formed
+
+  // Key-fragment read kb of the tile buffer at ab (region A) / bb (region B).
+  auto read_k = [&](auto KI, uint32_t ab, uint32_t bb, u32x4& dst) {
+    constexpr int kb = decltype(KI)::value;
+    if constexpr (4 * kb < CA)
+      lds_read_b128<2 * 32 * kb>(ab, dst);
+    else
+      lds_read_b128<0>(bb + bx[kb - CA / 4], dst);
+  };
+  // Softmax of one tile's scores sc[rb][r] (key kt0 + keyS[r], row 16 rb +
+  // (lane & 15)) in pieces: 0 masks and takes the maxima, 1 + 4 rb + r forms
+  // one probability, 9 packs them into pown.  Base-2 units
+  // x = s tau log2(e): tau > 0, so the maximum of the raw products gives the
+  // maximum of x.  Keys past the slot (last tile only) get -inf.
+  auto sm_piece = [&](auto PI, f32x4 (&sc)[2], int kt0) {
+    constexpr int pc = decltype(PI)::value;
+    if constexpr (pc == 0) {
+      if (kt0 + KT > k_end) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kt0 + keyS[r] >= k_end) sc[rb][r] = -INFINITY;
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        m_all[rb] = fmaxf(m_all[rb], fmaxf(fmaxf(sc[rb][0], sc[rb][1]), fmaxf(sc[rb][2], sc[rb][3])) * c2);
+    } else if constexpr (pc <= 8) {
+      constexpr int rb = (pc - 1) / 4, r = (pc - 1) % 4;
+      pr[rb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][r], c2, -m_run[rb]));
+      l_run[rb] += pr[rb][r];  // this lane's keys only
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        pown[2 * rb] = pack_bf16x2(pr[rb][0], pr[rb][1]);
+        pown[2 * rb + 1] = pack_bf16x2(pr[rb][2], pr[rb][3]);
+      }
+    }
+  };
+  constexpr int NPIECE = 10;
+  // Scores of the tile in buffer tb (both row blocks).
+  auto scores = [&](const uint16_t* tb, f32x4 (&sc)[2]) {
+    sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t ab = lds_addr(tb + offA), bb = lds_addr(tb + offB);
+    constexpr int W0 = 6;
+    u32x4 kf[NKB];
+    static_for<W0 < NKB ? W0 : NKB>([&](auto KI) { read_k(KI, ab, bb, kf[decltype(KI)::value]); });
+    static_for<NKB>([&](auto KI) {
+      constexpr int kb = decltype(KI)::value;
+      if constexpr (kb + W0 < NKB) read_k(std::integral_constant<int, kb + W0>{}, ab, bb, kf[kb + W0]);
+      constexpr int ahead = NKB - 1 - kb < W0 ? NKB - 1 - kb : W0;
+      lds_wait<ahead>(kf[kb]);
+      const bf16x8 kfb = __builtin_bit_cast(bf16x8, kf[kb]);
+      sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfb, qf[0][kb], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfb, qf[1][kb], sc[1], 0, 0, 0);
+    });
+  };
+
+  // The query rows into buffers 2 and 3 (free until tile 2, issued after
+  // the reference exchange, once every wave has read its query fragments)
+  // and tiles 0 and 1, then the wait: direct-to-LDS copies complete in no
+  // fixed order with respect to each other, so only a full count proves
+  // that a tile has landed; each wave waits for all of its copies and the
+  // barrier covers every wave's.
+  issue_q();
+#pragma unroll 1
+  for (int i = 0; i < min(2, ntiles); ++i) issue(i);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  {
+    const uint16_t* qb = k_lds + (2 + (wave >> 1)) * G::BUF;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int rr = 16 * rb + (lane & 15);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        qf[rb][kb] = 4 * kb < CA ? *(const bf16x8*)(qb + rr * G::ROW_A + 32 * kb + 8 * grp)
+                                 : *(const bf16x8*)(qb + G::SIZE_A + rr * CB * 8 +
+                                                    8 * ((4 * (kb - CA / 4) + grp) ^ bswz<CB>(rr)));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
+
+  // Softmax reference: the first tile's row maximum (pass 0).  The tile loop
+  // never rescales the accumulators; if a later score exceeds the reference
+  // by more than REDO_SLACK, the workgroup redoes the slot once with the
+  // exact row maximum (pass 1).
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l_run[rb] = 0.f;
+      if (pass == 1) m_run[rb] = m_all[rb];
+    }
+    // Pass 1 fetches tiles 0 and 1 again (pass 0 did so with the query rows,
+    // before this loop) and streams tile 2 in during the prologue.
+    if (pass == 1) {
+#pragma unroll 1
+      for (int i = 0; i < min(2, ntiles); ++i) issue(i);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    {  // S and P of tile 0 (pass 0: the reference is its row maximum over both halves)
+      f32x4 sc[2];
+      scores(k_lds, sc);
+      sm_piece(std::integral_constant<int, 0>{}, sc, k_begin);
+      if (pass == 0) {
+        float tm[2];  // row maxima of this wave's keys of tile 0
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          tm[rb] = fmaxf(m_all[rb], __shfl_xor(m_all[rb], 16, 64));
+          tm[rb] = fmaxf(tm[rb], __shfl_xor(tm[rb], 32, 64));
+          if (grp == 0) xm[wave][rb][lane] = tm[rb];
+        }
+        __syncthreads();
+        // both members take the same reference (max is commutative)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) m_run[rb] = fmaxf(tm[rb], xm[wave ^ 1][rb][lane & 15]);
+      }
+      // tile 2 into buffer 2: in pass 0 every wave has read its query
+      // fragments (the exchange's barrier above), in pass 1 the prologue's
+      // barrier ended the previous pass
+      if (2 < ntiles) issue(2);
+      static_for<NPIECE - 1>([&](auto PI) { sm_piece(std::integral_constant<int, decltype(PI)::value + 1>{}, sc, k_begin); });
+      *(u32x4*)&xp[0][wave][lane] = pown;
+    }
+    if (1 < ntiles) scores(k_lds + G::BUF, scn);
+
+    // Step t: barrier (P(t) of both members written, tile t + 2 landed,
+    // every wave done with step t - 1, whose value tile t - 1 the refill of
+    // tile t + 3 overwrites), then P(t) V(t), S(t + 2) and P(t + 1).
+    auto step = [&](auto K2, auto K1, int t) {
+      constexpr bool KEYS = decltype(K2)::value;  // tile t + 2 exists
+      constexpr bool NEXT = decltype(K1)::value;  // tile t + 1 exists
+      using IT = StepItems<ND, NKB, KEYS>;
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if constexpr (KEYS)  // (a step without tile t + 2 has no tile t + 3 either)
+        if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
+      const uint32_t vaddr = lds_addr(k_lds + (t % NBUF) * G::BUF + offV);
+      const uint16_t* t2 = k_lds + ((t + 2) % NBUF) * G::BUF;
+      const uint32_t ab = lds_addr(t2 + offA), bb = lds_addr(t2 + offB);
+      const int kt1 = k_begin + (t + 1) * KT;
+      u32x4 par;
+      lds_read_b128<0>(xp_par + (t & 1) * XP_PARITY, par);
+
+      constexpr int W = 6;
+      u32x2 vlo[ND], vhi[ND];
+      u32x4 kf[KEYS ? NKB : 1];
+      f32x4 sn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      auto issue_item = [&](auto II) {
+        constexpr int i = decltype(II)::value;
+        constexpr int j = IT::idx(i);
+        if constexpr (IT::is_v(i))
+          tr_read_pair<32 * j, 32 * j + 2 * 16 * G::ROW_A>(vaddr, vlo[j], vhi[j]);
+        else
+          read_k(std::integral_constant<int, j>{}, ab, bb, kf[j]);
+      };
+      static_for<W < IT::N ? W : IT::N>(issue_item);
+      bf16x8 pf[2];
+      static_for<IT::N>([&](auto II) {
+        constexpr int i = decltype(II)::value;
+        constexpr int j = IT::idx(i);
+        if constexpr (i + W < IT::N) issue_item(std::integral_constant<int, i + W>{});
+        constexpr int after = IT::template after<W>(i);
+        if constexpr (IT::is_v(i)) {
+          if constexpr (j == 0) {
+            lds_wait_pair_x<after>(vlo[0], vhi[0], par);
+            // k slots 0..3: keys of tile half 0, 4..7: half 1
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              const u32x4 lo_first = {pown[2 * rb], pown[2 * rb + 1], par[2 * rb], par[2 * rb + 1]};
+              const u32x4 hi_first = {par[2 * rb], par[2 * rb + 1], pown[2 * rb], pown[2 * rb + 1]};
+              pf[rb] = __builtin_bit_cast(bf16x8, mem ? hi_first : lo_first);
+            }
+          } else {
+            lds_wait_pair<after>(vlo[j], vhi[j]);
+          }
+          const bf16x8 v8 = __builtin_bit_cast(bf16x8, u32x4{vlo[j][0], vlo[j][1], vhi[j][0], vhi[j][1]});
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pf[0], acc[0][j], 0, 0, 0);
+          acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pf[1], acc[1][j], 0, 0, 0);
+        } else {
+          lds_wait<after>(kf[j]);
+          const bf16x8 kfb = __builtin_bit_cast(bf16x8, kf[j]);
+          sn[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfb, qf[0][j], sn[0], 0, 0, 0);
+          sn[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfb, qf[1][j], sn[1], 0, 0, 0);
+        }
+        // probabilities of tile t + 1 between the matrix instructions (after
+        // item 0, whose operands already hold this step's P(t))
+        if constexpr (NEXT && i < NPIECE) sm_piece(std::integral_constant<int, i>{}, scn, kt1);
+      });
+      if constexpr (NEXT) {
+        static_for<(IT::N < NPIECE ? NPIECE - IT::N : 0)>(
+            [&](auto PI) { sm_piece(std::integral_constant<int, IT::N + decltype(PI)::value>{}, scn, kt1); });
+        *(u32x4*)&xp[(t + 1) & 1][wave][lane] = pown;
+      }
+      if constexpr (KEYS) {
+        scn[0] = sn[0];
+        scn[1] = sn[1];
+      }
+    };
+    int t = 0;
+#pragma unroll 1
+    for (; t + 2 < ntiles; ++t) step(std::true_type{}, std::true_type{}, t);
+    if (t + 1 < ntiles) step(std::false_type{}, std::true_type{}, t++);
+    step(std::false_type{}, std::false_type{}, t);
+
+    // combine the four lanes of each row (fixed butterfly: same bits in all)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      m_all[rb] = fmaxf(m_all[rb], __shfl_xor(m_all[rb], 16, 64));
+      m_all[rb] = fmaxf(m_all[rb], __shfl_xor(m_all[rb], 32, 64));
+      l_run[rb] += __shfl_xor(l_run[rb], 16, 64);
+      l_run[rb] += __shfl_xor(l_run[rb], 32, 64);
+      if (grp == 0) xl[wave][rb][lane] = l_run[rb];
+    }
+    // one barrier: every wave is done with the tile buffers, the row sums of
+    // both halves and the redo votes are visible
+    const float lim = REDO_SLACK * 1.4426950408889634f;
+    const bool vote = pass == 0 && __any(m_all[0] > m_run[0] + lim || m_all[1] > m_run[1] + lim);
+    if (lane == 0) xv[wave] = vote;
+    __syncthreads();
+    if (pass == 1 || !(xv[0] | xv[1] | xv[2] | xv[3])) break;
+    // the exact row maximum over both halves is the redo's reference
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      if (grp == 0) xm[wave][rb][lane] = m_all[rb];
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) m_all[rb] = fmaxf(m_all[rb], xm[wave ^ 1][rb][lane & 15]);
+  }
+
+  // ---- partials: O^T[dim][row] / l, a convex combination of value rows,
+  //      stored as fp16 (11-bit significand, finer than the bf16 operands);
+  //      layout [row][slot][dim] so the merge of one row reads contiguous
+  //      memory; l >= 1 (the reference key contributes exp(0)).  The pair's
+  //      row sums add both key halves; the 64 rows are staged in LDS (the
+  //      barrier above ended every wave's tile reads) and stored as whole
+  //      rows. ----
+  float inv_l[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    l_run[rb] += xl[wave ^ 1][rb][lane & 15];  // the same sum in both members
+    inv_l[rb] = 1.f / l_run[rb];
+  }
+  constexpr int RB = R * 2 + 16;  // bytes per staged row (the pad spreads the banks)
+  unsigned char* stage = (unsigned char*)k_lds;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      u32x2 h;
+      h[0] = pack_f16x2(acc[rb][d][0] * inv_l[rb], acc[rb][d][1] * inv_l[rb]);
+      h[1] = pack_f16x2(acc[rb][d][2] * inv_l[rb], acc[rb][d][3] * inv_l[rb]);
+      const int lrow = (wave >> 1) * 32 + 16 * rb + (lane & 15);
+      *(u32x2*)(stage + lrow * RB + (16 * ND * mem + 16 * d + 4 * grp) * 2) = h;
+    }
+  __syncthreads();
   constexpr int LPR = R / 8;     // lanes per row, 16 bytes each
   constexpr int RPI = 64 / LPR;  // rows per store
   static_assert(64 % LPR == 0 && 16 % RPI == 0, "row staging");
 #pragma unroll
   for (int it = 0; it < 16 / RPI; ++it) {
-    const int rr = it * RPI + lane / LPR, cb = (lane % LPR) * 16;
+    const int rr = wave * 16 + it * RPI + lane / LPR, cb = (lane % LPR) * 16;
     const u32x4 v = *(const u32x4*)(stage + rr * RB + cb);
-    *(u32x4*)((unsigned char*)(a.o_part + ((long long)(row0 + rr) * a.slots + slot) * a.r) + cb) = v;
+    *(u32x4*)((unsigned char*)(a.o_part + ((long long)(rgrp * 64 + rr) * a.slots + slot) * a.r) + cb) = v;
   }
-  if (grp == 0) {
-    a.ml_part[prow * 2] = m_run * 0.6931471805599453f;  // back to natural-log units
-    a.ml_part[prow * 2 + 1] = l_run;
+  if (mem == 0 && grp == 0) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const long long prow = (long long)(prow0 + 16 * rb + lane) * a.slots + slot;
+      a.ml_part[prow * 2] = m_run[rb] * 0.6931471805599453f;  // back to natural-log units
+      a.ml_part[prow * 2 + 1] = l_run[rb];
+    }
   }
 }
 

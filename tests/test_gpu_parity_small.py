@@ -101,6 +101,24 @@ def test_mla_head_geometry(fmt, lens):
     full_parity(g, ref, tol=2e-2, max_ties=2)
 
 
+MLA_WIDE = C.small_model(n_heads=16, q_lora=256, kv_lora=512, qk_nope=128, qk_rope=64, v_head=128)
+
+
+@pytest.mark.parametrize("lens", [(300,), (0, 37, 600)])
+def test_mla_head_geometry_sharp(lens):
+    """The full model's latent and head sizes with 16 heads (112 query rows:
+    two groups of 64 per attention workgroup grid) and W_UK scaled x10, so
+    the scores span several units: probabilities formed against different
+    reference maxima would show."""
+    from tests.gpu_common import full_parity
+    wl = C.Workload("mla_wide_sharp", MLA_WIDE, C.ALL_BF16, seed=783, kv_lens=lens, fixture_gains=True,
+                    sharp_attention=True)
+    print("case", lens, flush=True)
+    g = _gw(wl)
+    ref = O.draft_block(wl, g.stored, g.inputs)
+    full_parity(g, ref, tol=2e-2, max_ties=2)
+
+
 def test_small_sharp_attention_bf16():
     from tests.gpu_common import full_parity
     wl = C.Workload("small_sharp", SMALL, C.ALL_BF16, seed=778, kv_lens=(129,), fixture_gains=True,
