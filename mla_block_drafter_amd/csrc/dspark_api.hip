@@ -484,6 +484,7 @@ GemvArgs gemv_base(const Mat& mt, const GemvPlan& p, const Frag& f, int M) {
   a.M = M;
   a.hilo = p.hilo;
   a.ksteps_per_split = p.ksteps_per_split;
+  a.ksteps_lo = p.ksteps_lo;
   a.out_ld = (long long)mt.pm.ngroups * mt.pm.G;
   a.out_split_stride = (long long)M * a.out_ld;
   return a;

@@ -452,8 +452,12 @@ __global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
   auto tj = [&](int j) { return j + (j >= TPW / 2 ? jump : 0); };
   const int span = TPW + jump;
   const int KB = a.w.KB;
-  const int kb0 = (NW ? wave : (int)blockIdx.y) * a.ksteps_per_split;
-  const int kb1 = min(KB, kb0 + a.ksteps_per_split);
+  // k range: split-K slice of the workgroup, or the wave's share (waves
+  // 4..7 of eight take ksteps_lo, see plan_own)
+  const int hi = a.ksteps_per_split, lo = NW == 8 ? a.ksteps_lo : hi;
+  const int kb0 = min(KB, NW == 8 ? (wave < 4 ? wave * hi : 4 * hi + (wave - 4) * lo)
+                                  : (NW ? wave : (int)blockIdx.y) * hi);
+  const int kb1 = min(KB, kb0 + (NW == 8 && wave >= 4 ? lo : hi));
   OwnPre pre{};
   if constexpr (NW > 0) {
     if (wave == 0 && active) own_prefetch<TPW>(a, t0, lane, pre);

@@ -1,6 +1,7 @@
 // Work planning and format dispatch of the skinny GEMM (kernels in gemv_impl.h,
 // instantiated per weight format in k_gemv_<fmt>.hip).
 #include <algorithm>
+#include <cmath>
 
 #include "kernels.h"
 
@@ -76,6 +77,10 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   return p;
 }
 
+// Share of the reduction taken by waves 0..3 of an eight-wave column-owning
+// workgroup.
+constexpr double OWN_SPLIT_HI = 0.5625;
+
 // Column-owning plan: a workgroup per OWN_COLS output columns, its waves
 // splitting the reduction.  About 2000 waves in all (eight per workgroup for
 // the 224-workgroup hidden-size outputs, four for the 448 of the fused
@@ -92,7 +97,16 @@ GemvPlan plan_own(const PackedMat& w, int M, bool swiglu, bool i8_in) {
   const int units = (w.KB + unit - 1) / unit;
   int nw = nwg >= 384 ? 4 : 8;
   if (units < nw) nw = 4;
-  int per = (units + nw - 1) / nw * unit;
+  int per = (units + nw - 1) / nw * unit, lo = per;
+  if (nw == 8) {
+    // Waves 4..7 share their SIMDs with waves 0..3 and lose the issue
+    // arbitration to the older waves (about a fifth slower on the same
+    // k range, measured), so waves 0..3 take the larger share.
+    const int hi_u = std::min(units, (int)std::ceil(units * OWN_SPLIT_HI / 4.0));
+    const int lo_u = std::max(0, (units - 4 * hi_u + 3) / 4);
+    per = hi_u * unit;
+    lo = lo_u * unit;
+  }
   p.hilo = 1;
   p.MT = 1;
   p.TPW = swiglu ? 4 : 2;
@@ -100,6 +114,7 @@ GemvPlan plan_own(const PackedMat& w, int M, bool swiglu, bool i8_in) {
   p.grid_x = nwg;
   p.S = 1;
   p.ksteps_per_split = per;
+  p.ksteps_lo = lo;
   p.amode = w.fmt == DT_Q8_0 ? 3 : 0;
   return p;
 }

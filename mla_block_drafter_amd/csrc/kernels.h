@@ -64,6 +64,7 @@ struct GemvArgs {
   int M;                  // valid activation rows
   int hilo;               // bf16 family with M <= 8
   int ksteps_per_split;   // in 32-wide blocks (bf16 family) or 16-wide groups (f32)
+  int ksteps_lo;          // GEMV_OWN with 8 waves: k steps of waves 4..7 (waves 0..3 take ksteps_per_split)
   RowScale rs;            // optional output row scale (STORE, FRAG)
   // STORE
   float* out;             // [S][M][out_ld]
@@ -94,6 +95,7 @@ struct GemvArgs {
 
 struct GemvPlan {
   int MT, TPW, S, ksteps_per_split, hilo;
+  int ksteps_lo;          // GEMV_OWN with 8 waves: k steps of waves 4..7
   int nw;                 // GEMV_OWN: waves per workgroup splitting the reduction; 0: split-K over workgroups
   int grid_x;
   int amode;              // activation operand: 0 prepared global fragments,
