@@ -378,7 +378,8 @@ __device__ __forceinline__ void own_epilogue(const GemvArgs& a, const f32x4 (&ac
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2, A_GLOBAL_I8 = 3, A_LDS_I8 = 4 };
+enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2, A_GLOBAL_I8 = 3, A_LDS_I8 = 4, A_LDS_BF = 5 };
+constexpr int LDS_BF_CK = 4;  // A_LDS_BF: k blocks per staged chunk
 
 // Wait until at most N vector memory operations of this wave are outstanding:
 // the compiler's own builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
@@ -431,6 +432,14 @@ __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, 
 //             v_mfma_i32_16x16x32_i8 directly: no weight decode, exact
 //             integer products, one convert and one fp32 fma per output per
 //             block (factor d_w); s is applied once at the end.
+//  A_LDS_BF:  FP8 or BF16 weights with several m-tiles (M > 8): the workgroup's
+//             four waves share one k range, so the bf16 activation fragments
+//             of a chunk of LDS_BF_CK k blocks (all m-tiles) are loaded once
+//             per workgroup, a quarter per wave, one chunk ahead into
+//             registers, then written to LDS (two buffers) and read from there
+//             by every wave.  Ordinary loads return in order, so the chunk's
+//             wait leaves the weight prefetch in flight (direct-to-LDS copies
+//             would need a full wait).
 // Weight loads are issued in stages of U k steps x TPW tiles before any of
 // them is consumed.
 //
@@ -666,6 +675,109 @@ __global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
       compute_stage(sb, q + U);
     } else if (nst > 0) {
       compute_stage(sa, q);
+    }
+    staged = true;
+  } else if constexpr (AMODE == A_LDS_BF) {
+    static_assert((FMT == DT_FP8 || FMT == DT_BF16) && MT > 1 && NW == 0 && MODE != GEMV_MARKOV,
+                  "A_LDS_BF: FP8 or BF16 weights, several m-tiles, split-K");
+    constexpr int WL = FMT == DT_FP8 ? 1 : 2;  // 16-byte weight loads per tile and pair of k blocks
+    constexpr int CK = LDS_BF_CK;          // k blocks per chunk
+    constexpr int D = CK / 2;              // pairs of k blocks per chunk = weight pairs in flight
+    constexpr int NA = (MT * CK + 3) / 4;  // activation fragments per wave per chunk
+    const int KP = KB >> 1, P0 = kb0 >> 1, P1 = kb1 >> 1;
+    const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)(active ? t0 : 0) * KP * WL * 1024,
+                                               active ? (uint32_t)(span * KP * WL * 1024) : 0u);
+    const __amdgpu_buffer_rsrc_t ar = buf_rsrc((const bf16x8*)a.act + (long long)g * (a.act_gstride / 8),
+                                               (uint32_t)(MT * KB * 1024));
+    u32x4* lds_a = (u32x4*)gemv_smem;  // [2][MT][CK][64]
+    const uint32_t l16 = lane * 16;
+    u32x4 areg[NA];
+    auto load_chunk = [&](int c) {
+#pragma unroll
+      for (int n = 0; n < NA; ++n) {
+        const int i = wave + 4 * n, mt = i / CK, kk = i % CK, kb = kb0 + c * CK + kk;
+        const bool ok = i < MT * CK && kb < kb1;
+        areg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            ar, ok ? (uint32_t)((mt * KB + kb) * 1024) + l16 : BUF_OOB, 0, 0));
+      }
+    };
+    auto store_chunk = [&](int buf) {
+#pragma unroll
+      for (int n = 0; n < NA; ++n) {
+        const int i = wave + 4 * n;
+        if (i < MT * CK) lds_a[((buf * MT + i / CK) * CK + i % CK) * 64 + lane] = areg[n];
+      }
+    };
+    // LDS stores complete, then the barrier (no wait on the weight loads in
+    // flight, which a __syncthreads would add)
+    auto lds_barrier = [&]() {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // weights: a ring of R = 2 D pairs (two chunks), slot r holding pair
+    // P0 + 2 D c2 + r during chunks 2 c2, 2 c2 + 1, refilled with the same
+    // slot's pair of the next two chunks as soon as it is consumed (R pairs
+    // of matrix work hide each load)
+    constexpr int R = 2 * D;
+    u32x4 wring[R][TPW][WL];
+    auto load_w = [&](u32x4 (&w)[TPW][WL], int p) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int h = 0; h < WL; ++h)  // FP8: one 1 KiB chunk per pair; BF16: one per k block
+          w[j][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+              wr, p < P1 ? (uint32_t)(((tj(j) * KP + p) * WL + h) * 1024) + l16 : BUF_OOB, 0, BUF_NT));
+    };
+    const int nch = (kb1 - kb0 + CK - 1) / CK;
+    if (nch > 0) {
+      load_chunk(0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) load_w(wring[r], P0 + r);
+      store_chunk(0);
+    }
+    lds_barrier();
+    for (int c2 = 0; 2 * c2 < nch; ++c2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // chunk c = 2 c2 + h in buffer h
+        const int c = 2 * c2 + h;
+        if (c >= nch) break;
+        if (c + 1 < nch) load_chunk(c + 1);
+#pragma unroll
+        for (int pp = 0; pp < D; ++pp) {
+          const int r = h * D + pp;
+          bf16x8 B0[TPW], B1[TPW];
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            if constexpr (FMT == DT_FP8) {
+              B0[j] = fp8x8_to_bf16x8(wring[r][j][0][0], wring[r][j][0][1]);
+              B1[j] = fp8x8_to_bf16x8(wring[r][j][0][2], wring[r][j][0][3]);
+            } else {
+              B0[j] = __builtin_bit_cast(bf16x8, wring[r][j][0]);
+              B1[j] = __builtin_bit_cast(bf16x8, wring[r][j][WL - 1]);
+            }
+          }
+          load_w(wring[r], P0 + R * (c2 + 1) + r);  // out of range: zeros, no memory access
+          __builtin_amdgcn_sched_barrier(0);  // issue the refill here, a whole ring ahead of its use
+          // pairs past the k range: zero weights times zero fragments
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const bf16x8 A0 = __builtin_bit_cast(bf16x8, lds_a[((h * MT + mt) * CK + 2 * pp) * 64 + lane]);
+            const bf16x8 A1 = __builtin_bit_cast(bf16x8, lds_a[((h * MT + mt) * CK + 2 * pp + 1) * 64 + lane]);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+              acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0[j], acc[mt][j], 0, 0, 0);
+              acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B1[j], acc[mt][j], 0, 0, 0);
+            }
+          }
+        }
+        if (c + 1 < nch) {
+          // every wave finished chunk c - 1 (the last barrier), whose buffer
+          // takes chunk c + 1
+          store_chunk(h ^ 1);
+          lds_barrier();
+        }
+      }
     }
     staged = true;
   } else if (active) {
@@ -1115,6 +1227,7 @@ inline size_t gemv_lds_bytes(const GemvPlan& p) {
   if (p.amode == A_ROWS_BF) return (size_t)p.MT * p.ksteps_per_split * 64 * 16;
   if (p.amode == A_ROWS_I8) return (size_t)p.ksteps_per_split * 512 + 256;
   if (p.amode == A_GLOBAL_I8) return (size_t)p.ksteps_per_split * 520;  // the A_LDS_I8 copy
+  if (p.amode == A_LDS_BF) return (size_t)2 * p.MT * LDS_BF_CK * 1024;
   return 0;
 }
 
@@ -1137,6 +1250,11 @@ hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
       hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_LDS_I8>), grid, block, lds, st, a);
     else
       hipLaunchKernelGGL((k_gemv_bf<FMT, 1, TPW, MODE, A_GLOBAL_I8>), grid, block, 0, st, a);
+  } else if (p.amode == A_LDS_BF) {
+    if constexpr ((FMT == DT_FP8 || FMT == DT_BF16) && MT > 1 && MODE != GEMV_MARKOV)
+      hipLaunchKernelGGL((k_gemv_bf<FMT, MT, TPW, MODE, A_LDS_BF>), grid, block, lds, st, a);
+    else
+      return hipErrorInvalidValue;
   } else if (p.amode == A_GLOBAL) {
     hipLaunchKernelGGL((k_gemv_bf<FMT, MT, TPW, MODE, A_GLOBAL>), grid, block, 0, st, a);
   } else {
@@ -1151,6 +1269,17 @@ hipError_t dispatch_out(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
     if (p.TPW == 4) return go<FMT, 1, 4, MODE>(a, p, st);
     if (p.TPW == 2) return go<FMT, 1, 2, MODE>(a, p, st);
     return go<FMT, 1, 1, MODE>(a, p, st);
+  }
+  if ((FMT == DT_FP8 || FMT == DT_BF16) && p.TPW == 2) {
+    switch (p.MT) {
+      case 2: return go<FMT, 2, 2, MODE>(a, p, st);
+      case 3: return go<FMT, 3, 2, MODE>(a, p, st);
+      case 4: return go<FMT, 4, 2, MODE>(a, p, st);
+      case 5: return go<FMT, 5, 2, MODE>(a, p, st);
+      case 6: return go<FMT, 6, 2, MODE>(a, p, st);
+      case 7: return go<FMT, 7, 2, MODE>(a, p, st);
+    }
+    return hipErrorInvalidValue;
   }
   if (p.TPW == 4) {
     switch (p.MT) {

@@ -39,8 +39,11 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
     // load (with one, the fragments of all m-tiles were re-read from L2 for
     // every 16 weight rows).  Not for eight m-tiles (their accumulators alone
     // take 128 registers) nor for the per-head W_UK / W_UV groups (measured
-    // slower there).
-    if (!gather && p.MT <= 7 && w.ngroups == 1 && w.TG % 4 == 0 && T / 4 >= 64) p.TPW = 4;
+    // slower there).  FP8 and BF16 weights read the fragments from LDS (A_LDS_BF),
+    // where two tiles per wave measured faster: half the registers, so two
+    // waves per SIMD hide each other's waits.
+    if (!gather && p.MT <= 7 && w.ngroups == 1 && w.TG % 4 == 0 && T / 4 >= 64)
+      p.TPW = (w.fmt == DT_FP8 || w.fmt == DT_BF16) ? 2 : 4;
   } else if (p.MT == 1) {
     if (w.TG % 4 == 0 && ((gather && T / 4 >= 256) || (allow_split && T / 4 >= 448))) p.TPW = 4;
     else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 128 : 256)) p.TPW = 2;
@@ -48,7 +51,10 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   const int waves = T / p.TPW;
   p.grid_x = (waves + 3) / 4;
   const int ksteps = f32 ? (w.Kp >> 4) : w.KB;
-  const int unit = w.fmt == DT_MXFP4 ? 4 : (w.fmt == DT_Q8_0 || w.fmt == DT_FP8) ? 2 : 1;
+  // activation fragments of several m-tiles shared through LDS (A_LDS_BF),
+  // whose k loop steps over pairs of k blocks
+  const bool lds_bf = (w.fmt == DT_FP8 || w.fmt == DT_BF16) && p.MT > 1 && !gather && w.ngroups == 1;
+  const int unit = w.fmt == DT_MXFP4 ? 4 : (w.fmt == DT_Q8_0 || w.fmt == DT_FP8 || lds_bf) ? 2 : 1;
   int S = 1;
   if (allow_split)
     S = std::max(1, std::min(kMaxWaves / std::max(waves, 1), ksteps / 8));
@@ -64,7 +70,9 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
   // GEMM): bf16 hi/lo fragments for BF16 / FP8 weights, int8 hi/lo codes for
   // Q8_0 when the producer supports them; otherwise Q8_0 stages fp32 rows.
   p.amode = 0;
-  if (i8 && i8_in && !gather) {
+  if (lds_bf) {
+    p.amode = 5;  // A_LDS_BF: the workgroup's activation chunks shared through LDS
+  } else if (i8 && i8_in && !gather) {
     p.amode = 3;
   } else if (w.fmt == DT_Q8_0 && !gather && one_group) {
     if (allow_split) {

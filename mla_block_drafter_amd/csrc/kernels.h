@@ -102,6 +102,7 @@ struct GemvPlan {
                           // 1 fp32 rows -> bf16 fragments in LDS,
                           // 2 fp32 rows -> int8 hi/lo codes in LDS (Q8_0, M <= 8)
                           // 3 int8 hi/lo fragments from the producer (Q8_0, M <= 8)
+                          // 5 bf16 fragments of several m-tiles shared through LDS (FP8 / BF16, M > 8)
 };
 
 // i8_in: the producer of the input can write int8 fragments (frag_put_wave /
