@@ -437,18 +437,31 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   P.zero_end = off;
   P.part = take(part);
   P.bkeys = take((long long)M * (c.kv_lora + c.qk_rope) * (kv_f32 ? 4 : 2));
-  // Keys per attention slot: 256, doubled (up to 2048) while the slot
-  // partials, written and read back once, would outweigh the cache bytes the
-  // slots cover, as long as the attention grid keeps at least two workgroups
-  // per CU (256 CUs).  Long contexts get large slots; short ones keep the
-  // parallelism.
+  // Keys per attention slot: the multiple of 32 in [256, 2048] with the
+  // smallest estimated attention time.  One workgroup runs per CU (256 on
+  // MI355X), so the grid of (rows / 64) x slots workgroups runs in whole
+  // rounds; a workgroup costs about seven key tiles' time in fixed work (query
+  // and first-tile loads, partial stores) plus one per key tile, and its slot
+  // partials are written and read back once more (at ~6 TB/s).  At context
+  // 98,304 this picks 1376 keys (2 rounds of 72 slots) over 1024 (3 rounds);
+  // short contexts keep 256.  The slot count uses the bound cdiv(keys, C) +
+  // n_seq, which holds for any split of the context between sequences.
   {
+    constexpr int kCUs = 256;
     const long long keys = total_ctx + (long long)n_seq * c.block;
-    const long long part_slot = 2LL * P.rows_pad * ((long long)c.kv_lora * 2 + 8);
-    const long long kv_row = (long long)(c.kv_lora + c.qk_rope) * (kv_f32 ? 4 : 2);
-    auto nslots = [&](long long cc) { return cdiv(keys, cc) + n_seq; };
-    P.C = 256;
-    while (P.C < 2048 && part_slot > P.C * kv_row && (P.rows_pad / 64) * nslots(2LL * P.C) >= 512) P.C *= 2;
+    const long long part_row = (long long)c.kv_lora * 2 + 8;
+    const double step_s = 1.05e-6;  // one key tile of a workgroup, measured
+    double best = 0.0;
+    for (int cc = 256; cc <= 2048; cc += 32) {
+      const long long slots = cdiv(keys, cc) + n_seq;
+      const long long rounds = cdiv((long long)(P.rows_pad / 64) * slots, kCUs);
+      const double cost = (double)rounds * (7 + cc / 32) +
+                          2.0 * (double)slots * P.rows_pad * part_row / 6e12 / step_s;
+      if (cc == 256 || cost < best) {
+        best = cost;
+        P.C = cc;
+      }
+    }
   }
   P.slots = (int)(cdiv(total_ctx + (long long)n_seq * c.block, P.C) + n_seq);
   if (!kv_f32) {
