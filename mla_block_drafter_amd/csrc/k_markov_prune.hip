@@ -192,6 +192,7 @@ __global__ __launch_bounds__(256) void k_markov_prune(MarkovPruneArgs a) {
   __shared__ int lst[MB][CG];
   __shared__ float zc[MB][CG];
   __shared__ unsigned Lord[MB];  // order-preserving bits of the position's threshold
+  __shared__ unsigned ovf[MB];   // bit c: chunk c of the position had more candidates than slots
   __shared__ int nl[MB];
   __shared__ float rsp[MB], hdp[MB];
   __shared__ float cw[256];  // w_m
@@ -203,6 +204,7 @@ __global__ __launch_bounds__(256) void k_markov_prune(MarkovPruneArgs a) {
   if (threadIdx.x < MB) {
     nl[threadIdx.x] = 0;
     Lord[threadIdx.x] = 0u;
+    ovf[threadIdx.x] = 0u;
   }
   __syncthreads();
   // round 1: every global read before the rows, issued together
@@ -255,7 +257,10 @@ __global__ __launch_bounds__(256) void k_markov_prune(MarkovPruneArgs a) {
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
     const int it = e * 256 + threadIdx.x, i = it / (NCH * CC), k = it % CC;
-    if (cnt[e] > CC) bad = 1;
+    if (cnt[e] > CC) {  // the slots hold only part of the chunk: rescanned below
+      if (k == 0) atomicOr(&ovf[i], 1u << ((it / CC) % NCH));
+      continue;
+    }
     if (k >= cnt[e]) continue;  // (also every item outside the positions and chunks: cnt 0)
     const float zv = __uint_as_float(ent[e][1]), nb = __uint_as_float(ent[e][2]);
     if (zv + nb + prune_slack(zv, nb) >= ord2f(Lord[i])) {
@@ -265,6 +270,35 @@ __global__ __launch_bounds__(256) void k_markov_prune(MarkovPruneArgs a) {
         zc[i][j] = zv;
       } else {
         bad = 1;
+      }
+    }
+  }
+  __syncthreads();
+  // Chunks with more candidates than slots: every row of the chunk against
+  // the position's final threshold, its bound formed as k_markov_cand forms
+  // it (the same candidates the slots would have held).
+  {
+    const float B1 = __uint_as_float(*a.w1max);
+    for (int i = 0; i < B; ++i) {
+      unsigned bits = ovf[i];  // uniform (after the barrier)
+      const float L = ord2f(Lord[i]);
+      const float* zr = a.z + ((long long)s * B + i) * a.vocab;
+      while (bits) {
+        const int c = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        const int v1 = min((c + 1) * MK_CHUNK, a.vocab);
+        for (int v = c * MK_CHUNK + (int)threadIdx.x; v < v1; v += 256) {
+          const float zv = zr[v], nb = a.n2[v] * B1;
+          if (zv + nb + prune_slack(zv, nb) >= L) {
+            const int j = atomicAdd(&nl[i], 1);
+            if (j < CG) {
+              lst[i][j] = v;
+              zc[i][j] = zv;
+            } else {
+              bad = 1;
+            }
+          }
+        }
       }
     }
   }

@@ -11,6 +11,10 @@ original card, "Model Overview": the sequential low-rank Markov head).
   takes the fallback: status 0 and the full rollout's bits.
 * Poisoned workspaces give the same bits.
 * The bench workload (full Q8_0, context 8192) takes the candidate path.
+* The batched FP8 workload (16 sequences) has a vocabulary chunk with more
+  rows above its own lower bound than the chunk's slots hold (14 > 8, while
+  at most 8 per position pass the position's threshold): the chunk is
+  rescanned and the candidate path still drafts the full rollout's tokens.
 """
 import numpy as np
 import pytest
@@ -111,4 +115,13 @@ def test_bench_workload_takes_the_candidate_path():
     full = _run(g, True)
     pr = _run(g, False)
     assert pr["status"] == 2
+    _check_same_draft(full, pr)
+
+
+def test_batched_workload_rescans_overflowing_chunks():
+    from tests.gpu_common import GpuWorkload
+    g = GpuWorkload(C.CFG5)
+    full = _run(g, True)
+    pr = _run(g, False)
+    assert pr["status"] == 2, "expected the candidate path"
     _check_same_draft(full, pr)
