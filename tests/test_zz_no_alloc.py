@@ -34,6 +34,17 @@ def _pass(g, total_ctx, offs, static):
     return [t.cpu().numpy() for t in (tokens, conf, logits, hidden)]
 
 
+def big_static_ctx(model) -> int:
+    """A one-sequence context whose workspace exceeds the static scratch
+    (asserted here, on the host, before any call uses it)."""
+    from mla_block_drafter_amd import dspark as D
+    ctx = 1 << 17
+    while model.workspace_bytes(1, ctx) <= D.STATIC_SCRATCH_BYTES and ctx < (1 << 29):
+        ctx *= 2
+    assert model.workspace_bytes(1, ctx) > D.STATIC_SCRATCH_BYTES
+    return ctx
+
+
 def _same(a, b):
     for x, y in zip(a, b):
         np.testing.assert_array_equal(np.ascontiguousarray(x).view(np.uint8), np.ascontiguousarray(y).view(np.uint8))
@@ -53,13 +64,17 @@ def test_static_scratch_matches_caller_workspace_full_q8_0():
     _same(got_long, ref_long)
     _same(got_short, ref_short)
     assert not np.array_equal(ref_long[2], ref_short[2])       # the two inputs really differ
-    # a call beyond the static scratch is refused, nothing enqueued
+    # a call beyond the static scratch is refused, nothing enqueued.  The KV
+    # buffers hold only the long call's rows, so the context is taken from the
+    # workspace query and checked on the host to exceed the scratch before the
+    # call: a context the library accepted would read past them.
+    big = big_static_ctx(g.model)
     m = g.wl.model
     tokens = torch.full((1, m.block), -7, dtype=torch.int32, device="cuda")
     conf = torch.zeros((1, m.block), dtype=torch.float32, device="cuda")
     with pytest.raises(D.DsparkError) as e:
-        g.model.draft_block(g.cap, g.kv, torch.tensor([0, 1 << 17], dtype=torch.int32, device="cuda"), g.prev,
-                            1 << 17, tokens, conf, None)
+        g.model.draft_block(g.cap, g.kv, torch.tensor([0, big], dtype=torch.int32, device="cuda"), g.prev,
+                            big, tokens, conf, None)
     assert e.value.code == D.EWORKSPACE and "static scratch" in str(e.value)
     torch.cuda.synchronize()
     assert (tokens.cpu().numpy() == -7).all()
