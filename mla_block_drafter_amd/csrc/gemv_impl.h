@@ -238,38 +238,39 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, f32x4 (&acc)[MT
 }
 
 // Inputs of the column-owning epilogue that do not depend on the product,
-// loaded by wave 0 before its weight stream starts (their latency then hides
-// under the stream instead of following it): per lane rows 4 (lane >> 4) + r,
-// columns 16 jo + (lane & 15) of the workgroup's 32 columns.
+// loaded by each epilogue wave before its weight stream starts (their latency
+// then hides under the stream instead of following it).  Epilogue wave r
+// (r < 4) finishes rows 4 (lane >> 4) + r, i.e. rows r and r + 4, of the
+// workgroup's 32 columns: lane l < 32 holds column 16 jo + (l & 15).
 struct OwnPre {
-  float x[4][2];     // RESID: residual stream
+  float x[2];        // RESID: residual stream, columns jo = 0, 1
   float g1[2], dw[2];  // gain of the next input, confidence weights
-  float ck[8];       // row-scale chunk sums, per lane (summed over the wave later)
+  float ck[2];       // row-scale chunk sums of rows r and r + 4, per lane (summed over the wave later)
   float fs[4];       // FP8 column scales of the TPW tiles
 };
 
 template <int TPW>
-__device__ __forceinline__ void own_prefetch(const GemvArgs& a, int t0, int lane, OwnPre& pre) {
+__device__ __forceinline__ void own_prefetch(const GemvArgs& a, int t0, int lane, int r, OwnPre& pre) {
   const int M = a.M, G = a.w.G;
   constexpr int TO = 2;
   const bool swiglu = TPW == 2 * TO;
   const int outG = swiglu ? G / 2 : G;
   const int c0 = blockIdx.x * (16 * TO);
+  const int m = (lane >> 4) * 4 + r;
 #pragma unroll
   for (int jo = 0; jo < TO; ++jo) {
     const int col = c0 + 16 * jo + (lane & 15);
     const bool cok = col < outG;
     pre.g1[jo] = a.g1 && cok ? a.g1[col] : 0.f;
     pre.dw[jo] = a.dotw && cok ? a.dotw[col] : 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = (lane >> 4) * 4 + r;
-      const bool ok = lane < 32 && m < M && cok;
-      pre.x[r][jo] = a.epi == OWN_RESID && ok ? a.x_in[(long long)m * outG + col] : 0.f;
-    }
+    const bool ok = lane < 32 && m < M && cok;
+    pre.x[jo] = a.epi == OWN_RESID && ok ? a.x_in[(long long)m * outG + col] : 0.f;
   }
 #pragma unroll
-  for (int m = 0; m < 8; ++m) pre.ck[m] = a.rs.ssq && m < M ? chunk_lane_sum(a.rs.ssq + (long long)m * SSQ_LD, a.rs.nch, lane) : 0.f;
+  for (int h = 0; h < 2; ++h) {
+    const int mr = r + 4 * h;
+    pre.ck[h] = a.rs.ssq && mr < M ? chunk_lane_sum(a.rs.ssq + (long long)mr * SSQ_LD, a.rs.nch, lane) : 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < TPW && j < 4; ++j)
     pre.fs[j] = a.w.fmt == DT_FP8 ? ((const float*)a.w.scales)[(long long)(t0 + j + (j >= TPW / 2 ? a.tile_jump : 0)) * 16 +
@@ -278,30 +279,31 @@ __device__ __forceinline__ void own_prefetch(const GemvArgs& a, int t0, int lane
 }
 
 // Epilogue of the column-owning GEMM (NW waves share TPW tiles, each wave
-// summed its own k range).  The waves' accumulators meet in LDS and wave 0
-// adds them in wave order (fixed: deterministic), folds the hi/lo rows, and
-// writes the fused outputs of the workgroup's 32 columns: lane l < 32 holds
-// rows 4 (l >> 4) + r, column 16 jo + (l & 15) of output tile jo (jo = 0, 1;
-// for SWIGLU tiles 0, 1 are the gate and 2, 3 the up columns).  Per-row sums
-// over the 32 columns (RMSNorm statistics, the int8 block maximum) are taken
-// over each 16-lane DPP row, every lane taking part.
+// summed its own k range).  The waves' accumulators meet in LDS; waves 0..3
+// each finish one accumulator row r = wave of the MFMA layout: they add the
+// NW partial sums in wave order (fixed: deterministic), fold the hi/lo rows,
+// and write the fused outputs of rows r and r + 4 of the workgroup's 32
+// columns (for SWIGLU tiles 0, 1 are the gate and 2, 3 the up columns).
+// Per-row sums over the 32 columns (RMSNorm statistics, the int8 block
+// maximum) are taken over each 16-lane DPP row, every lane taking part.
 template <int TPW, int NW>
 __device__ __forceinline__ void own_epilogue(const GemvArgs& a, const f32x4 (&acc)[TPW], int t0, int lane, int wave,
                                              const OwnPre& pre) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gemv_smem[];
   f32x4* red = (f32x4*)gemv_smem;  // [NW][TPW][64]
+  const float* redf = (const float*)gemv_smem;
 #pragma unroll
   for (int j = 0; j < TPW; ++j) red[(wave * TPW + j) * 64 + lane] = acc[j];
   __syncthreads();
-  if (wave != 0) return;
-  f32x4 v[TPW];
+  if (wave >= 4) return;
+  const int r = wave;
+  float v[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
-    v[j] = red[j * 64 + lane];
+    v[j] = redf[(j * 64 + lane) * 4 + r];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v[j] += red[(w * TPW + j) * 64 + lane];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[j][r] += __shfl_xor(v[j][r], 32, 64);
+    for (int w = 1; w < NW; ++w) v[j] += redf[((w * TPW + j) * 64 + lane) * 4 + r];
+    v[j] += __shfl_xor(v[j], 32, 64);
   }
   const int M = a.M, G = a.w.G;
   constexpr int TO = 2;  // output tiles: 32 columns
@@ -309,69 +311,60 @@ __device__ __forceinline__ void own_epilogue(const GemvArgs& a, const f32x4 (&ac
   const bool swiglu = TPW == 2 * TO;
   const int outG = swiglu ? G / 2 : G;      // output columns of the matrix
   const int c0 = blockIdx.x * (16 * TO);    // first output column of the workgroup
-  // row scales from the prefetched chunk sums (the order gemv_row_scales uses)
-  float rsv[1][4] = {{1.f, 1.f, 1.f, 1.f}};
+  // row scale of this lane's row from the prefetched chunk sums (the order
+  // gemv_row_scales uses)
+  float rs = 1.f;
   if (a.rs.ssq) {
-    float t[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) t[m] = wave_sum(pre.ck[m]);
-    const int q = lane >> 4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rsv[0][r] = rsqrtf((q == 0 ? t[r] : t[4 + r]) * a.rs.invn + a.rs.eps);
+    const float t0s = wave_sum(pre.ck[0]), t1s = wave_sum(pre.ck[1]);
+    rs = rsqrtf(((lane >> 4) == 0 ? t0s : t1s) * a.rs.invn + a.rs.eps);
   }
-  float fsv[TPW];
+  const int m = (lane >> 4) * 4 + r;
+  const bool rowok = lane < 32 && m < M;
+  float fin[TO], sq = 0.f, dt = 0.f, bm = 0.f;
+  int col[TO];
+  bool ok[TO];
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) fsv[j] = pre.fs[j];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = (lane >> 4) * 4 + r;
-    const bool rowok = lane < 32 && m < M;
-    float fin[TO], sq = 0.f, dt = 0.f, bm = 0.f;
-    int col[TO];
-    bool ok[TO];
-#pragma unroll
-    for (int jo = 0; jo < TO; ++jo) {
-      col[jo] = c0 + 16 * jo + (lane & 15);
-      ok[jo] = rowok && col[jo] < outG;
-      const long long xi = (long long)m * outG + col[jo];
-      float y = 0.f;
-      fin[jo] = 0.f;
-      if (ok[jo]) {
-        if (swiglu) {
-          const float g = v[jo][r] * fsv[jo] * rsv[0][r], u = v[jo + TO][r] * fsv[jo + TO] * rsv[0][r];
-          fin[jo] = g / (1.f + __expf(-g)) * u;
-        } else {
-          y = v[jo][r] * fsv[jo] * rsv[0][r];
-          if (a.epi == OWN_RESID) y += pre.x[r][jo];
-          a.x_out[xi] = y;
-          sq += y * y;
-          if (a.g1) {
-            fin[jo] = pre.g1[jo] * y;
-            if (a.dotw) dt += fin[jo] * pre.dw[jo];
-          }
+  for (int jo = 0; jo < TO; ++jo) {
+    col[jo] = c0 + 16 * jo + (lane & 15);
+    ok[jo] = rowok && col[jo] < outG;
+    const long long xi = (long long)m * outG + col[jo];
+    float y = 0.f;
+    fin[jo] = 0.f;
+    if (ok[jo]) {
+      if (swiglu) {
+        const float g = v[jo] * pre.fs[jo] * rs, u = v[jo + TO] * pre.fs[jo + TO] * rs;
+        fin[jo] = g / (1.f + __expf(-g)) * u;
+      } else {
+        y = v[jo] * pre.fs[jo] * rs;
+        if (a.epi == OWN_RESID) y += pre.x[jo];
+        a.x_out[xi] = y;
+        sq += y * y;
+        if (a.g1) {
+          fin[jo] = pre.g1[jo] * y;
+          if (a.dotw) dt += fin[jo] * pre.dw[jo];
         }
       }
-      bm = fmaxf(bm, fabsf(fin[jo]));
     }
-    if (a.ssq_out) {
-      sq = row16_sum(sq);
-      if ((lane & 15) == 0 && rowok) a.ssq_out[m * SSQ_LD + blockIdx.x] = sq;
-    }
-    if (a.dot_out) {
-      dt = row16_sum(dt);
-      if ((lane & 15) == 0 && rowok) a.dot_out[m * SSQ_LD + blockIdx.x] = dt;
-    }
-    if (a.fd.ptr && (swiglu || a.g1)) {
-      if (a.fd.i8) {
-        bm = row16_max(bm);
+    bm = fmaxf(bm, fabsf(fin[jo]));
+  }
+  if (a.ssq_out) {
+    sq = row16_sum(sq);
+    if ((lane & 15) == 0 && rowok) a.ssq_out[m * SSQ_LD + blockIdx.x] = sq;
+  }
+  if (a.dot_out) {
+    dt = row16_sum(dt);
+    if ((lane & 15) == 0 && rowok) a.dot_out[m * SSQ_LD + blockIdx.x] = dt;
+  }
+  if (a.fd.ptr && (swiglu || a.g1)) {
+    if (a.fd.i8) {
+      bm = row16_max(bm);
 #pragma unroll
-        for (int jo = 0; jo < TO; ++jo)
-          if (ok[jo]) frag_put_i8(a.fd, 0, m, col[jo], fin[jo], bm);
-      } else {
+      for (int jo = 0; jo < TO; ++jo)
+        if (ok[jo]) frag_put_i8(a.fd, 0, m, col[jo], fin[jo], bm);
+    } else {
 #pragma unroll
-        for (int jo = 0; jo < TO; ++jo)
-          if (ok[jo]) frag_put(a.fd, 0, m, col[jo], fin[jo]);
-      }
+      for (int jo = 0; jo < TO; ++jo)
+        if (ok[jo]) frag_put(a.fd, 0, m, col[jo], fin[jo]);
     }
   }
 }
@@ -469,7 +462,7 @@ __global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
   const int kb1 = min(KB, kb0 + (NW == 8 && wave >= 4 ? lo : hi));
   OwnPre pre{};
   if constexpr (NW > 0) {
-    if (wave == 0 && active) own_prefetch<TPW>(a, t0, lane, pre);
+    if (wave < 4 && active) own_prefetch<TPW>(a, t0, lane, wave, pre);
   }
   const int nkb = kb1 - kb0;
   const int g = (AMODE == A_ROWS_BF || AMODE == A_ROWS_I8) ? min(blockIdx.x * 4 * TPW, T - 1) / a.w.TG
