@@ -10,7 +10,7 @@ with every input already resident in HBM.  Prints ONE JSON line.
 
 value = draft-pass latency in microseconds per 7-token block (lower is
 better), timed over K replays of the pass captured in a HIP graph (the pass
-is a chain of ~67 dependent launches, so a serving loop replays it as a
+is a chain of 53 dependent launches, so a serving loop replays it as a
 graph; with --no-graph, or should capture fail, K eager passes); the eager
 time is reported beside it.  The JSON also carries the achieved algorithmic HBM bandwidth of the
 pass, the roofline of the dominant kernel (the lm_head GEMM, one launch per
@@ -233,6 +233,66 @@ def secondary_record(k: int, steps: int, warmup: int) -> dict:
     return rec
 
 
+def layer_record(steps: int, warmup: int) -> dict:
+    """One full-size MLA layer, attention half (input norm, q/kv projections,
+    absorbed attention over 4,096 latent rows, o_proj and the residual), all
+    bf16, through dspark_layer_forward.  Its 207 MB fit in the 256 MB
+    Infinity Cache, so a 1 GiB buffer is read and written between timed calls
+    (outside each call's events); back-to-back calls are reported as warm."""
+    import numpy as np
+    import torch
+    from mla_block_drafter_amd import dspark as D
+    from synth import accounting as A, configs as C, gen
+    wl = C.CFG2
+    m = wl.model
+    t = time.time()
+    stored = gen.make_weights(wl)
+    inp = gen.make_inputs(wl)
+    model = D.Model(m, D.upload_stored(stored), layers_only=True)
+    del stored
+    xi = torch.from_numpy(np.ascontiguousarray(inp.x_in, np.float32)).cuda()
+    xo = torch.empty_like(xi)
+    kv = torch.from_numpy(inp.caches[0].view(np.int16)).cuda().view(torch.bfloat16)
+    offs = torch.from_numpy(inp.kv_offsets.astype(np.int32)).cuda()
+    ws = model.workspace(wl.n_seq, wl.total_ctx)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+
+    def run():
+        model.layer_forward(0, False, xi, xo, kv, offs, wl.total_ctx, ws)
+
+    for _ in range(warmup):
+        flush.add_(1.0)
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        flush.add_(1.0)
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    cold = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    warm = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    total = A.total_bytes(wl)
+    med = float(np.median(cold))
+    gbs = total / (med * 1e-6) / 1e9
+    rec = {"workload": wl.name, "calls": steps, "us_median_p10_p90": [round(med, 2), round(float(np.percentile(cold, 10)), 2),
+                                                                     round(float(np.percentile(cold, 90)), 2)],
+           "warm_us_median": round(float(np.median(warm)), 2), "infinity_cache": "flushed (1 GiB read and written between calls)",
+           "algorithmic_bytes": total, "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "launch": "eager"}
+    log(f"[bench] layer {wl.name}: {rec['us_median_p10_p90']} us flushed, {rec['warm_us_median']} us warm "
+        f"({time.time() - t:.0f}s with generation)")
+    del model, ws, kv, flush
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,7 +311,7 @@ def main():
     ap.add_argument("--read-calibration", action="store_true",
                     help="only run a 1 GiB device read (second byte-counter calibration) and exit")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the secondary records (long-context BF16, batched FP8)")
+                    help="skip the secondary records (long-context BF16, batched FP8, one MLA layer)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -271,7 +331,10 @@ def main():
 
     wl = C.PRESETS[args.config]
     m = wl.model
-    assert not wl.attn_only, "bench runs whole draft passes"
+    if wl.attn_only:
+        # the single-layer workload: its own record (not the headline metric)
+        print(json.dumps(layer_record(steps=max(args.steps, 10), warmup=args.warmup)), flush=True)
+        return
     t = time.time()
     stored = gen.make_weights(wl)
     inp = gen.make_inputs(wl)
@@ -512,6 +575,7 @@ def main():
         del model, ws, kv, cap
         torch.cuda.empty_cache()
         out["secondary"] = [secondary_record(k, steps=min(K, 20), warmup=min(args.warmup, 3)) for k in (4, 5)]
+        out["layer"] = layer_record(steps=max(K, 50), warmup=args.warmup)
     print(json.dumps(out), flush=True)
 
 

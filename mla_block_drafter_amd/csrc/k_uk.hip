@@ -19,9 +19,15 @@ namespace {
 constexpr int QBA_TPW = 2;  // W_UK tiles per wave
 constexpr int QBA_KB = 4;   // k blocks of 32 (qk_nope = 128)
 constexpr int QBA_NI = 3;   // column pairs per thread: M (dn + dr) / 2 <= 768
+// A fragments in LDS: 16 bytes per (k block, lane), one pad unit after every
+// 16 lanes, so that the 4-byte writes of one row's columns (consecutive
+// threads: consecutive column pairs) fall on distinct banks; the MFMA reads
+// of 16 consecutive lanes stay contiguous.
+constexpr int QBA_AKB = 68;  // 16-byte units per k block
+__device__ __forceinline__ int qba_pos(int kb, int l) { return kb * QBA_AKB + (l >> 4) * 17 + (l & 15); }
 
 __global__ __launch_bounds__(256) void k_qb_absorb(QbAbsorbArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t afr[QBA_KB][64][4];  // A fragments [k block][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 afr[QBA_KB * QBA_AKB];  // A fragments (qba_pos)
   const GemvArgs& g = a.g;
   const QbPost& p = a.qb;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -103,8 +109,8 @@ __global__ __launch_bounds__(256) void k_qb_absorb(QbAbsorbArgs a) {
   for (int i = threadIdx.x; i < QBA_KB * 4 * 8; i += 256) {
     const int row = i & 7, q = (i >> 3) & 3, kb = i >> 5;
     if (row >= M) {
-      *(u32x4*)afr[kb][q * 16 + row] = u32x4{0u, 0u, 0u, 0u};
-      *(u32x4*)afr[kb][q * 16 + 8 + row] = u32x4{0u, 0u, 0u, 0u};
+      afr[qba_pos(kb, q * 16 + row)] = u32x4{0u, 0u, 0u, 0u};
+      afr[qba_pos(kb, q * 16 + 8 + row)] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 #pragma unroll
@@ -126,8 +132,8 @@ __global__ __launch_bounds__(256) void k_qb_absorb(QbAbsorbArgs a) {
       const uint32_t hi = pack_bf16x2(v[0], v[1]);
       const uint32_t lo = pack_bf16x2(v[0] - bf16_bits_to_f32(hi & 0xFFFFu), v[1] - bf16_bits_to_f32(hi >> 16));
       const int kb = e >> 5, q = (e >> 3) & 3, wd = (e & 7) >> 1;
-      afr[kb][q * 16 + m][wd] = hi;
-      afr[kb][q * 16 + 8 + m][wd] = lo;
+      ((uint32_t*)&afr[qba_pos(kb, q * 16 + m)])[wd] = hi;
+      ((uint32_t*)&afr[qba_pos(kb, q * 16 + 8 + m)])[wd] = lo;
     } else {
       const int s = m / p.block, i = m % p.block, er = e - p.dn;
       float y0, y1;
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(256) void k_qb_absorb(QbAbsorbArgs a) {
   for (int j = 0; j < QBA_TPW; ++j) acc[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < QBA_KB; ++kb) {
-    const bf16x8 A = __builtin_bit_cast(bf16x8, *(const u32x4*)afr[kb][lane]);
+    const bf16x8 A = __builtin_bit_cast(bf16x8, afr[qba_pos(kb, lane)]);
 #pragma unroll
     for (int j = 0; j < QBA_TPW; ++j)
       acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, w[kb][j]), acc[0][j], 0, 0, 0);

@@ -28,6 +28,12 @@ constexpr int UVC_TILES = 8;   // W_UV tiles per head at most (one per wave)
 constexpr int UVC_CHUNK = 40;  // slots whose partials are requested together
 constexpr int UVC_OLD = UVC_TILES * 16 + 4;  // LDS row stride of the GEMM outputs
 constexpr int UVC_RPW = 2;     // block rows per workgroup
+// A fragments in LDS: 16 bytes per (k block, lane), one pad unit after every
+// 16 lanes, so that the writes of one row (lanes q 16 + w over the k blocks)
+// spread over the banks; the MFMA reads of 16 consecutive lanes stay
+// contiguous.
+constexpr int UVC_AKB = 68;    // 16-byte units per k block
+__device__ __forceinline__ int afr_pos(int kb, int l) { return kb * UVC_AKB + (l >> 4) * 17 + (l & 15); }
 
 // Slot U of the first chunk (weight in lane U of e0), then the next slot:
 // each waits only for its own partials (issued in slot order, NAFTER more
@@ -47,7 +53,7 @@ __device__ __forceinline__ void merge_chunk0(float (&v)[8], const u32x4 (&x)[NU]
 }
 
 template <int KB>
-__device__ __forceinline__ void uv_combine(const UvCombineArgs& a, unsigned char* wlds, bf16x8 (*afr)[64],
+__device__ __forceinline__ void uv_combine(const UvCombineArgs& a, unsigned char* wlds, bf16x8* afr,
                                            float (*olds)[UVC_OLD]) {
   constexpr int NCOPYW = 8 - UVC_RPW;        // waves that copy W_UV
   constexpr int NCH = UVC_TILES * KB;        // 1 KiB chunks of W_UV space in LDS
@@ -149,16 +155,16 @@ __device__ __forceinline__ void uv_combine(const UvCombineArgs& a, unsigned char
         lo[q] = pack_bf16x2(v[2 * q] - bf16_bits_to_f32(hi[q] & 0xFFFFu), v[2 * q + 1] - bf16_bits_to_f32(hi[q] >> 16));
       }
       const int kb = lane >> 2, q = lane & 3;
-      afr[kb][q * 16 + wave] = __builtin_bit_cast(bf16x8, hi);
-      afr[kb][q * 16 + 8 + wave] = __builtin_bit_cast(bf16x8, lo);
+      afr[afr_pos(kb, q * 16 + wave)] = __builtin_bit_cast(bf16x8, hi);
+      afr[afr_pos(kb, q * 16 + 8 + wave)] = __builtin_bit_cast(bf16x8, lo);
     }
   } else if (wave < UVC_RPW) {
     // no row for this wave: its fragment rows are zero
     if (lane < NLANE) {
       const int kb = lane >> 2, q = lane & 3;
       const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      afr[kb][q * 16 + wave] = z;
-      afr[kb][q * 16 + 8 + wave] = z;
+      afr[afr_pos(kb, q * 16 + wave)] = z;
+      afr[afr_pos(kb, q * 16 + 8 + wave)] = z;
     }
   } else {
     // the head's W_UV tiles into LDS; fragment rows UVC_RPW..7 are zero.
@@ -167,8 +173,8 @@ __device__ __forceinline__ void uv_combine(const UvCombineArgs& a, unsigned char
     if (lane < NLANE) {
       const int kb = lane >> 2, q = lane & 3;
       const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      afr[kb][q * 16 + wave] = z;
-      afr[kb][q * 16 + 8 + wave] = z;
+      afr[afr_pos(kb, q * 16 + wave)] = z;
+      afr[afr_pos(kb, q * 16 + 8 + wave)] = z;
     }
     const unsigned char* wsrc = g.w.codes + (long long)h * TG * KB * 1024;
     const int nch = TG * KB;
@@ -186,7 +192,7 @@ __device__ __forceinline__ void uv_combine(const UvCombineArgs& a, unsigned char
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 A = afr[kb][lane];
+      const bf16x8 A = afr[afr_pos(kb, lane)];
       const bf16x8 B = *(const bf16x8*)(wlds + ((wave * KB + kb) * 64 + lane) * 16);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
     }
@@ -227,7 +233,7 @@ __device__ __forceinline__ void uv_combine(const UvCombineArgs& a, unsigned char
 template <int KB>
 __global__ __launch_bounds__(512) void k_uv_combine(UvCombineArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char wlds[UVC_TILES * KB * 1024];  // W_UV tiles of the head
-  __shared__ __attribute__((aligned(16))) bf16x8 afr[KB][64];                          // A fragments [k block][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 afr[KB * UVC_AKB];                    // A fragments (afr_pos)
   __shared__ float olds[16][UVC_OLD];                                                  // GEMM outputs
   uv_combine<KB>(a, wlds, afr, olds);
 }
