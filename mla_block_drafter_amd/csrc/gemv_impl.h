@@ -290,19 +290,20 @@ template <int TPW, int NW>
 __device__ __forceinline__ void own_epilogue(const GemvArgs& a, const f32x4 (&acc)[TPW], int t0, int lane, int wave,
                                              const OwnPre& pre) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gemv_smem[];
-  f32x4* red = (f32x4*)gemv_smem;  // [NW][TPW][64]
-  const float* redf = (const float*)gemv_smem;
+  float* red = (float*)gemv_smem;  // [NW][TPW][4 accumulator rows][64 lanes]: both sides lane-contiguous
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) red[(wave * TPW + j) * 64 + lane] = acc[j];
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[((wave * TPW + j) * 4 + q) * 64 + lane] = acc[j][q];
   __syncthreads();
   if (wave >= 4) return;
   const int r = wave;
   float v[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
-    v[j] = redf[(j * 64 + lane) * 4 + r];
+    v[j] = red[(j * 4 + r) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) v[j] += redf[((w * TPW + j) * 64 + lane) * 4 + r];
+    for (int w = 1; w < NW; ++w) v[j] += red[((w * TPW + j) * 4 + r) * 64 + lane];
     v[j] += __shfl_xor(v[j], 32, 64);
   }
   const int M = a.M, G = a.w.G;
@@ -426,9 +427,9 @@ __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, 
 //             integer products, one convert and one fp32 fma per output per
 //             block (factor d_w); s is applied once at the end.
 //  A_LDS_BF:  FP8 or BF16 weights with several m-tiles (M > 8): the workgroup's
-//             four waves share one k range, so the bf16 activation fragments
-//             of a chunk of LDS_BF_CK k blocks (all m-tiles) are loaded once
-//             per workgroup, a quarter per wave, one chunk ahead into
+//             lds_bf_waves(FMT) waves share one k range, so the bf16 activation
+//             fragments of a chunk of LDS_BF_CK k blocks (all m-tiles) are
+//             loaded once per workgroup, a share per wave, one chunk ahead into
 //             registers, then written to LDS (two buffers) and read from there
 //             by every wave.  Ordinary loads return in order, so the chunk's
 //             wait leaves the weight prefetch in flight (direct-to-LDS copies
@@ -441,13 +442,14 @@ __device__ __forceinline__ void load_row8(const GemvArgs& a, const float* rows, 
 // waves of a workgroup own consecutive tile sets and the k range is the
 // workgroup's split-K slice (blockIdx.y).
 template <int FMT, int MT, int TPW, int MODE, int AMODE, int NW = 0>
-__global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
+__global__ __launch_bounds__(NW ? 64 * NW : (AMODE == A_LDS_BF ? 64 * lds_bf_waves(FMT) : 256)) void k_gemv_bf(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gemv_smem[];
   // wave index made wave-uniform (scalar): tile bases and buffer resources
   // derived from it live in scalar registers
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = a.w.ngroups * a.w.TG;
-  const int t0 = NW ? blockIdx.x * (a.tile_jump ? TPW / 2 : TPW) : (blockIdx.x * 4 + wave) * TPW;
+  constexpr int WPG = AMODE == A_LDS_BF ? lds_bf_waves(FMT) : 4;  // split-K: waves per workgroup
+  const int t0 = NW ? blockIdx.x * (a.tile_jump ? TPW / 2 : TPW) : (blockIdx.x * WPG + wave) * TPW;
   const bool active = t0 < T;
   // tile j of this wave is t0 + tj(j); the span of tiles its loads cover
   const int jump = NW ? a.tile_jump : 0;
@@ -676,7 +678,7 @@ __global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
     constexpr int WL = FMT == DT_FP8 ? 1 : 2;  // 16-byte weight loads per tile and pair of k blocks
     constexpr int CK = LDS_BF_CK;          // k blocks per chunk
     constexpr int D = CK / 2;              // pairs of k blocks per chunk = weight pairs in flight
-    constexpr int NA = (MT * CK + 3) / 4;  // activation fragments per wave per chunk
+    constexpr int NA = (MT * CK + WPG - 1) / WPG;  // activation fragments per wave per chunk
     const int KP = KB >> 1, P0 = kb0 >> 1, P1 = kb1 >> 1;
     const __amdgpu_buffer_rsrc_t wr = buf_rsrc((const unsigned char*)a.w.codes + (long long)(active ? t0 : 0) * KP * WL * 1024,
                                                active ? (uint32_t)(span * KP * WL * 1024) : 0u);
@@ -688,7 +690,7 @@ __global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
     auto load_chunk = [&](int c) {
 #pragma unroll
       for (int n = 0; n < NA; ++n) {
-        const int i = wave + 4 * n, mt = i / CK, kk = i % CK, kb = kb0 + c * CK + kk;
+        const int i = wave + WPG * n, mt = i / CK, kk = i % CK, kb = kb0 + c * CK + kk;
         const bool ok = i < MT * CK && kb < kb1;
         areg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
             ar, ok ? (uint32_t)((mt * KB + kb) * 1024) + l16 : BUF_OOB, 0, 0));
@@ -697,7 +699,7 @@ __global__ __launch_bounds__(NW ? 64 * NW : 256) void k_gemv_bf(GemvArgs a) {
     auto store_chunk = [&](int buf) {
 #pragma unroll
       for (int n = 0; n < NA; ++n) {
-        const int i = wave + 4 * n;
+        const int i = wave + WPG * n;
         if (i < MT * CK) lds_a[((buf * MT + i / CK) * CK + i % CK) * 64 + lane] = areg[n];
       }
     };
@@ -1230,7 +1232,7 @@ inline bool gemv_lds_i8(const GemvPlan& p) { return p.ksteps_per_split * 520 <= 
 
 template <int FMT, int MT, int TPW, int MODE>
 hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
-  dim3 grid(p.grid_x, p.S), block(256);
+  dim3 grid(p.grid_x, p.S), block(p.amode == A_LDS_BF ? 64 * lds_bf_waves(FMT) : 256);
   const size_t lds = gemv_lds_bytes(p);
   if (FMT == DT_F32) {
     hipLaunchKernelGGL((k_gemv_f32<MT, TPW, MODE>), grid, block, 0, st, a);

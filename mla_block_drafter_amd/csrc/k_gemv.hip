@@ -49,11 +49,13 @@ GemvPlan plan_gemv(const PackedMat& w, int M, bool allow_split, bool gather, boo
     else if (w.TG % 2 == 0 && T / 2 >= (allow_split ? 128 : 256)) p.TPW = 2;
   }
   const int waves = T / p.TPW;
-  p.grid_x = (waves + 3) / 4;
   const int ksteps = f32 ? (w.Kp >> 4) : w.KB;
   // activation fragments of several m-tiles shared through LDS (A_LDS_BF),
-  // whose k loop steps over pairs of k blocks
+  // whose k loop steps over pairs of k blocks; lds_bf_waves() waves per
+  // workgroup share each staged chunk
   const bool lds_bf = (w.fmt == DT_FP8 || w.fmt == DT_BF16) && p.MT > 1 && !gather && w.ngroups == 1;
+  const int wpg = lds_bf ? lds_bf_waves(w.fmt) : 4;
+  p.grid_x = (waves + wpg - 1) / wpg;
   const int unit = w.fmt == DT_MXFP4 ? 4 : (w.fmt == DT_Q8_0 || w.fmt == DT_FP8 || lds_bf) ? 2 : 1;
   int S = 1;
   if (allow_split)

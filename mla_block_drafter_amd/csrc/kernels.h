@@ -93,6 +93,13 @@ struct GemvArgs {
   float* dot_out;
 };
 
+// Waves of a split-K workgroup whose activation chunks are shared through LDS
+// (amode 5): every staged chunk feeds that many x TPW weight tiles.  FP8
+// weights (1 byte per weight against 2 per activation element) read half as
+// many activation bytes with eight waves; the BF16 lm_head measured faster
+// with four.
+constexpr int lds_bf_waves(int fmt) { return fmt == DT_FP8 ? 8 : 4; }
+
 struct GemvPlan {
   int MT, TPW, S, ksteps_per_split, hilo;
   int ksteps_lo;          // GEMV_OWN with 8 waves: k steps of waves 4..7
