@@ -123,20 +123,22 @@ def read_calibration():
 
 
 def read_probe_gbs(torch) -> float:
-    """Device read bandwidth of a streaming reduction over 1 GiB (bytes read
-    / time): the achievable rate for a read-only weight stream."""
+    """Device read bandwidth of the library's streaming-read probe over 1 GiB
+    (dspark_read_probe: 16-byte non-temporal loads, 2048 workgroups; bytes
+    read / time): the achievable rate for a read-only weight stream."""
+    from mla_block_drafter_amd import dspark as D
     n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-    acc = torch.zeros((), dtype=torch.float32, device="cuda")
-    acc += src.sum()
+    out = torch.zeros(D.READ_PROBE_WORDS, dtype=torch.int32, device="cuda")
+    D.read_probe(src, out)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(5):
-        acc += src.sum()
+        D.read_probe(src, out)
     b.record()
     torch.cuda.synchronize()
     gbs = n * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src
+    del src, out
     torch.cuda.empty_cache()
     return gbs
 
@@ -566,7 +568,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "lm_head GEMM (k_gemv_bf, BF16 weights)",
                      "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
+                     "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2),
+                     "frac_of_read_probe": round(lm_gbs / read_gbs, 4)},
         "cpu_baseline": cpu,
         "cache_append": append,
         "sampling": sampling,

@@ -386,6 +386,17 @@ int32_t dspark_accept_len_host(const int32_t* draft, const int32_t* verifier, in
  * Asynchronous on `stream`.  Intended for tests. */
 int32_t dspark_dequant(const dspark_model* m, int32_t weight_id, float* out, void* stream);
 
+/* Read-bandwidth probe (a measurement aid, no part of the draft pass): reads
+ * `bytes` bytes of device memory at `buf` once, with the 16-byte
+ * non-temporal loads and the kind of grid the weight-streaming GEMMs use, and
+ * writes one 32-bit XOR of the words each workgroup read to out[0 .. 2047]
+ * (device memory, 2048 entries, so that no load can be dropped).  Timing it
+ * gives the achievable streaming-read rate that the GEMMs' rates are compared
+ * with.  buf must be 16-byte aligned and bytes a multiple of 16.
+ * Asynchronous on `stream`; DSPARK_EINVAL for a NULL, misaligned or
+ * mis-sized argument. */
+int32_t dspark_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
 /* Thread-local text of the last error ("" if none). */
 const char* dspark_last_error(void);
 

@@ -437,14 +437,15 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   P.zero_end = off;
   P.part = take(part);
   P.bkeys = take((long long)M * (c.kv_lora + c.qk_rope) * (kv_f32 ? 4 : 2));
-  // Keys per attention slot: the multiple of 32 in [256, 2048] with the
+  // Keys per attention slot: the multiple of 32 in [128, 2048] with the
   // smallest estimated attention time.  One workgroup runs per CU (256 on
   // MI355X), so the grid of (rows / 64) x slots workgroups runs in whole
   // rounds; a workgroup costs about seven key tiles' time in fixed work (query
   // and first-tile loads, partial stores) plus one per key tile, and its slot
   // partials are written and read back once more (at ~6 TB/s).  At context
   // 98,304 this picks 1376 keys (2 rounds of 72 slots) over 1024 (3 rounds);
-  // short contexts keep 256.  The slot count uses the bound cdiv(keys, C) +
+  // context 8192 keeps 256 (one round), and context 4096 takes 160 (189
+  // workgroups of 5 tiles instead of 126 of 8).  The slot count uses the bound cdiv(keys, C) +
   // n_seq, which holds for any split of the context between sequences.
   {
     constexpr int kCUs = 256;
@@ -452,12 +453,12 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
     const long long part_row = (long long)c.kv_lora * 2 + 8;
     const double step_s = 1.05e-6;  // one key tile of a workgroup, measured
     double best = 0.0;
-    for (int cc = 256; cc <= 2048; cc += 32) {
+    for (int cc = 128; cc <= 2048; cc += 32) {
       const long long slots = cdiv(keys, cc) + n_seq;
       const long long rounds = cdiv((long long)(P.rows_pad / 64) * slots, kCUs);
       const double cost = (double)rounds * (7 + cc / 32) +
                           2.0 * (double)slots * P.rows_pad * part_row / 6e12 / step_s;
-      if (cc == 256 || cost < best) {
+      if (cc == 128 || cost < best) {
         best = cost;
         P.C = cc;
       }
@@ -1458,6 +1459,17 @@ int32_t dspark_accept_len(const int32_t* draft, const int32_t* verifier, int32_t
   if (n_seq < 0 || block < 0) return fail(DSPARK_EINVAL, "negative n_seq / block");
   if (n_seq == 0) return DSPARK_OK;
   HIPCHK(launch_accept_len(draft, verifier, n_seq, block, out_len, (hipStream_t)stream));
+  return DSPARK_OK;
+}
+
+static_assert(READ_PROBE_WGS == 2048, "the header promises 2048 output words");
+
+int32_t dspark_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  g_err.clear();
+  if (!buf || !out) return fail(DSPARK_EINVAL, "NULL pointer");
+  if (misaligned(buf, 16) || bytes % 16 || misaligned(out, 4))
+    return fail(DSPARK_EINVAL, "buf must be 16-byte aligned, bytes a multiple of 16, out 4-byte aligned");
+  HIPCHK(launch_read_probe(buf, bytes, out, (hipStream_t)stream));
   return DSPARK_OK;
 }
 

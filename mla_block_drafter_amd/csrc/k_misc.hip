@@ -1,7 +1,7 @@
 // Small kernels of the draft pass: workspace init and fc input fragments, the
 // Markov finaliser (tokens, confidence, hidden output), acceptance length, and
 // weight repack / decode.
-#include "kernels.h"
+#include "gemv_impl.h"
 
 namespace dspark {
 
@@ -35,6 +35,73 @@ __global__ __launch_bounds__(256) void k_init(InitArgs a) {
   const int K = a.ncap * a.H;
   const int Kp = fd.rows ? K : fd.f32 ? fd.KG * 16 : fd.KB * 32;
   const int rows = fd.rows ? M : (fd.hilo || fd.i8) ? 8 : fd.MT * 16;
+  if (!fd.rows && !fd.f32 && a.H % 8 == 0) {
+    // bf16 / int8 fragments keep eight consecutive columns of a row together:
+    // one thread per (row, 8 columns), one 8- or 16-byte store per code row.
+    // K8 is a multiple of 4 and the thread count of 64, so each quad of lanes
+    // holds one 32-column block of one row (its int8 scale: a quad maximum).
+    const int K8 = Kp / 8;
+    const long long total8 = (long long)rows * K8;
+    const bool al16 = ((uintptr_t)a.captured & 15) == 0;  // idx is a multiple of 8
+    for (long long e = tid; e < total8; e += nthr) {
+      const int m = (int)(e / K8), k0 = (int)(e % K8) * 8;
+      float v[8];
+      const bool in = m < M && k0 < K;
+      const int s = m / a.block, i = m % a.block, c = k0 / a.H, h = k0 % a.H;
+      const long long idx = in ? (((long long)s * a.ncap + c) * a.block + i) * a.H + h : 0;
+      if (!in) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = 0.f;
+      } else if (al16 && a.cap_f32) {
+        const f32x4 x0 = *(const f32x4*)((const float*)a.captured + idx);
+        const f32x4 x1 = *(const f32x4*)((const float*)a.captured + idx + 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[u] = x0[u];
+          v[4 + u] = x1[u];
+        }
+      } else if (al16) {
+        const u32x4 x = *(const u32x4*)((const uint16_t*)a.captured + idx);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[2 * u] = bf16_bits_to_f32(x[u] & 0xFFFFu);
+          v[2 * u + 1] = bf16_bits_to_f32(x[u] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = a.cap_f32 ? ((const float*)a.captured)[idx + u]
+                           : bf16_bits_to_f32(((const uint16_t*)a.captured)[idx + u]);
+      }
+      if (fd.i8) {
+        float bm = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) bm = fmaxf(bm, fabsf(v[u]));
+        bm = fmaxf(bm, dpp_mov<DPP_XOR1>(bm));
+        bm = fmaxf(bm, dpp_mov<DPP_XOR2>(bm));
+        frag_put_i8_x8(fd, 0, m, k0, v, frag_i8_exp(bm));
+      } else {
+        const int kb = k0 >> 5, q = (k0 >> 3) & 3;
+        uint16_t* p = (uint16_t*)fd.ptr;
+        u32x4 hw, lw;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t h0 = f32_to_bf16_bits(v[2 * u]), h1 = f32_to_bf16_bits(v[2 * u + 1]);
+          hw[u] = h0 | (h1 << 16);
+          lw[u] = f32_to_bf16_bits(v[2 * u] - bf16_bits_to_f32(h0)) |
+                  (f32_to_bf16_bits(v[2 * u + 1] - bf16_bits_to_f32(h1)) << 16);
+        }
+        if (fd.hilo) {
+          *(u32x4*)(p + ((long long)kb * 64 + q * 16 + m) * 8) = hw;
+          *(u32x4*)(p + ((long long)kb * 64 + q * 16 + 8 + m) * 8) = lw;
+        } else {
+          const int mt = m >> 4;
+          *(u32x4*)(p + ((long long)(mt * fd.KB + kb) * 64 + q * 16 + (m & 15)) * 8) = hw;
+        }
+      }
+    }
+    return;
+  }
   const long long total = (long long)rows * Kp;
   for (long long e = tid; e < total; e += nthr) {
     const int m = (int)(e / Kp), k = (int)(e % Kp);
@@ -251,6 +318,43 @@ __global__ __launch_bounds__(256) void k_dequant(PackedMat w, float* out) {
 }
 
 }  // namespace
+
+// Streaming read laid out as the weight-streaming GEMMs read: each wave owns
+// one contiguous range of 1 KiB chunks (64 lanes x 16 bytes) and keeps eight
+// chunks in flight with non-temporal buffer loads (loads past the buffer
+// return zeros without a memory access); each workgroup folds what it read
+// into one XOR word.
+__global__ __launch_bounds__(256) void k_read_probe(const unsigned char* p, long long bytes, uint32_t* out) {
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long nchunk = (bytes + 1023) / 1024, nw = (long long)gridDim.x * 4;
+  const long long per = (nchunk + nw - 1) / nw, c0 = min(nchunk, ((long long)blockIdx.x * 4 + wave) * per);
+  const long long c1 = min(nchunk, c0 + per);
+  const long long rbytes = max(0ll, min(bytes - c0 * 1024, (c1 - c0) * 1024));  // 0 for waves past the data
+  const __amdgpu_buffer_rsrc_t r = buf_rsrc(p + c0 * 1024, (uint32_t)rbytes);
+  u32x4 x = {0u, 0u, 0u, 0u};
+  for (long long c = 0; c < c1 - c0; c += 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r, c + u < c1 - c0 ? (uint32_t)((c + u) * 1024 + lane * 16) : BUF_OOB, 0, BUF_NT));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u];
+  }
+  uint32_t v = x[0] ^ x[1] ^ x[2] ^ x[3];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v ^= (uint32_t)__shfl_xor((int)v, o, 64);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t st) {
+  if (bytes / 1024 / (READ_PROBE_WGS * 4) >= (1ll << 22)) return hipErrorInvalidValue;  // a wave's range < 4 GiB
+  hipLaunchKernelGGL(k_read_probe, dim3(READ_PROBE_WGS), dim3(256), 0, st, (const unsigned char*)buf, (long long)bytes, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_init(const InitArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_init, dim3(512), dim3(256), 0, st, a);

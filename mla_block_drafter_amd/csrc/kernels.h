@@ -180,6 +180,10 @@ struct InitArgs {
 };
 hipError_t launch_init(const InitArgs& a, hipStream_t st);
 
+// Streaming-read probe (measurement): READ_PROBE_WGS workgroups, one XOR word each.
+constexpr int READ_PROBE_WGS = 2048;
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t st);
+
 // Split-K partial sums [S][M][ld] of one GEMM.
 struct PartIn {
   const float* part;

@@ -32,7 +32,7 @@ EXPORTS = ["dspark_packed_bytes", "dspark_model_create", "dspark_model_destroy",
            "dspark_append_workspace_bytes", "dspark_cache_append",
            "dspark_verify_workspace_bytes", "dspark_verify",
            "dspark_accept_len", "dspark_accept_len_host", "dspark_dequant", "dspark_last_error",
-           "dspark_draft_block_static"]
+           "dspark_draft_block_static", "dspark_read_probe"]
 STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -146,6 +146,8 @@ def lib():
     L.dspark_accept_len_host.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
     L.dspark_dequant.restype = C.c_int32
     L.dspark_dequant.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]
+    L.dspark_read_probe.restype = C.c_int32
+    L.dspark_read_probe.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
     L.dspark_last_error.restype = C.c_char_p
     L.dspark_last_error.argtypes = []
     _lib = L
@@ -359,6 +361,18 @@ def accept_len_host(draft, verifier):
     out = np.zeros(d.shape[0], dtype=np.int32)
     check(lib().dspark_accept_len_host(d.ctypes.data, v.ctypes.data, d.shape[0], d.shape[1], out.ctypes.data))
     return out
+
+
+READ_PROBE_WORDS = 2048
+
+
+def read_probe(buf, out, stream=None) -> None:
+    """Stream-read the device tensor `buf` once (dspark_read_probe); `out`:
+    int32 device tensor of READ_PROBE_WORDS entries (one XOR word per
+    workgroup)."""
+    assert out.numel() >= READ_PROBE_WORDS and out.element_size() == 4
+    check(lib().dspark_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
+                                  _stream_ptr(stream)))
 
 
 def upload_stored(stored: Dict[str, object], device: str = "cuda") -> Dict[str, tuple]:

@@ -45,3 +45,17 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(D, "_lib", None, raising=False)
     with pytest.raises(ImportError):
         D.lib()
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libdspark.so not built (run __graft_entry__.build())")
+def test_read_probe_rejects_bad_arguments_before_enqueue():
+    """dspark_read_probe validates on the host (no device is touched)."""
+    lib = ctypes.CDLL(LIB)
+    lib.dspark_read_probe.restype = ctypes.c_int32
+    lib.dspark_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    EINVAL = -1
+    assert lib.dspark_read_probe(None, 16, 0x2000, None) == EINVAL
+    assert lib.dspark_read_probe(0x1000, 16, None, None) == EINVAL
+    assert lib.dspark_read_probe(0x1008, 16, 0x2000, None) == EINVAL   # buf not 16-byte aligned
+    assert lib.dspark_read_probe(0x1000, 24, 0x2000, None) == EINVAL   # bytes not a multiple of 16
+    assert lib.dspark_read_probe(0x1000, 16, 0x2002, None) == EINVAL   # out not 4-byte aligned
