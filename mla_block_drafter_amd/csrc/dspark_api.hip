@@ -444,8 +444,8 @@ void make_plan(const dspark_model& m, int n_seq, long long total_ctx, bool kv_f3
   // and first-tile loads, partial stores) plus one per key tile, and its slot
   // partials are written and read back once more (at ~6 TB/s).  At context
   // 98,304 this picks 1376 keys (2 rounds of 72 slots) over 1024 (3 rounds);
-  // context 8192 keeps 256 (one round), and context 4096 takes 160 (189
-  // workgroups of 5 tiles instead of 126 of 8).  The slot count uses the bound cdiv(keys, C) +
+  // context 8192 keeps 256 (one round), and context 4096 takes 160 (26
+  // slots of 5 tiles per row group instead of 17 of 8).  The slot count uses the bound cdiv(keys, C) +
   // n_seq, which holds for any split of the context between sequences.
   {
     constexpr int kCUs = 256;
