@@ -373,7 +373,6 @@ __device__ __forceinline__ void own_epilogue(const GemvArgs& a, const f32x4 (&ac
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 enum { A_GLOBAL = 0, A_ROWS_BF = 1, A_ROWS_I8 = 2, A_GLOBAL_I8 = 3, A_LDS_I8 = 4, A_LDS_BF = 5 };
-constexpr int LDS_BF_CK = 4;  // A_LDS_BF: k blocks per staged chunk
 
 // Wait until at most N vector memory operations of this wave are outstanding:
 // the compiler's own builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
@@ -467,8 +466,11 @@ __global__ __launch_bounds__(NW ? 64 * NW : (AMODE == A_LDS_BF ? 64 * lds_bf_wav
     if (wave < 4 && active) own_prefetch<TPW>(a, t0, lane, wave, pre);
   }
   const int nkb = kb1 - kb0;
-  const int g = (AMODE == A_ROWS_BF || AMODE == A_ROWS_I8) ? min(blockIdx.x * 4 * TPW, T - 1) / a.w.TG
-                                                             : (active ? t0 / a.w.TG : 0);
+  // activation group: the workgroup's for operands staged per workgroup (its
+  // tiles lie in one group), else the wave's
+  const int g = (AMODE == A_ROWS_BF || AMODE == A_ROWS_I8 || AMODE == A_LDS_BF)
+                    ? min(blockIdx.x * WPG * TPW, T - 1) / a.w.TG
+                    : (active ? t0 / a.w.TG : 0);
 
   // ---------------------------------------------------------- prologue --
   bf16x8* alds = (bf16x8*)gemv_smem;            // A_ROWS_BF: [MT][nkb][64]

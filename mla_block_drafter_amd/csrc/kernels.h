@@ -99,6 +99,7 @@ struct GemvArgs {
 // many activation bytes with eight waves; the BF16 lm_head measured faster
 // with four.
 constexpr int lds_bf_waves(int fmt) { return fmt == DT_FP8 ? 8 : 4; }
+constexpr int LDS_BF_CK = 4;  // amode 5: k blocks per staged chunk
 
 struct GemvPlan {
   int MT, TPW, S, ksteps_per_split, hilo;
