@@ -187,6 +187,32 @@ __device__ __forceinline__ void frag_put(const FragDesc& fd, int g, int m, int k
   }
 }
 
+// Eight consecutive columns k0 .. k0 + 7 (k0 a multiple of 8) of row m of
+// group g: bf16 fragments keep them together (one 16-byte store per code
+// row); other layouts element by element.
+__device__ __forceinline__ void frag_put8(const FragDesc& fd, int g, int m, int k0, const float (&v)[8]) {
+  if (fd.rows || fd.f32 || fd.i8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) frag_put(fd, g, m, k0 + i, v[i]);
+    return;
+  }
+  const int kb = k0 >> 5, q = (k0 >> 3) & 3;
+  uint16_t* p = (uint16_t*)fd.ptr + (long long)g * fd.gstride;
+  u32x4 hw, lw;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t h0 = f32_to_bf16_bits(v[2 * u]), h1 = f32_to_bf16_bits(v[2 * u + 1]);
+    hw[u] = h0 | (h1 << 16);
+    lw[u] = f32_to_bf16_bits(v[2 * u] - bf16_bits_to_f32(h0)) | (f32_to_bf16_bits(v[2 * u + 1] - bf16_bits_to_f32(h1)) << 16);
+  }
+  if (fd.hilo) {
+    *(u32x4*)(p + ((long long)kb * 64 + q * 16 + m) * 8) = hw;
+    *(u32x4*)(p + ((long long)kb * 64 + q * 16 + 8 + m) * 8) = lw;
+  } else {
+    *(u32x4*)(p + ((long long)((m >> 4) * fd.KB + kb) * 64 + q * 16 + (m & 15)) * 8) = hw;
+  }
+}
+
 // int8 activation fragments (the A operand of v_mfma_i32_16x16x32_i8 for
 // M <= 8 rows): per group, codes [KB][64 lanes][8 bytes] then exponents
 // [KB][8 rows] (int8).  Row m of 32-block kb is v ~ (hi + lo / 256) * 2^e with

@@ -648,77 +648,55 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(AttnArgs a) {
 
 // Merge the slots of each (sequence, row) in slot order and write the
 // un-absorb fragments: with w_p = exp(m_p - M) l_p and the stored
-// Ohat_p = O_p / l_p, O = sum_p w_p Ohat_p / sum_p w_p.  Each lane owns eight
-// adjacent dims (one 16-byte load of the fp16 row per slot); wave g sums the
-// slots p = g mod 4 in slot order, the four waves' sums are added in a fixed
-// order, and each wave writes a quarter of the dims.
+// Ohat_p = O_p / l_p, O = sum_p w_p Ohat_p / sum_p w_p.  One wave per
+// (sequence, row), four per workgroup: lane p holds slot p's weight (64
+// slots per round), lane l owns dims 8 l .. 8 l + 7 (one 16-byte load of the
+// fp16 row per slot), eight slots' loads are in flight at a time, and the
+// slots are added in order with each weight read from its lane.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  __shared__ float wgt[MAX_COMBINE_SLOTS];
-  __shared__ float red[4];
-  const int row = blockIdx.x;  // i * nh + h
-  const int s = blockIdx.y;
-  if (row >= a.rows) return;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);  // s * rows + row
+  const int s = item / a.rows, row = item % a.rows;       // row = i * nh + h
+  if (s >= a.n_seq) return;                               // the whole wave
   int base = 0;
-  for (int t = 0; t < s; ++t) {
-    const int J = a.offs[t + 1] - a.offs[t] + a.block;
-    base += (J + a.C - 1) / a.C;
-  }
+  for (int t = 0; t < s; ++t) base += (a.offs[t + 1] - a.offs[t] + a.block + a.C - 1) / a.C;
   const int J = (a.len1 >= 0 ? a.len1 : a.offs[s + 1] - a.offs[s]) + a.block;
   const int ns = (J + a.C - 1) / a.C;
   const float* ml = a.ml_part + ((long long)row * a.slots + base) * 2;
   float mx = -INFINITY;
-  for (int p = threadIdx.x; p < ns; p += 256) mx = fmaxf(mx, ml[2 * p]);
-  mx = block_max256(mx, red);
-  float l = 0.f;
-  for (int p = threadIdx.x; p < ns; p += 256) {
-    const float w = __expf(ml[2 * p] - mx) * ml[2 * p + 1];
-    wgt[p] = w;
-    l += w;
-  }
-  l = block_sum256(l, red);  // also orders the wgt writes before the reads below
-  const float invL = 1.f / l;
-  const int i = row / a.nh, h = row % a.nh;
-  const int m = s * a.block + i;
-  // lane ln of wave g holds dims 8 ln .. 8 ln + 7 (one 16-byte load per
-  // slot) over slots g, g + 4, ...; four slots per lane in flight; the four
-  // waves' sums are added in a fixed order
-  const int g = threadIdx.x >> 6, ln = threadIdx.x & 63;
-  const int nl = a.r / 8;  // lanes holding data (kv_lora % 16 == 0)
+  for (int p = lane; p < ns; p += 64) mx = fmaxf(mx, ml[2 * p]);
+  mx = wave_max(mx);
+  const int nl = a.r / 8;  // lanes holding data (kv_lora % 8 == 0, <= 512)
+  const u32x4* op = (const u32x4*)(a.o_part + ((long long)row * a.slots + base) * a.r) + (lane < nl ? lane : 0);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (ln < nl) {
-    const u32x4* op = (const u32x4*)(a.o_part + ((long long)row * a.slots + base) * a.r) + ln;
-    for (int p0 = g; p0 < ns; p0 += 16) {
-      u32x4 v[4];
-      float w[4];
+  float L = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += 64) {
+    const int pl = c0 + lane;
+    const float wl = pl < ns ? __expf(ml[2 * pl] - mx) * ml[2 * pl + 1] : 0.f;
+    L += wave_sum(wl);
+    const int n = min(64, ns - c0);
+    for (int u0 = 0; u0 < n; u0 += 8) {
+      u32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int p = p0 + 4 * u;
-        v[u] = p < ns ? op[(long long)p * nl] : u32x4{0u, 0u, 0u, 0u};
-        w[u] = p < ns ? wgt[p] : 0.f;
-      }
+      for (int u = 0; u < 8; ++u)
+        v[u] = u0 + u < n && lane < nl ? op[(long long)(c0 + u0 + u) * nl] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u) {
+        const float w = u0 + u < n ? lane_value(wl, u0 + u) : 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += w[u] * fp16_bits_to_f32(v[u][e] & 0xFFFFu);
-          acc[2 * e + 1] += w[u] * fp16_bits_to_f32(v[u][e] >> 16);
+          acc[2 * e] += w * fp16_bits_to_f32(v[u][e] & 0xFFFFu);
+          acc[2 * e + 1] += w * fp16_bits_to_f32(v[u][e] >> 16);
         }
+      }
     }
   }
-  // every wave stores its sums, then wave g writes dims 8 ln + 2g, 8 ln + 2g + 1
-  __shared__ float gsum[4][8][64];
-  if (ln < nl) {
+  if (lane < nl) {
+    const float invL = 1.f / L;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) gsum[g][e][ln] = acc[e];
-  }
-  __syncthreads();
-  if (ln < nl) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int e = 2 * g + k;
-      frag_put(a.fd_uv, h, m, 8 * ln + e,
-               ((gsum[0][e][ln] + gsum[1][e][ln]) + (gsum[2][e][ln] + gsum[3][e][ln])) * invL);
-    }
+    for (int e = 0; e < 8; ++e) acc[e] *= invL;
+    const int i = row / a.nh, h = row % a.nh;
+    frag_put8(a.fd_uv, h, s * a.block + i, 8 * lane, acc);
   }
 }
 
@@ -808,7 +786,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st) {
   if (a.slots > MAX_COMBINE_SLOTS || a.r % 8 || a.r > 512) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn_combine, dim3(a.rows, a.n_seq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(((long long)a.rows * a.n_seq + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
