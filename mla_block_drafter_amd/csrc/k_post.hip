@@ -16,10 +16,26 @@ namespace {
 
 // One row per workgroup (blockIdx.y), 256 columns per workgroup (blockIdx.x).
 
-// Row scale of row m (computed by wave 0), broadcast through LDS.
-__device__ __forceinline__ float shared_row_scale(const RowScale& s, int m, float* slot) {
+// Row scale of row m (computed by wave 0), broadcast through LDS, in two
+// steps: wave 0 requests the chunk sums first, the kernel then issues its own
+// loads (split-K partials, inputs), and the scale is formed after them, so the
+// two requests share one memory round trip.  The arithmetic is
+// row_scale_wave's.
+struct RowScaleLoads {
+  float t[4];
+};
+__device__ __forceinline__ RowScaleLoads row_scale_issue(const RowScale& s, int m) {
+  RowScaleLoads l{{0.f, 0.f, 0.f, 0.f}};
+  if (threadIdx.x < 64 && s.ssq) {
+    const float* row = s.ssq + (long long)m * SSQ_LD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l.t[i] = (int)threadIdx.x + 64 * i < s.nch ? row[threadIdx.x + 64 * i] : 0.f;
+  }
+  return l;
+}
+__device__ __forceinline__ float row_scale_finish(const RowScale& s, const RowScaleLoads& l, float* slot) {
   if (threadIdx.x < 64) {
-    const float v = row_scale_wave(s, m);
+    const float v = s.ssq ? rsqrtf(wave_sum((l.t[0] + l.t[1]) + (l.t[2] + l.t[3])) * s.invn + s.eps) : 1.f;
     if (threadIdx.x == 0) *slot = v;
   }
   __syncthreads();
@@ -59,9 +75,17 @@ __device__ __forceinline__ void part_sum_r(const PartIn& p, int m, const int (&c
     out[n] = v[n][0];
   }
 }
+// Splits per round: the smallest of 2, 4 and 8 that covers S (8 beyond), so
+// that few loads repeat the last split (the fused gate/up GEMM has two
+// splits: its SwiGLU post went from 11.1 to 8.5 us per launch at M = 112).
+// The sums equal those of eight splits per round: the tree levels that pair
+// a split with an absent one add zeros.  (Sixteen per round, one round trip
+// for up to 16 splits, measured slower for the q_a / kv_a post.)
 template <int N>
 __device__ __forceinline__ void part_sum_n(const PartIn& p, int m, const int (&c)[N], float (&out)[N]) {
-  part_sum_r<N, 8>(p, m, c, out);
+  if (p.S <= 2) part_sum_r<N, 2>(p, m, c, out);
+  else if (p.S <= 4) part_sum_r<N, 4>(p, m, c, out);
+  else part_sum_r<N, 8>(p, m, c, out);
 }
 
 __device__ __forceinline__ float part_sum(const PartIn& p, int m, int c) {
@@ -82,7 +106,8 @@ __device__ __forceinline__ void rope_pair(float x0, float x1, const float* cs, f
 // col0 .. col0 + latent - 1 (scaled by r): c = RMSNorm(first rr columns; g)
 // and the rotated rope pairs (cos, sin per pair in cs), written as one row
 // at element offset `at` of dst (fp32 or bf16).  All threads of the block.
-__device__ __forceinline__ void latent_row(const PartIn& p, int m, int col0, float r, int latent, int rr, int dr,
+__device__ __forceinline__ void latent_row(const PartIn& p, int m, int col0, const RowScale& rs_in,
+                                           const RowScaleLoads& rl, float* rs_slot, int latent, int rr, int dr,
                                            const float* g, float eps, const float* cs, void* dst, long long at,
                                            int f32, float* red, float* lat) {
   // latent columns k = tid + 256 u (latent <= 1024), all partial loads in flight together
@@ -93,6 +118,7 @@ __device__ __forceinline__ void latent_row(const PartIn& p, int m, int col0, flo
     for (int u = 0; u < 4; ++u) cc[u] = (int)threadIdx.x + 256 * u < latent ? col0 + (int)threadIdx.x + 256 * u : -1;
     float v[4];
     part_sum_n<4>(p, m, cc, v);
+    const float r = row_scale_finish(rs_in, rl, rs_slot);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int k = threadIdx.x + 256 * u;
@@ -123,17 +149,21 @@ __global__ __launch_bounds__(256) void k_post_resid(ResidPost a) {
   __shared__ float rs;
   const int m = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  float r = 1.f;
-  if (a.mode == RP_NORM) r = shared_row_scale(a.rs_in, m, &rs);
   float sq = 0.f, dt = 0.f;
   const bool ok = c < a.H;
   float x = 0.f;
+  if (a.mode == RP_NORM) {
+    const RowScaleLoads rl = row_scale_issue(a.rs_in, m);
+    const float xi = ok ? a.x_in[(long long)m * a.H + c] : 0.f, g0 = ok ? a.g0[c] : 0.f;
+    const float r = row_scale_finish(a.rs_in, rl, &rs);
+    x = g0 * (xi * r);
+  }
   if (ok) {
     const long long i = (long long)m * a.H + c;
     switch (a.mode) {
       case RP_SUM: x = part_sum(a.p, m, c); break;
       case RP_ADD: x = a.x_in[i] + part_sum(a.p, m, c); break;
-      case RP_NORM: x = a.g0[c] * (a.x_in[i] * r); break;
+      case RP_NORM: break;
       default: x = a.x_in[i]; break;
     }
     a.x_out[i] = x;
@@ -162,14 +192,16 @@ __global__ __launch_bounds__(256) void k_post_qkva(QkvaPost a) {
   __shared__ float rs;
   __shared__ float lat[1024];
   const int m = blockIdx.y;
-  const float r = shared_row_scale(a.rs_in, m, &rs);
+  const RowScaleLoads rl = row_scale_issue(a.rs_in, m);
   const int ncq = (a.q_lora + 255) / 256;
   if ((int)blockIdx.x < ncq) {
     const int c = blockIdx.x * 256 + threadIdx.x;
     const bool ok = c < a.q_lora;
+    const float ps = ok ? part_sum(a.p, m, c) : 0.f;
+    const float r = row_scale_finish(a.rs_in, rl, &rs);
     float sq = 0.f, v = 0.f;
     if (ok) {
-      v = r * part_sum(a.p, m, c);
+      v = r * ps;
       sq = v * v;
     }
     frag_put_wave(a.fd_qb, 0, m, c, ok ? a.g_qa[c] * v : 0.f, ok);
@@ -177,8 +209,8 @@ __global__ __launch_bounds__(256) void k_post_qkva(QkvaPost a) {
     if (threadIdx.x == 0) a.ssq_cq[m * SSQ_LD + blockIdx.x] = sq;
     return;
   }
-  latent_row(a.p, m, a.q_lora, r, a.latent, a.r, a.dr, a.g_kva, a.eps, a.rope + (long long)m * (a.dr / 2) * 2,
-             a.bkeys, (long long)m * a.latent, a.kv_f32, red, lat);
+  latent_row(a.p, m, a.q_lora, a.rs_in, rl, &rs, a.latent, a.r, a.dr, a.g_kva, a.eps,
+             a.rope + (long long)m * (a.dr / 2) * 2, a.bkeys, (long long)m * a.latent, a.kv_f32, red, lat);
 }
 
 // ---------------------------------------------------------- cache append --
@@ -188,9 +220,9 @@ __global__ __launch_bounds__(256) void k_post_kv_rows(KvRowPost a) {
   __shared__ float rs;
   __shared__ float lat[1024];
   const int m = blockIdx.x;
-  const float r = shared_row_scale(a.rs_in, m, &rs);
-  latent_row(a.p, m, 0, r, a.latent, a.r, a.dr, a.g_kva, a.eps, a.rope + (long long)m * (a.dr / 2) * 2, a.dst,
-             a.slot[m] * a.latent, a.dst_f32, red, lat);
+  const RowScaleLoads rl = row_scale_issue(a.rs_in, m);
+  latent_row(a.p, m, 0, a.rs_in, rl, &rs, a.latent, a.r, a.dr, a.g_kva, a.eps, a.rope + (long long)m * (a.dr / 2) * 2,
+             a.dst, a.slot[m] * a.latent, a.dst_f32, red, lat);
 }
 
 // ------------------------------------------------------------------ q_b --
@@ -199,16 +231,18 @@ __global__ __launch_bounds__(256) void k_post_kv_rows(KvRowPost a) {
 __global__ __launch_bounds__(256) void k_post_qb(QbPost a) {
   __shared__ float rs;
   const int m = blockIdx.y;
-  const float r = shared_row_scale(a.rs, m, &rs);
+  const RowScaleLoads rl = row_scale_issue(a.rs, m);
   const int hd = a.dn + a.dr;
   const int c0 = 2 * (blockIdx.x * 256 + threadIdx.x);
-  if (c0 >= a.nh * hd) return;
-  const int h = c0 / hd, e = c0 % hd;
+  const bool live = c0 < a.nh * hd;
   float v[2];
   {
-    const int cc[2] = {c0, c0 + 1};
+    const int cc[2] = {live ? c0 : -1, live ? c0 + 1 : -1};
     part_sum_n<2>(a.p, m, cc, v);
   }
+  const float r = row_scale_finish(a.rs, rl, &rs);  // every thread reaches the barrier
+  if (!live) return;
+  const int h = c0 / hd, e = c0 % hd;
   const float v0 = r * v[0], v1 = r * v[1];
   if (e < a.dn) {
     frag_put(a.fd_uk, h, m, e, v0);
@@ -232,14 +266,17 @@ __global__ __launch_bounds__(256) void k_post_qb(QbPost a) {
 __global__ __launch_bounds__(256) void k_post_swiglu(SwigluPost a) {
   __shared__ float rs;
   const int m = blockIdx.y;
-  const float r = shared_row_scale(a.rs, m, &rs);
+  const RowScaleLoads rl = row_scale_issue(a.rs, m);
   const int c = blockIdx.x * 256 + threadIdx.x;
   const bool ok = c < a.inter;
+  float gu[2];
+  {
+    const int cc[2] = {ok ? c : -1, ok ? a.inter + c : -1};
+    part_sum_n<2>(a.p, m, cc, gu);
+  }
+  const float r = row_scale_finish(a.rs, rl, &rs);
   float h = 0.f;
   if (ok) {
-    float gu[2];
-    const int cc[2] = {c, a.inter + c};
-    part_sum_n<2>(a.p, m, cc, gu);
     const float g = r * gu[0], u = r * gu[1];
     h = g / (1.f + __expf(-g)) * u;
   }
