@@ -160,12 +160,14 @@ __device__ __forceinline__ float conf_dot16(const uint16_t* w1row, const float* 
   return ((ws[0] + ws[1]) + ws[2]) + ws[3];
 }
 
-// One workgroup per sequence: one memory round for every position's chunk
+// One workgroup per sequence: one memory trip for every position's chunk
 // thresholds and slots (and every small input), one for the rows, then LDS
-// only.
+// only (plus one sweep of the logits of any chunk whose candidates
+// overflowed its slots).
 //  1. the position's threshold is the largest chunk L; keep the slot entries
-//     whose upper end reaches it (too many anywhere, or none: the fallback
-//     flag is raised, nothing written);
+//     whose upper end reaches it, and rescan the chunks that had more
+//     candidates than slots against it (more than MK_CAPG candidates for a
+//     position, or none: the fallback flag is raised, nothing written);
 //  2. W2's row of every candidate and W1's row of every possible predecessor
 //     (the candidates of the previous position, the last verified token, or
 //     the forced predecessors) into LDS;
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256) void k_markov_prune(MarkovPruneArgs a) {
     ovf[threadIdx.x] = 0u;
   }
   __syncthreads();
-  // round 1: every global read before the rows, issued together
+  // first memory trip: every global read before the rows, issued together
   const float cwv = (int)threadIdx.x < a.R ? a.conf_wm[threadIdx.x] : 0.f;
   const float cbv = a.conf_b[0];
   int tpv = -1;
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256) void k_markov_prune(MarkovPruneArgs a) {
         base = v[t];
       }
   };
-  // round 2: rows into LDS, 16 bytes per piece.  W2 rows are packed in
+  // second memory trip: rows into LDS, 16 bytes per piece.  W2 rows are packed in
   //    16-row tiles: dims 8 q .. 8 q + 7 of k block kb of row v sit at
   //    ((tile KB + kb) 64 + q 16 + v % 16) 16 bytes.  W1 rows are plain
   //    (row stride w1_ld).  Pieces: [0, n2p) W2 rows of the candidates,
