@@ -262,8 +262,8 @@ int32_t dspark_draft_block(const dspark_model* m, const dspark_block_in* in,
  * (DSPARK_STATIC_SCRATCH_BYTES, one copy per GPU, held until the process
  * ends).  Same arguments, semantics and results as dspark_draft_block.
  * Calls whose workspace would exceed the array (see dspark_workspace_bytes;
- * e.g. one sequence with more than ~28k cached tokens at the full geometry)
- * fail with DSPARK_EWORKSPACE and enqueue nothing.  Every call on a GPU shares
+ * e.g. one sequence with more than about 220k cached tokens at the full
+ * geometry) fail with DSPARK_EWORKSPACE and enqueue nothing.  Every call on a GPU shares
  * that GPU's array: calls that overlap on one GPU (concurrent streams, or
  * threads) race and must be ordered by the caller.  The array keeps the last
  * call's contents; the pass clears what it needs zeroed itself, with a kernel
